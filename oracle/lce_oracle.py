@@ -209,14 +209,18 @@ def linear_cross_entropy(X, W, b, t, *, ignore_index: int = -100,
 def softmax_cross_entropy(z, t, *, ignore_index: int = -100,
                           reduction: str = "mean", grad_scale: float = 1.0):
     """Standalone CE on given logits ([LIG]): returns (loss, dL) where dL is
-    what the in-place kernel writes over the logits buffer."""
+    what the in-place kernel writes over the logits buffer: the gradient of
+    grad_scale * loss for mean / sum, of sum_n grad_scale * loss_n for none."""
     z = np.asarray(z, np.float64)
     V = z.shape[1]
     valid, _, n_valid, _ = target_masks(t, V, ignore_index)
     tc = corrected_targets(t, valid)
     lse = logsumexp_rows(z)
     loss = reduce_loss(row_losses(z, lse, tc, valid), n_valid, reduction)
-    g = row_weights(valid, reduction, grad_scale)
+    # 'none': the gradient of sum_n grad_scale * loss_n (the same upstream
+    # value on every row).
+    up = np.full(z.shape[0], grad_scale) if reduction == "none" else None
+    g = row_weights(valid, reduction, grad_scale, up)
     return loss, dlogits(z, lse, tc, g)
 
 
@@ -260,3 +264,31 @@ def columns_grad_w_b(X_rows, W, b, t_rows, g_rows, cols, *,
     dL = dlogits(z, logsumexp_rows(z), tc, np.asarray(g_rows, np.float64))
     dLc = dL[:, cols]
     return dLc.T @ np.asarray(X_rows, np.float64), dLc.sum(axis=0)
+
+
+def row_block(X_rows, W, b, t_rows, g_rows, cols=None, *, ignore_index: int = -100,
+              grad_x: bool = False, return_z: bool = False) -> dict:
+    """All per-row quantities of a block of rows from one logits product:
+    lse, loss_n, argmax, top-2 gap, row max; optionally the block's grad_X
+    rows and its contribution to grad_W[cols] and grad_b[cols]; optionally
+    the block's logits."""
+    V = np.asarray(W).shape[0]
+    valid, _, _, _ = target_masks(t_rows, V, ignore_index)
+    tc = corrected_targets(t_rows, valid)
+    z = logits(X_rows, W, b)
+    lse = logsumexp_rows(z)
+    out = {"lse": lse, "loss_rows": row_losses(z, lse, tc, valid), "argmax": argmax_rows(z)}
+    part = np.partition(z, V - 2, axis=1)[:, V - 2:] if V > 1 else None
+    out["rowmax"] = z.max(axis=1)
+    out["top2_gap"] = (part[:, 1] - part[:, 0]) if V > 1 else np.full(z.shape[0], np.inf)
+    if grad_x or cols is not None:
+        dL = dlogits(z, lse, tc, np.asarray(g_rows, np.float64))
+        if grad_x:
+            out["grad_X"] = dL @ np.asarray(W, np.float64)
+        if cols is not None:
+            dLc = dL[:, cols]
+            out["grad_W_cols"] = dLc.T @ np.asarray(X_rows, np.float64)
+            out["grad_b_cols"] = dLc.sum(axis=0)
+    if return_z:
+        out["z"] = z
+    return out

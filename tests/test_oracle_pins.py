@@ -118,7 +118,8 @@ def test_matches_torch_cpu_cross_entropy(reduction, ignore_index):
     np.testing.assert_allclose(r["grad_b"], b.grad.numpy(), rtol=1e-12, atol=1e-15)
 
 
-def test_standalone_ce_matches_torch():
+@pytest.mark.parametrize("scale", [1.0, 1.5])
+def test_standalone_ce_matches_torch(scale):
     rng = np.random.default_rng(7)
     z = rng.standard_normal((17, 13))
     t = rng.integers(0, 13, 17)
@@ -127,8 +128,8 @@ def test_standalone_ce_matches_torch():
     for red in RED:
         zt.grad = None
         loss = torch.nn.functional.cross_entropy(zt, torch.tensor(t), reduction=red)
-        (loss.sum() if red == "none" else loss).backward()
-        ol, dL = oracle.softmax_cross_entropy(z, t, reduction=red)
+        (scale * (loss.sum() if red == "none" else loss)).backward()
+        ol, dL = oracle.softmax_cross_entropy(z, t, reduction=red, grad_scale=scale)
         np.testing.assert_allclose(ol, loss.detach().numpy(), rtol=1e-13)
         np.testing.assert_allclose(dL, zt.grad.numpy(), rtol=1e-12, atol=1e-16)
 
@@ -317,5 +318,27 @@ def test_row_subset_helpers_agree_with_full():
                                         full["g"][sl], cols)
         gw += a
         gb += bb
+    np.testing.assert_allclose(gw, full["grad_W"][cols], rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(gb, full["grad_b"][cols], rtol=1e-12, atol=1e-16)
+
+
+def test_row_block_agrees_with_full():
+    c = _case(N=40, D=6, V=25, seed=19)
+    full = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction="sum")
+    cols = np.array([0, 3, 24])
+    gw = np.zeros((3, 6))
+    gb = np.zeros(3)
+    for r0 in range(0, 40, 11):
+        sl = slice(r0, r0 + 11)
+        r = oracle.row_block(c["X"][sl], c["W"], c["b"], c["t"][sl], full["g"][sl], cols,
+                             grad_x=True, return_z=True)
+        np.testing.assert_allclose(r["lse"], full["lse"][sl], rtol=1e-15)
+        np.testing.assert_allclose(r["loss_rows"], full["loss_rows"][sl], rtol=1e-15)
+        np.testing.assert_allclose(r["grad_X"], full["grad_X"][sl], rtol=1e-13, atol=1e-17)
+        np.testing.assert_array_equal(r["argmax"], full["argmax"][sl])
+        zs = np.sort(r["z"], axis=1)
+        np.testing.assert_allclose(r["top2_gap"], zs[:, -1] - zs[:, -2], rtol=1e-15)
+        gw += r["grad_W_cols"]
+        gb += r["grad_b_cols"]
     np.testing.assert_allclose(gw, full["grad_W"][cols], rtol=1e-12, atol=1e-16)
     np.testing.assert_allclose(gb, full["grad_b"][cols], rtol=1e-12, atol=1e-16)
