@@ -1,0 +1,229 @@
+/*
+ * lce.h -- C ABI of the chunked fused linear-cross-entropy library (liblce.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For inputs X[N,D], an output-head weight W[V,D], an
+ * optional bias b[V] and int64 targets t[N], the logits are z = X W^T + b.
+ * The library forms the row-wise log-sum-exp, the per-row loss
+ * lse_n - z[n, t_n] (0 on ignored rows), its mean / sum / per-row value, and
+ * the gradients grad_X = dL W, grad_W = dL^T X and grad_b = sum_n dL[n, :],
+ * where dL = g (softmax(z) - onehot(t)) and g is the per-row weight of the
+ * reduction.  It walks the batch rows in chunks of chunk_rows rows, so the
+ * full N x V logit matrix never exists; the gradients are formed during the
+ * same pass as the loss.
+ *
+ * Sources: the PyTorch module source torch/nn/modules/linear_cross_entropy.py
+ * (custom ops _linear_cross_entropy_batch_chunked and
+ * _linear_cross_entropy_batch_chunked_no_reduction, their argument lists and
+ * fake-tensor output contract; _ChunkContext.build validation;
+ * neg_weight_target for the per-row weights), the
+ * torch.nn.LinearCrossEntropyOptions documentation page (batch_chunk_size,
+ * chunking_method "aspect_ratio", acc_policy, acc_dtype), and Liger-Kernel
+ * issue #343 (a cross-entropy kernel that overwrites its logits with the
+ * gradient in place).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers live on the current HIP device (hipSetDevice /
+ *     torch.cuda.set_device); the library never changes the device.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Compute entry points only enqueue work on it: no host synchronisation,
+ *     no device allocation.  Errors found on the host are returned before
+ *     anything is enqueued.
+ *   - The caller owns every device buffer, including the workspace; the
+ *     library owns only the host-side handle.  Inputs are never modified,
+ *     except the logits buffer of lce_ce_inplace, which by contract is
+ *     overwritten with the gradient.
+ *   - All matrices are dense row-major with the row length as stride.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t).
+ *   - Rows of X and W must be 16-byte aligned: D % 8 == 0 for bf16,
+ *     D % 4 == 0 for fp32 (LCE_ERR_UNSUPPORTED otherwise); base pointers
+ *     16-byte aligned.
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define LCE_API __attribute__((visibility("default")))
+#else
+#define LCE_API
+#endif
+
+typedef struct lce_handle lce_handle;  /* opaque, host memory only */
+
+/* Status codes.  Host validation maps the pages' Python exceptions
+ * (_ChunkContext.build: TypeError / NotImplementedError / RuntimeError for
+ * bad dtypes, unsupported reductions, shape mismatches) onto these. */
+typedef enum {
+  LCE_OK = 0,
+  LCE_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
+  LCE_ERR_DTYPE = 2,        /* dtype not in {LCE_F32, LCE_BF16} */
+  LCE_ERR_UNSUPPORTED = 3,  /* acc_dtype != LCE_F32, unaligned rows, ... */
+  LCE_ERR_WORKSPACE = 4,    /* workspace NULL, misaligned or too small */
+  LCE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
+} lce_status;
+
+typedef enum { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype;
+
+/* Loss reduction (the pages' reduction argument). */
+typedef enum { LCE_MEAN = 0, LCE_SUM = 1, LCE_NONE = 2 } lce_reduction;
+
+/* How grad_W is accumulated across chunks when the input dtype is bf16
+ * (the pages' acc_policy).  ACCURATE keeps an fp32 V x D accumulator in the
+ * workspace across all chunks and rounds to bf16 once at the end; COMPACT
+ * adds each chunk's fp32 tile straight into the bf16 grad_W (one rounding
+ * per chunk) and needs no V x D accumulator.  Identical for fp32 input. */
+typedef enum { LCE_ACCURATE = 0, LCE_COMPACT = 1 } lce_acc_policy;
+
+/* Output flags (the pages' compute_input_grad / compute_linear_weight_grad /
+ * compute_linear_bias_grad, plus the per-row argmax of the logits). */
+enum {
+  LCE_GRAD_X = 1u,
+  LCE_GRAD_W = 2u,
+  LCE_GRAD_B = 4u,
+  LCE_ARGMAX = 8u
+};
+
+/* Special chunk_rows values. */
+#define LCE_CHUNK_ASPECT_RATIO 0   /* next_pow2(ceil(N / ceil(V / D))) rows */
+#define LCE_CHUNK_ALL (-1)         /* one chunk of N rows */
+
+/* Problem description, fixed at lce_create.  Enum-typed fields are int32. */
+typedef struct {
+  int64_t N;             /* rows (batch x sequence, folded) >= 0 */
+  int64_t D;             /* in_features >= 1 */
+  int64_t V;             /* classes >= 1 */
+  int64_t ignore_index;  /* rows with this target are ignored (default -100) */
+  int64_t chunk_rows;    /* > 0 rows per chunk, or LCE_CHUNK_* */
+  int32_t dtype;         /* lce_dtype of X, W, b and of the gradients */
+  int32_t acc_dtype;     /* must be LCE_F32 */
+  int32_t has_bias;      /* 0 or 1 */
+  int32_t reduction;     /* lce_reduction */
+  int32_t acc_policy;    /* lce_acc_policy */
+  uint32_t flags;        /* LCE_GRAD_* | LCE_ARGMAX */
+} lce_desc;
+
+/* Buffers of one call.  All pointers are device pointers. */
+typedef struct {
+  const void* X;             /* [N, D] dtype */
+  const void* W;             /* [V, D] dtype */
+  const void* b;             /* [V] dtype; NULL iff has_bias == 0 */
+  const int64_t* targets;    /* [N] int64 */
+  const float* grad_output;  /* LCE_NONE only: NULL -> loss-only forward
+                                (no gradients); non-NULL -> [N] per-row
+                                upstream gradient, gradients recomputed from
+                                the inputs.  Must be NULL for MEAN / SUM. */
+  float* loss;               /* MEAN / SUM: [1] fp32.  NONE: [N] fp32, 0 on
+                                ignored rows (may be NULL in the NONE
+                                backward). */
+  void* grad_X;              /* [N, D] dtype, needs LCE_GRAD_X, else ignored */
+  void* grad_W;              /* [V, D] dtype, needs LCE_GRAD_W, else ignored */
+  void* grad_b;              /* [V] dtype, needs LCE_GRAD_B and has_bias */
+  int32_t* argmax;           /* [N] int32, needs LCE_ARGMAX, else ignored:
+                                lowest class index attaining the row max */
+  int64_t* n_valid;          /* [1] int64 or NULL: rows that count */
+  int64_t* n_bad;            /* [1] int64 or NULL: rows whose target is
+                                outside [0, V) and not ignore_index */
+  float grad_scale;          /* MEAN / SUM: the upstream gradient of the
+                                scalar loss, folded into the gradients
+                                (1.0 for a plain backward) */
+  int32_t reserved;          /* set to 0 */
+} lce_io;
+
+/* Validate `d`, resolve the chunk size and build a handle.  Host only.
+ * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, bad
+ * reduction / acc_policy / has_bias, unknown flag bits, NULL pointers),
+ * DTYPE, UNSUPPORTED (acc_dtype != LCE_F32; D not a multiple of 8 for bf16
+ * or 4 for fp32; N, V or D above 2^31 - 1).  LCE_GRAD_B without a bias is
+ * INVALID_ARG. */
+LCE_API lce_status lce_create(const lce_desc* d, lce_handle** out);
+
+/* Bytes of device workspace lce_forward_backward needs (host only). */
+LCE_API lce_status lce_workspace_size(const lce_handle* h, size_t* bytes);
+
+/* The resolved rows per chunk (0 when N == 0) and the chunk count. */
+LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
+                          int64_t* n_chunks);
+
+/* Enqueue the whole chunked forward+backward on `stream`.
+ *
+ * Per-row weight g_n (the negated neg_weight_target of the pages):
+ *   MEAN: grad_scale / n_valid on counted rows (NaN on every row when
+ *         n_valid == 0, so the loss and every gradient are NaN);
+ *   SUM:  grad_scale on counted rows;
+ *   NONE: grad_output[n] on counted rows (backward only).
+ * Ignored rows and rows with out-of-range targets have g_n = 0, loss 0 and a
+ * zero grad_X row.  With N == 0, MEAN gives a NaN loss, SUM a zero loss, and
+ * grad_W / grad_b are filled with zeros.
+ *
+ * `workspace` is a device buffer of at least lce_workspace_size bytes,
+ * 256-byte aligned; its contents on entry are irrelevant and on return are
+ * unspecified.  Calls that share a workspace or outputs must be ordered on
+ * one stream.  Errors: INVALID_ARG (NULL required pointer, grad_output set
+ * for MEAN / SUM, grad_b requested without bias), WORKSPACE, HIP. */
+LCE_API lce_status lce_forward_backward(lce_handle* h, const lce_io* io,
+                                void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/* Release the handle (NULL is accepted). */
+LCE_API lce_status lce_destroy(lce_handle* h);
+
+/* Bytes of device workspace for lce_ce_inplace on N rows. */
+LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
+
+/* Standalone softmax cross-entropy on precomputed fp32 logits [N, V]
+ * (row-major, row stride V, 16-byte aligned, V % 4 == 0), enqueued on
+ * `stream`.  Writes the loss (MEAN / SUM: loss[1]; NONE: loss[N]) and
+ * overwrites `logits` in place with the gradient g_n (softmax - onehot), g_n
+ * as for lce_forward_backward with grad_output = grad_scale on every counted
+ * row for NONE.  n_valid may be NULL.  Errors: INVALID_ARG, UNSUPPORTED,
+ * WORKSPACE, HIP. */
+LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets, int64_t N,
+                          int64_t V, int64_t ignore_index, int32_t reduction,
+                          float grad_scale, float* loss, int64_t* n_valid,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Kernel classes of lce_forward_backward, for the timing hook below. */
+enum {
+  LCE_K_PREP = 0,       /* target counts and row weights */
+  LCE_K_LOGITS = 1,     /* logits GEMM with the fused softmax-statistics epilogue */
+  LCE_K_COMBINE = 2,    /* per-row log-sum-exp, loss, argmax */
+  LCE_K_FINALIZE = 3,   /* dL = g (softmax - onehot) in place, dL^T, bias partials */
+  LCE_K_GEMM_X = 4,     /* grad_X = dL . W (split-K partials) */
+  LCE_K_SPLIT_SUM = 5,  /* split-K reduction into grad_X */
+  LCE_K_TRANSPOSE = 6,  /* W^T once per call, X_chunk^T per chunk */
+  LCE_K_GEMM_W = 7,     /* grad_W += dL^T . X_chunk */
+  LCE_K_BIAS = 8,       /* grad_b reduction */
+  LCE_K_LOSS = 9,       /* final loss reduction, zero fills */
+  LCE_K_COUNT = 10
+};
+
+/* Timing hook for benchmarks.  While enabled, every launch of a kernel class
+ * whose bit (1u << LCE_K_*) is in `kernel_mask` is bracketed by two
+ * hipEventRecord calls on the call's stream (events come from a fixed pool
+ * created here; launches beyond the pool are not timed).  mask 0 disables
+ * the hook and releases the events.  Host only; HIP errors -> LCE_ERR_HIP. */
+LCE_API lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask);
+
+/* Wait for the recorded events, then write per-class totals since the last
+ * read: ms[k] (milliseconds) and launches[k] for k < LCE_K_COUNT (either
+ * pointer may be NULL), and restart the count. */
+LCE_API lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches);
+
+/* Static, human-readable name of a status code. */
+LCE_API const char* lce_status_string(lce_status s);
+
+/* Text of the last HIP error seen by this thread's calls ("" if none). */
+LCE_API const char* lce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -1,0 +1,431 @@
+// C ABI of liblce.so: validation, chunk planning, workspace layout and the
+// per-chunk launch sequence.  See include/lce.h for the contract.
+//
+// The chunk loop follows the batch-chunked accumulator of the PyTorch module
+// torch/nn/modules/linear_cross_entropy.py: for each chunk of rows, the logits
+// GEMM with bias, the row statistics and loss terms, then (when gradients are
+// requested) the logits gradient in place and the three gradient products,
+// with grad_W and grad_b accumulated across chunks in fp32 and committed to
+// the input dtype once.  The chunk size defaults to the "aspect_ratio" rule of
+// the torch.nn.LinearCrossEntropyOptions page.
+#include "../../include/lce.h"
+#include "lce_kernels.h"
+
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+// Events bracketing selected kernel classes (the benchmark timing hook).
+struct TimingPool {
+  static constexpr size_t kPairs = 2048;
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> ev;   // 2 per slot
+  std::vector<int> kind;        // kernel class per slot
+  size_t used = 0;
+};
+
+struct lce_handle {
+  lce_desc d;
+  bool bf16;
+  int esize;
+  int64_t c;          // rows per chunk
+  int64_t n_chunks;
+  int64_t c_pad;      // c rounded up to 64 (row stride of dLt, Xt and partials)
+  int64_t V_pad;      // V rounded up to 256 (row stride of T, Wt)
+  int n_vt;           // 256-class tiles
+  int splits;         // split-K of the grad_X GEMM
+  int k_split;
+  bool want_x, want_w, want_b, want_argmax, want_any;
+  bool w_acc32;       // fp32 grad_W accumulator in the workspace
+  // workspace offsets (bytes)
+  size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
+      o_gw32, o_gbp, o_gb32, o_lrows, o_cnt, total;
+  TimingPool timing;
+};
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+lce_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return LCE_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
+           hipGetErrorString(e));
+  return LCE_ERR_HIP;
+}
+
+#define LCE_HIP(call)                                  \
+  do {                                                 \
+    const lce_status st_ = hip_status(call);           \
+    if (st_ != LCE_OK) return st_;                     \
+  } while (0)
+
+// Launch `call`; when the timing hook selects kernel class `k`, bracket it
+// with two events on stream `s`.
+#define LCE_LAUNCH(h, k, call)                                                   \
+  do {                                                                           \
+    TimingPool& tp_ = (h)->timing;                                               \
+    const bool on_ = ((tp_.mask >> (k)) & 1u) && tp_.used < tp_.kind.size();    \
+    if (on_) LCE_HIP(hipEventRecord(tp_.ev[2 * tp_.used], s));                   \
+    LCE_HIP(call);                                                               \
+    if (on_) {                                                                   \
+      LCE_HIP(hipEventRecord(tp_.ev[2 * tp_.used + 1], s));                      \
+      tp_.kind[tp_.used++] = (k);                                                \
+    }                                                                            \
+  } while (0)
+
+// next power of two >= x (x >= 1)
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Rows per chunk.  aspect_ratio: the logits buffer (rows, V) holds as many
+// elements as the input (N, D): next_pow2(ceil(N / ceil(V / D))).
+int64_t resolve_chunk_rows(const lce_desc& d) {
+  if (d.N == 0) return 0;
+  int64_t c;
+  if (d.chunk_rows > 0) c = d.chunk_rows;
+  else if (d.chunk_rows == LCE_CHUNK_ALL) c = d.N;
+  else c = next_pow2(cdiv64(d.N, cdiv64(d.V, d.D)));
+  return std::min(c, d.N);
+}
+
+void plan(lce_handle* h) {
+  const lce_desc& d = h->d;
+  h->bf16 = d.dtype == LCE_BF16;
+  h->esize = h->bf16 ? 2 : 4;
+  h->c = resolve_chunk_rows(d);
+  h->n_chunks = h->c ? cdiv64(d.N, h->c) : 0;
+  h->c_pad = round_up(std::max<int64_t>(h->c, 1), 64);
+  h->V_pad = round_up(d.V, lce::kTile);
+  h->n_vt = static_cast<int>(h->V_pad / lce::kTile);
+  h->want_x = d.flags & LCE_GRAD_X;
+  h->want_w = d.flags & LCE_GRAD_W;
+  h->want_b = d.flags & LCE_GRAD_B;
+  h->want_argmax = d.flags & LCE_ARGMAX;
+  h->want_any = h->want_x || h->want_w || h->want_b;
+  h->w_acc32 = h->want_w && h->bf16 && d.acc_policy == LCE_ACCURATE;
+
+  // split-K for grad_X = dL . W: aim at >= 512 workgroups, >= 1024 K per split.
+  const int64_t tiles = cdiv64(h->c, lce::kTile) * cdiv64(d.D, lce::kTile);
+  int64_t splits = std::max<int64_t>(1, cdiv64(512, std::max<int64_t>(tiles, 1)));
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, h->V_pad / 1024));
+  int64_t ks = round_up(cdiv64(h->V_pad, splits), 64);
+  h->splits = static_cast<int>(cdiv64(h->V_pad, ks));
+  h->k_split = static_cast<int>(ks);
+
+  const int64_t es = h->esize, c = h->c_pad, V = d.V, Vp = h->V_pad, D = d.D, N = d.N;
+  size_t o = 0;
+  auto take = [&](size_t bytes, bool need) {
+    const size_t at = o;
+    if (need) o = align_up(o + bytes);
+    return need ? at : static_cast<size_t>(-1);
+  };
+  h->o_T = take(c * Vp * es, h->want_any);
+  h->o_dLt = take(Vp * c * es, h->want_w);
+  h->o_Wt = take(D * Vp * es, h->want_x);
+  h->o_Xt = take(D * c * es, h->want_w);
+  h->o_mp = take(h->n_vt * c * 4, true);
+  h->o_sp = take(h->n_vt * c * 4, true);
+  h->o_ip = take(h->n_vt * c * 4, h->want_argmax);
+  h->o_zt = take(c * 4, true);
+  h->o_lse = take(c * 4, true);
+  h->o_g = take(std::max<int64_t>(N, 1) * 4, true);
+  h->o_tc = take(std::max<int64_t>(N, 1) * 4, true);
+  h->o_gxp = take(static_cast<size_t>(h->splits) * c * D * 4, h->want_x);
+  h->o_gw32 = take(V * D * 4, h->w_acc32);
+  h->o_gbp = take((c / 64) * Vp * 4, h->want_b);
+  h->o_gb32 = take(Vp * 4, h->want_b);
+  h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
+  h->o_cnt = take(2 * 8, true);
+  h->total = o;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return off == static_cast<size_t>(-1) ? nullptr
+                                         : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lce_status_string(lce_status s) {
+  switch (s) {
+    case LCE_OK: return "LCE_OK";
+    case LCE_ERR_INVALID_ARG: return "LCE_ERR_INVALID_ARG";
+    case LCE_ERR_DTYPE: return "LCE_ERR_DTYPE";
+    case LCE_ERR_UNSUPPORTED: return "LCE_ERR_UNSUPPORTED";
+    case LCE_ERR_WORKSPACE: return "LCE_ERR_WORKSPACE";
+    case LCE_ERR_HIP: return "LCE_ERR_HIP";
+  }
+  return "LCE_ERR_UNKNOWN";
+}
+
+const char* lce_last_error(void) { return g_last_error; }
+
+lce_status lce_create(const lce_desc* d, lce_handle** out) {
+  if (!d || !out) return LCE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (d->N < 0 || d->D < 1 || d->V < 1 || d->chunk_rows < LCE_CHUNK_ALL)
+    return LCE_ERR_INVALID_ARG;
+  if (d->dtype != LCE_F32 && d->dtype != LCE_BF16) return LCE_ERR_DTYPE;
+  if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
+  if (d->acc_policy != LCE_ACCURATE && d->acc_policy != LCE_COMPACT) return LCE_ERR_INVALID_ARG;
+  if (d->has_bias != 0 && d->has_bias != 1) return LCE_ERR_INVALID_ARG;
+  if (d->flags & ~static_cast<uint32_t>(LCE_GRAD_X | LCE_GRAD_W | LCE_GRAD_B | LCE_ARGMAX))
+    return LCE_ERR_INVALID_ARG;
+  if ((d->flags & LCE_GRAD_B) && !d->has_bias) return LCE_ERR_INVALID_ARG;
+  // Mixed precision is bf16 (or fp32) inputs with an fp32 accumulator only.
+  if (d->acc_dtype != LCE_F32) return LCE_ERR_UNSUPPORTED;
+  const int64_t vec = d->dtype == LCE_BF16 ? 8 : 4;
+  if (d->D % vec != 0) return LCE_ERR_UNSUPPORTED;
+  const int64_t kMax = 2147483647LL - 1024;
+  if (d->N > kMax || d->V > kMax || d->D > kMax) return LCE_ERR_UNSUPPORTED;
+  lce_handle* h = new (std::nothrow) lce_handle();
+  if (!h) return LCE_ERR_INVALID_ARG;
+  h->d = *d;
+  plan(h);
+  *out = h;
+  return LCE_OK;
+}
+
+lce_status lce_workspace_size(const lce_handle* h, size_t* bytes) {
+  if (!h || !bytes) return LCE_ERR_INVALID_ARG;
+  *bytes = h->total;
+  return LCE_OK;
+}
+
+lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows, int64_t* n_chunks) {
+  if (!h) return LCE_ERR_INVALID_ARG;
+  if (chunk_rows) *chunk_rows = h->c;
+  if (n_chunks) *n_chunks = h->n_chunks;
+  return LCE_OK;
+}
+
+lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask) {
+  if (!h) return LCE_ERR_INVALID_ARG;
+  TimingPool& tp = h->timing;
+  if (kernel_mask == 0) {
+    for (hipEvent_t e : tp.ev) (void)hipEventDestroy(e);
+    tp.ev.clear();
+    tp.kind.clear();
+    tp.used = 0;
+    tp.mask = 0;
+    return LCE_OK;
+  }
+  if (tp.ev.empty()) {
+    tp.ev.resize(2 * TimingPool::kPairs, nullptr);
+    for (hipEvent_t& e : tp.ev) LCE_HIP(hipEventCreate(&e));
+    tp.kind.assign(TimingPool::kPairs, 0);
+  }
+  tp.used = 0;
+  tp.mask = kernel_mask;
+  return LCE_OK;
+}
+
+lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches) {
+  if (!h) return LCE_ERR_INVALID_ARG;
+  TimingPool& tp = h->timing;
+  double tot[LCE_K_COUNT] = {0};
+  int64_t cnt[LCE_K_COUNT] = {0};
+  if (tp.used > 0) LCE_HIP(hipEventSynchronize(tp.ev[2 * tp.used - 1]));
+  for (size_t i = 0; i < tp.used; ++i) {
+    float t = 0.0f;
+    LCE_HIP(hipEventElapsedTime(&t, tp.ev[2 * i], tp.ev[2 * i + 1]));
+    tot[tp.kind[i]] += t;
+    cnt[tp.kind[i]] += 1;
+  }
+  tp.used = 0;
+  for (int k = 0; k < LCE_K_COUNT; ++k) {
+    if (ms) ms[k] = tot[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return LCE_OK;
+}
+
+lce_status lce_destroy(lce_handle* h) {
+  if (h) lce_timing_enable(h, 0);
+  delete h;
+  return LCE_OK;
+}
+
+lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  if (!h || !io) return LCE_ERR_INVALID_ARG;
+  const lce_desc& d = h->d;
+  const bool none = d.reduction == LCE_NONE;
+  if (!none && io->grad_output) return LCE_ERR_INVALID_ARG;
+  const bool grads = h->want_any && (!none || io->grad_output != nullptr);
+  const bool want_x = grads && h->want_x, want_w = grads && h->want_w,
+             want_b = grads && h->want_b;
+  if (!io->targets && d.N > 0) return LCE_ERR_INVALID_ARG;
+  if (d.N > 0 && (!io->X || !io->W)) return LCE_ERR_INVALID_ARG;
+  if (d.has_bias && !io->b) return LCE_ERR_INVALID_ARG;
+  if (!d.has_bias && io->b) return LCE_ERR_INVALID_ARG;
+  if (!io->loss && !(none && io->grad_output)) return LCE_ERR_INVALID_ARG;
+  if ((want_x && !io->grad_X && d.N > 0) || (want_w && !io->grad_W) || (want_b && !io->grad_b))
+    return LCE_ERR_INVALID_ARG;
+  if (h->want_argmax && !io->argmax && d.N > 0) return LCE_ERR_INVALID_ARG;
+  if ((io->X && !aligned16(io->X)) || (io->W && !aligned16(io->W)))
+    return LCE_ERR_UNSUPPORTED;
+  if (h->total > 0 && (!workspace || ws_bytes < h->total ||
+                       (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))))
+    return LCE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = h->bf16;
+  const int es = h->esize;
+  const int N = static_cast<int>(d.N), D = static_cast<int>(d.D), V = static_cast<int>(d.V);
+  const int64_t cp = h->c_pad, Vp = h->V_pad;
+  void* T = at<char>(workspace, h->o_T);
+  void* dLt = at<char>(workspace, h->o_dLt);
+  void* Wt = at<char>(workspace, h->o_Wt);
+  void* Xt = at<char>(workspace, h->o_Xt);
+  float* mp = at<float>(workspace, h->o_mp);
+  float* sp = at<float>(workspace, h->o_sp);
+  int* ip = at<int>(workspace, h->o_ip);
+  float* zt = at<float>(workspace, h->o_zt);
+  float* lse = at<float>(workspace, h->o_lse);
+  float* g = at<float>(workspace, h->o_g);
+  int* tc = at<int>(workspace, h->o_tc);
+  float* gxp = at<float>(workspace, h->o_gxp);
+  float* gw32 = at<float>(workspace, h->o_gw32);
+  float* gbp = at<float>(workspace, h->o_gbp);
+  float* gb32 = at<float>(workspace, h->o_gb32);
+  float* lrows = at<float>(workspace, h->o_lrows);
+  int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
+
+  LCE_LAUNCH(h, LCE_K_PREP, lce::prep_targets(io->targets, N, V, d.ignore_index, d.reduction, io->grad_scale,
+                            io->grad_output, tc, g, cnt, io->n_valid, io->n_bad, s));
+
+  if (N == 0) {
+    if (want_w) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_W, static_cast<size_t>(d.V) * d.D * es, s));
+    if (want_b) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_b, static_cast<size_t>(d.V) * es, s));
+    if (!none) LCE_LAUNCH(h, LCE_K_LOSS, lce::loss_reduce(lrows, 0, cnt, d.reduction, io->loss, s));
+    return LCE_OK;
+  }
+
+  if (want_x) LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
+
+  const char* Xb = static_cast<const char*>(io->X);
+  for (int64_t ck = 0; ck < h->n_chunks; ++ck) {
+    const int64_t row0 = ck * h->c;
+    const int rows = static_cast<int>(std::min<int64_t>(h->c, d.N - row0));
+    const int rows_pad = static_cast<int>(round_up(rows, 64));
+    const bool first = ck == 0, last = ck + 1 == h->n_chunks;
+    const void* Xc = Xb + row0 * d.D * es;
+
+    lce::LogitsLse la{};
+    la.X = Xc; la.ldx = D;
+    la.W = io->W; la.ldw = D;
+    la.bias = io->b;
+    la.tc = tc + row0;
+    la.rows = rows; la.V = V; la.D = D;
+    la.T = grads ? T : nullptr; la.ldt = Vp;
+    la.m_part = mp; la.s_part = sp; la.i_part = h->want_argmax ? ip : nullptr; la.ldp = cp;
+    la.zt = zt;
+    LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(bf16, la, s));
+
+    float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
+    LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0, rows, lse, loss_rows,
+                             h->want_argmax ? io->argmax + row0 : nullptr, s));
+    if (!grads) continue;
+
+    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, T, Vp, want_w ? dLt : nullptr, cp, mp, cp, lse, g + row0,
+                                  tc + row0, rows, rows_pad, V, static_cast<int>(Vp),
+                                  want_b ? gbp : nullptr, s));
+    if (want_x) {
+      lce::GemmNT gx{};
+      gx.A = T; gx.lda = Vp;
+      gx.B = Wt; gx.ldb = Vp;
+      gx.M = rows; gx.N = D; gx.K = static_cast<int>(Vp);
+      gx.splits = h->splits; gx.k_split = h->k_split;
+      gx.split_stride = static_cast<int64_t>(rows) * D;
+      gx.C = gxp; gx.ldc = D; gx.Cin = nullptr;
+      gx.mode = lce::EpiMode::kStoreF32;
+      gx.group_m = 8;
+      LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(bf16, gx, s));
+      LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(bf16, gxp, h->splits, gx.split_stride, rows, D,
+                              static_cast<char*>(io->grad_X) + row0 * d.D * es, s));
+    }
+    if (want_w) {
+      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, Xc, D, rows, D, Xt, cp, rows_pad, s));
+      lce::GemmNT gw{};
+      gw.A = dLt; gw.lda = cp;
+      gw.B = Xt; gw.ldb = cp;
+      gw.M = V; gw.N = D; gw.K = rows_pad;
+      gw.splits = 1; gw.k_split = rows_pad; gw.split_stride = 0;
+      gw.ldc = D;
+      gw.group_m = 4;
+      if (h->w_acc32) {
+        if (first && last) { gw.C = io->grad_W; gw.mode = lce::EpiMode::kStoreOut; }
+        else if (first) { gw.C = gw32; gw.mode = lce::EpiMode::kStoreF32; }
+        else if (!last) { gw.C = gw32; gw.mode = lce::EpiMode::kAccumF32; }
+        else { gw.C = io->grad_W; gw.Cin = gw32; gw.mode = lce::EpiMode::kFinalOut; }
+      } else {
+        gw.C = io->grad_W;
+        gw.mode = first ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
+      }
+      LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(bf16, gw, s));
+    }
+    if (want_b)
+      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(bf16, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
+                                    last, s));
+  }
+  if (!none) LCE_LAUNCH(h, LCE_K_LOSS, lce::loss_reduce(lrows, N, cnt, d.reduction, io->loss, s));
+  return LCE_OK;
+}
+
+lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes) {
+  if (!bytes || N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
+  const int64_t n = std::max<int64_t>(N, 1);
+  *bytes = align_up(n * 4) * 3 + align_up(16);
+  return LCE_OK;
+}
+
+lce_status lce_ce_inplace(float* logits, const int64_t* targets, int64_t N, int64_t V,
+                          int64_t ignore_index, int32_t reduction, float grad_scale, float* loss,
+                          int64_t* n_valid, void* workspace, size_t ws_bytes, void* stream) {
+  if (N < 0 || V < 1 || reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
+  if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
+  if (!loss) return LCE_ERR_INVALID_ARG;
+  if (V % 4 != 0 || (logits && !aligned16(logits))) return LCE_ERR_UNSUPPORTED;
+  if (N > 2147483647LL || V > 2147483647LL) return LCE_ERR_UNSUPPORTED;
+  size_t need = 0;
+  lce_ce_workspace_size(N, V, &need);
+  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return LCE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = std::max<int64_t>(N, 1);
+  char* ws = static_cast<char*>(workspace);
+  int* tc = reinterpret_cast<int*>(ws);
+  float* g = reinterpret_cast<float*>(ws + align_up(n * 4));
+  float* lrows = reinterpret_cast<float*>(ws + 2 * align_up(n * 4));
+  int64_t* cnt = reinterpret_cast<int64_t*>(ws + 3 * align_up(n * 4));
+  const bool none = reduction == LCE_NONE;
+  // Per-row weights: 'none' takes grad_scale on every counted row, which is
+  // the weight the 'sum' reduction gives.
+  LCE_HIP(lce::prep_targets(targets, static_cast<int>(N), static_cast<int>(V), ignore_index,
+                            none ? LCE_SUM : reduction, grad_scale, nullptr, tc, g, cnt, n_valid,
+                            nullptr, s));
+  LCE_HIP(lce::ce_inplace_rows(logits, static_cast<int>(N), static_cast<int>(V), tc, g,
+                               none ? loss : lrows, s));
+  if (!none) LCE_HIP(lce::loss_reduce(lrows, static_cast<int>(N), cnt, reduction, loss, s));
+  return LCE_OK;
+}
+
+}  // extern "C"

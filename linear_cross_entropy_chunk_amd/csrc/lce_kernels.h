@@ -1,0 +1,110 @@
+// Internal launchers shared by the translation units of liblce.so.
+// Every launcher only enqueues work on `s` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+// Square output tile of every GEMM launch (rows x cols of C per workgroup)
+// and the K depth, in bytes, of one LDS stage row.
+constexpr int kTile = 256;
+constexpr int kStageRowBytes = 128;
+// Rows per K4 finalize / transpose tile.
+constexpr int kSmallTile = 64;
+
+enum class EpiMode : int {
+  kStoreF32 = 0,     // C = acc                      (fp32 out, e.g. split-K parts)
+  kAccumF32 = 1,     // C = C + acc                  (fp32 in/out)
+  kFinalOut = 2,     // out = cvt(C_f32 + acc)       (fp32 in, dtype out)
+  kStoreOut = 3,     // out = cvt(acc)               (dtype out)
+  kAccumOut = 4      // out = cvt(out + acc)         (dtype in/out)
+};
+
+// ---- GEMM (lce_gemm.hip) -------------------------------------------------
+// C[m, n] = sum_k A[m, k] * B[n, k]; A is [M][lda], B is [N][ldb], both with
+// K contiguous ("NT").  K is split into `splits` ranges of k_split elements
+// (a multiple of the stage depth); split s writes C + s * split_stride.
+struct GemmNT {
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  int M, N, K;
+  int splits; int k_split; int64_t split_stride;
+  void* C; int64_t ldc;           // output
+  const void* Cin;                // input of the accumulate modes (ld = ldc)
+  EpiMode mode;
+  int group_m;                    // tile-order grouping along M
+};
+hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
+
+// Logits GEMM with the fused softmax-statistics epilogue.  Computes, for the
+// chunk's rows n < rows and classes v < V, z[n, v] = X[n] . W[v] + b[v]; per
+// 256-class tile k it writes the tile max m_part[k][n], the tile sum of
+// exp(z - m_part) s_part[k][n], the lowest class index attaining the tile max
+// i_part[k][n] (if i_part != null), z[n, tc[n]] into zt[n] (tc[n] < 0: none),
+// and when T != null, T[n][v] = exp(z[n, v] - m_part[k][n]) rounded to the
+// element type, for v < V_pad (0 beyond V).
+struct LogitsLse {
+  const void* X; int64_t ldx;     // chunk rows [rows][D]
+  const void* W; int64_t ldw;     // [V][D]
+  const void* bias;               // [V] or null
+  const int* tc;                  // [rows]
+  int rows, V, D;
+  void* T; int64_t ldt;           // [rows_pad][V_pad] or null
+  float* m_part; float* s_part; int* i_part; int64_t ldp;   // [n_vt][ldp]
+  float* zt;                      // [rows]
+};
+hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s);
+
+// ---- row-wise kernels (lce_rowops.hip) -------------------------------------
+// Target preparation: counts rows, forms corrected targets and row weights.
+//   tc[n] = t[n] if 0 <= t[n] < V and t[n] != ignore_index, else -1
+//   g[n]  = per-row weight of the reduction (see lce.h)
+// counts[0] = n_valid, counts[1] = n_bad (also copied to the optional outs).
+hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index,
+                        int reduction, float grad_scale, const float* upstream,
+                        int* tc, float* g, int64_t* counts, int64_t* n_valid_out,
+                        int64_t* n_bad_out, hipStream_t s);
+
+// Row combine over the n_vt class tiles of a chunk: lse[n] (chunk-local),
+// loss_rows[n] = lse - zt (0 if tc < 0), argmax_out[n] if non-null.
+hipError_t row_combine(const float* m_part, const float* s_part, const int* i_part,
+                       int64_t ldp, int n_vt, const float* zt, const int* tc,
+                       int rows, float* lse, float* loss_rows, int* argmax_out,
+                       hipStream_t s);
+
+// In-place finalize: T[n][v] <- dL = g_n (T * exp(m_part[v/256][n] - lse_n)
+// - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V);
+// optionally writes dLt[v][n] (ld = ldlt) and per-64-row column partials
+// gb_part[n/64][v] (ld = V_pad).
+hipError_t finalize_dlogits(bool bf16, void* T, int64_t ldt, void* dLt, int64_t ldlt,
+                            const float* m_part, int64_t ldp, const float* lse,
+                            const float* g, const int* tc, int rows, int rows_pad,
+                            int V, int V_pad, float* gb_part, hipStream_t s);
+
+// out[c][r] = r < rows ? in[r][c] : 0 for r < rows_pad, c < cols.
+hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int cols,
+                         void* out, int64_t ldo, int rows_pad, hipStream_t s);
+
+// out[r][c] = cvt(sum_s parts[s][r][c]) for r < rows, c < cols (ld = cols).
+hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride,
+                      int rows, int cols, void* out, hipStream_t s);
+
+// acc[v] = (first ? 0 : acc[v]) + sum_b parts[b][v]; if last: out[v] = cvt(acc).
+hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp,
+                            int V, float* acc, void* out, bool first, bool last,
+                            hipStream_t s);
+
+// Final loss: mean (sum / n_valid, NaN when 0) or sum, in float64, fixed order.
+hipError_t loss_reduce(const float* loss_rows, int N, const int64_t* counts,
+                       int reduction, float* loss, hipStream_t s);
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Standalone CE: rows of fp32 logits overwritten with g_n (softmax - onehot);
+// loss_rows[n] = lse - z_t (0 if tc < 0).
+hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
+                           float* loss_rows, hipStream_t s);
+
+}  // namespace lce

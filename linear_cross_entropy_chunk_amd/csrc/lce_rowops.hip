@@ -1,0 +1,474 @@
+// Row-wise and memory-bound kernels of the chunked linear-cross-entropy path:
+// target preparation, the per-row combine of the tile statistics, the in-place
+// finalize of the logits gradient, padded transposes, deterministic
+// reductions, and the standalone softmax cross-entropy that overwrites its
+// logits with the gradient.
+//
+// Sources: torch/nn/modules/linear_cross_entropy.py (_ChunkContext._mask,
+// corrected_target and neg_weight_target for the row weights; the chunk loop's
+// amax / sumexp / log / "output -=" steps for the loss; the in-place
+// softmax * weight step and the one-hot corrections for the gradient; the
+// empty-mean NaN fill) and Liger-Kernel issue #343 (cross entropy computed
+// and its gradient written over the logits in one kernel).
+#include "lce_kernels.h"
+
+#include <math.h>
+
+namespace lce {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float to_f32(float f) { return f; }
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// ------------------------------------------------------------ target prep
+// One workgroup: the mean's denominator must be known before any row weight.
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep(
+    const int64_t* __restrict__ t, int N, int V, int64_t ign, int reduction,
+    float grad_scale, const float* __restrict__ upstream, int* __restrict__ tc,
+    float* __restrict__ g, int64_t* __restrict__ counts, int64_t* n_valid_out,
+    int64_t* n_bad_out) {
+  __shared__ long long s_valid[kPrepThreads / 64], s_bad[kPrepThreads / 64];
+  __shared__ long long tot[2];
+  long long cv = 0, cb = 0;
+  for (int n = threadIdx.x; n < N; n += kPrepThreads) {
+    const int64_t x = t[n];
+    const bool ignored = x == ign;
+    const bool bad = !ignored && (x < 0 || x >= V);
+    cv += (!ignored && !bad) ? 1 : 0;
+    cb += bad ? 1 : 0;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    cv += __shfl_xor(cv, o);
+    cb += __shfl_xor(cb, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_valid[threadIdx.x >> 6] = cv;
+    s_bad[threadIdx.x >> 6] = cb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long a = 0, b = 0;
+    for (int w = 0; w < kPrepThreads / 64; ++w) {
+      a += s_valid[w];
+      b += s_bad[w];
+    }
+    tot[0] = a;
+    tot[1] = b;
+    counts[0] = a;
+    counts[1] = b;
+    if (n_valid_out) *n_valid_out = a;
+    if (n_bad_out) *n_bad_out = b;
+  }
+  __syncthreads();
+  const long long nv = tot[0];
+  // reduction codes follow lce.h: 0 mean, 1 sum, 2 none
+  const bool mean_nan = reduction == 0 && nv == 0;
+  const float gmean = nv > 0 ? grad_scale / static_cast<float>(nv) : 0.0f;
+  for (int n = threadIdx.x; n < N; n += kPrepThreads) {
+    const int64_t x = t[n];
+    const bool valid = x != ign && x >= 0 && x < V;
+    tc[n] = valid ? static_cast<int>(x) : -1;
+    float w;
+    if (mean_nan) w = NAN;
+    else if (!valid) w = 0.0f;
+    else if (reduction == 0) w = gmean;
+    else if (reduction == 1) w = grad_scale;
+    else w = upstream ? upstream[n] : 1.0f;
+    g[n] = w;
+  }
+}
+
+// ------------------------------------------------------------ row combine
+// 32 rows x 8 parts per workgroup; part p folds class tiles p, p + 8, ...
+__global__ __launch_bounds__(256) void k_row_combine(
+    const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
+    int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
+    int rows, float* __restrict__ lse, float* __restrict__ loss_rows, int* __restrict__ amax) {
+  __shared__ float sm[8][32], ss[8][32];
+  __shared__ int sk[8][32];
+  const int r = threadIdx.x & 31, p = threadIdx.x >> 5;
+  const int n = blockIdx.x * 32 + r;
+  float m = -INFINITY, s = 0.0f;
+  int kb = 0x7fffffff;
+  if (n < rows) {
+    for (int k = p; k < n_vt; k += 8) {
+      const float mk = mp[k * ldp + n];
+      const float sk_ = sp[k * ldp + n];
+      if (mk > m) {
+        s = s * expf(m - mk) + sk_;
+        m = mk;
+        kb = k;
+      } else {
+        s += sk_ * expf(mk - m);
+      }
+    }
+  }
+  sm[p][r] = m;
+  ss[p][r] = s;
+  sk[p][r] = kb;
+  __syncthreads();
+  if (p == 0 && n < rows) {
+    float M = sm[0][r];
+    for (int q = 1; q < 8; ++q) M = fmaxf(M, sm[q][r]);
+    float S = 0.0f;
+    int K = 0x7fffffff;
+    for (int q = 0; q < 8; ++q) {
+      if (sm[q][r] > -INFINITY) S += ss[q][r] * expf(sm[q][r] - M);
+      if (sm[q][r] == M && sk[q][r] < K) K = sk[q][r];
+    }
+    const float L = M + logf(S);
+    lse[n] = L;
+    loss_rows[n] = tc[n] >= 0 ? L - zt[n] : 0.0f;
+    // K stays unset only if every tile maximum is NaN; read tile 0 then.
+    if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
+  }
+}
+
+// ------------------------------------------------------- in-place finalize
+// 64 rows x 64 classes per workgroup; the 64 classes sit in one 256-class
+// statistics tile.  Writes dL over T, dL^T into dLt, and column partials.
+template <typename T>
+__global__ __launch_bounds__(256) void k_finalize(
+    T* __restrict__ Tm, int64_t ldt, T* __restrict__ dLt, int64_t ldlt,
+    const float* __restrict__ mp, int64_t ldp, const float* __restrict__ lse,
+    const float* __restrict__ g, const int* __restrict__ tc, int rows, int V,
+    int64_t ldgb, float* __restrict__ gbp) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kVecPerRow = 64 / kVec;
+  __shared__ float tile[64][65];
+  __shared__ float sc[64], gg[64];
+  __shared__ int tt[64];
+  const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int k = v0 >> 8;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int n = n0 + tid;
+    const bool in = n < rows;
+    const float gn = in ? g[n] : 0.0f;
+    sc[tid] = in ? gn * expf(mp[static_cast<int64_t>(k) * ldp + n] - lse[n]) : 0.0f;
+    gg[tid] = gn;
+    tt[tid] = in ? tc[n] : -1;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
+    const int n = n0 + rl;
+    const int vb = v0 + cv * kVec;
+    T* p = Tm + static_cast<int64_t>(n) * ldt + vb;
+    i32x4_t raw = *reinterpret_cast<const i32x4_t*>(p);
+    const T* x = reinterpret_cast<const T*>(&raw);
+    i32x4_t outv;
+    T* y = reinterpret_cast<T*>(&outv);
+    const bool nin = n < rows;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const int v = vb + e;
+      float d = 0.0f;
+      if (nin && v < V) d = sc[rl] * to_f32(x[e]) - (v == tt[rl] ? gg[rl] : 0.0f);
+      tile[rl][cv * kVec + e] = d;
+      y[e] = from_f32<T>(d);
+    }
+    *reinterpret_cast<i32x4_t*>(p) = outv;
+  }
+  if (dLt == nullptr && gbp == nullptr) return;
+  __syncthreads();
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int vl = idx / kVecPerRow, nv = idx % kVecPerRow;
+    i32x4_t outv;
+    T* y = reinterpret_cast<T*>(&outv);
+    float part = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float d = tile[nv * kVec + e][vl];
+      part += d;
+      y[e] = from_f32<T>(d);
+    }
+    if (dLt) *reinterpret_cast<i32x4_t*>(dLt + static_cast<int64_t>(v0 + vl) * ldlt + n0 + nv * kVec) = outv;
+    if (gbp) {
+#pragma unroll
+      for (int o = 1; o < kVecPerRow; o <<= 1) part += __shfl_xor(part, o);
+      if (nv == 0) gbp[static_cast<int64_t>(blockIdx.y) * ldgb + v0 + vl] = part;
+    }
+  }
+}
+
+// ------------------------------------------------------- padded transpose
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_pad(const T* __restrict__ in, int64_t ldi,
+                                                      int rows, int cols, T* __restrict__ out,
+                                                      int64_t ldo, int rows_pad) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kVecPerRow = 64 / kVec;
+  __shared__ T tile[64][64 + kVec];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
+    const int r = r0 + rl, c = c0 + cv * kVec;
+    i32x4_t raw = i32x4_t{0, 0, 0, 0};
+    if (r < rows && c < cols) raw = *reinterpret_cast<const i32x4_t*>(in + static_cast<int64_t>(r) * ldi + c);
+    const T* x = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) tile[rl][cv * kVec + e] = x[e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+    const int cl = idx / kVecPerRow, rv = idx % kVecPerRow;
+    const int c = c0 + cl, r = r0 + rv * kVec;
+    if (c >= cols || r >= rows_pad) continue;
+    i32x4_t outv;
+    T* y = reinterpret_cast<T*>(&outv);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) y[e] = tile[rv * kVec + e][cl];
+    *reinterpret_cast<i32x4_t*>(out + static_cast<int64_t>(c) * ldo + r) = outv;
+  }
+}
+
+// ---------------------------------------------------- split-K reduction
+template <typename T>
+__global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ parts, int splits,
+                                                   int64_t stride, int64_t count4,
+                                                   T* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count4) return;
+  f32x4_t acc = reinterpret_cast<const f32x4_t*>(parts)[i];
+  for (int s = 1; s < splits; ++s) acc += reinterpret_cast<const f32x4_t*>(parts + s * stride)[i];
+  if constexpr (sizeof(T) == 4) {
+    reinterpret_cast<f32x4_t*>(out)[i] = acc;
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + 4 * i;
+    uint2 pk;
+    pk.x = static_cast<uint32_t>(from_f32<uint16_t>(acc[0])) |
+           (static_cast<uint32_t>(from_f32<uint16_t>(acc[1])) << 16);
+    pk.y = static_cast<uint32_t>(from_f32<uint16_t>(acc[2])) |
+           (static_cast<uint32_t>(from_f32<uint16_t>(acc[3])) << 16);
+    *reinterpret_cast<uint2*>(o) = pk;
+  }
+}
+
+// ---------------------------------------------------- bias gradient
+template <typename T>
+__global__ __launch_bounds__(256) void k_bias_reduce(const float* __restrict__ parts, int nparts,
+                                                    int64_t ldp, int V, float* __restrict__ acc,
+                                                    T* __restrict__ out, int first, int last) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  float a = first ? 0.0f : acc[v];
+  for (int b = 0; b < nparts; ++b) a += parts[static_cast<int64_t>(b) * ldp + v];
+  if (last) out[v] = from_f32<T>(a);
+  else acc[v] = a;
+}
+
+// ---------------------------------------------------- loss reduction
+constexpr int kLossThreads = 1024;
+__global__ __launch_bounds__(kLossThreads) void k_loss_reduce(const float* __restrict__ lr, int N,
+                                                             const int64_t* __restrict__ counts,
+                                                             int reduction, float* __restrict__ loss) {
+  __shared__ double part[kLossThreads];
+  double s = 0.0;
+  for (int n = threadIdx.x; n < N; n += kLossThreads) s += static_cast<double>(lr[n]);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kLossThreads / 2; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double L = part[0];
+    if (reduction == 0) {
+      const long long nv = counts[0];
+      L = nv > 0 ? L / static_cast<double>(nv) : NAN;
+    }
+    loss[0] = static_cast<float>(L);
+  }
+}
+
+__global__ void k_fill_zero(i32x4_t* __restrict__ p, int64_t n16, char* __restrict__ tail,
+                            int tail_bytes) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n16) p[i] = i32x4_t{0, 0, 0, 0};
+  if (i < tail_bytes) tail[i] = 0;
+}
+
+// ---------------------------------------------------- standalone CE
+// One workgroup per row.  Pass 1 streams the row with 16-byte loads keeping
+// an online (max, sum of exp); pass 2 streams it again and overwrites it with
+// g_n (softmax - onehot).  The target logit is read before any overwrite.
+constexpr int kCeThreads = 1024;
+__global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, int V,
+                                                       const int* __restrict__ tc,
+                                                       const float* __restrict__ g,
+                                                       float* __restrict__ loss_rows) {
+  __shared__ float wm[kCeThreads / 64], wsum[kCeThreads / 64];
+  __shared__ float bcast[2];
+  const int n = blockIdx.x;
+  f32x4_t* row = reinterpret_cast<f32x4_t*>(z + static_cast<int64_t>(n) * V);
+  const int V4 = V >> 2;
+  const int t = tc[n];
+  float m = -INFINITY, s = 0.0f;
+  for (int i = threadIdx.x; i < V4; i += kCeThreads) {
+    const f32x4_t x = row[i];
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (mx > m) {
+      s *= fast_exp(m - mx);
+      m = mx;
+    }
+    s += fast_exp(x[0] - m) + fast_exp(x[1] - m) + fast_exp(x[2] - m) + fast_exp(x[3] - m);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
+    const float M = fmaxf(m, om);
+    s = (m > -INFINITY ? s * fast_exp(m - M) : 0.0f) + (om > -INFINITY ? os * fast_exp(om - M) : 0.0f);
+    m = M;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wm[threadIdx.x >> 6] = m;
+    wsum[threadIdx.x >> 6] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = wm[0];
+    for (int w = 1; w < kCeThreads / 64; ++w) M = fmaxf(M, wm[w]);
+    float S = 0.0f;
+    for (int w = 0; w < kCeThreads / 64; ++w)
+      if (wm[w] > -INFINITY) S += wsum[w] * expf(wm[w] - M);
+    const float L = M + logf(S);
+    const float zt = t >= 0 ? z[static_cast<int64_t>(n) * V + t] : 0.0f;
+    loss_rows[n] = t >= 0 ? L - zt : 0.0f;
+    bcast[0] = L;
+  }
+  __syncthreads();
+  const float L = bcast[0];
+  const float gn = g[n];
+  for (int i = threadIdx.x; i < V4; i += kCeThreads) {
+    const f32x4_t x = row[i];
+    f32x4_t y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = gn * fast_exp(x[e] - L);
+      if (4 * i + e == t) y[e] -= gn;
+    }
+    __builtin_nontemporal_store(y, row + i);
+  }
+}
+
+inline unsigned cdiv_u(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+}  // namespace
+
+hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index, int reduction,
+                        float grad_scale, const float* upstream, int* tc, float* g,
+                        int64_t* counts, int64_t* n_valid_out, int64_t* n_bad_out,
+                        hipStream_t s) {
+  k_prep<<<1, kPrepThreads, 0, s>>>(t, N, V, ignore_index, reduction, grad_scale, upstream, tc,
+                                    g, counts, n_valid_out, n_bad_out);
+  return hipGetLastError();
+}
+
+hipError_t row_combine(const float* m_part, const float* s_part, const int* i_part, int64_t ldp,
+                       int n_vt, const float* zt, const int* tc, int rows, float* lse,
+                       float* loss_rows, int* argmax_out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  k_row_combine<<<cdiv_u(rows, 32), 256, 0, s>>>(m_part, s_part, i_part, ldp, n_vt, zt, tc, rows,
+                                                 lse, loss_rows, argmax_out);
+  return hipGetLastError();
+}
+
+hipError_t finalize_dlogits(bool bf16, void* T, int64_t ldt, void* dLt, int64_t ldlt,
+                            const float* m_part, int64_t ldp, const float* lse, const float* g,
+                            const int* tc, int rows, int rows_pad, int V, int V_pad,
+                            float* gb_part, hipStream_t s) {
+  if (rows_pad <= 0) return hipSuccess;
+  const dim3 grid(V_pad / 64, rows_pad / 64);
+  if (bf16)
+    k_finalize<uint16_t><<<grid, 256, 0, s>>>(static_cast<uint16_t*>(T), ldt,
+                                              static_cast<uint16_t*>(dLt), ldlt, m_part, ldp, lse,
+                                              g, tc, rows, V, V_pad, gb_part);
+  else
+    k_finalize<float><<<grid, 256, 0, s>>>(static_cast<float*>(T), ldt, static_cast<float*>(dLt),
+                                           ldlt, m_part, ldp, lse, g, tc, rows, V, V_pad, gb_part);
+  return hipGetLastError();
+}
+
+hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int cols, void* out,
+                         int64_t ldo, int rows_pad, hipStream_t s) {
+  if (rows_pad <= 0 || cols <= 0) return hipSuccess;
+  const dim3 grid(cdiv_u(cols, 64), cdiv_u(rows_pad, 64));
+  if (bf16)
+    k_transpose_pad<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in), ldi, rows,
+                                                   cols, static_cast<uint16_t*>(out), ldo,
+                                                   rows_pad);
+  else
+    k_transpose_pad<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), ldi, rows, cols,
+                                                static_cast<float*>(out), ldo, rows_pad);
+  return hipGetLastError();
+}
+
+hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride, int rows,
+                      int cols, void* out, hipStream_t s) {
+  const int64_t count4 = static_cast<int64_t>(rows) * cols / 4;
+  if (count4 <= 0) return hipSuccess;
+  if (bf16_out)
+    k_sum_splits<uint16_t><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
+                                                               static_cast<uint16_t*>(out));
+  else
+    k_sum_splits<float><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
+                                                            static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp, int V,
+                            float* acc, void* out, bool first, bool last, hipStream_t s) {
+  if (V <= 0) return hipSuccess;
+  if (bf16_out)
+    k_bias_reduce<uint16_t><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
+                                                           static_cast<uint16_t*>(out), first,
+                                                           last);
+  else
+    k_bias_reduce<float><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
+                                                        static_cast<float*>(out), first, last);
+  return hipGetLastError();
+}
+
+hipError_t loss_reduce(const float* loss_rows, int N, const int64_t* counts, int reduction,
+                       float* loss, hipStream_t s) {
+  k_loss_reduce<<<1, kLossThreads, 0, s>>>(loss_rows, N, counts, reduction, loss);
+  return hipGetLastError();
+}
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  const int tail = static_cast<int>(bytes % 16);
+  const int64_t work = n16 > tail ? n16 : tail;
+  k_fill_zero<<<cdiv_u(work, 256), 256, 0, s>>>(static_cast<i32x4_t*>(p), n16,
+                                                static_cast<char*>(p) + n16 * 16, tail);
+  return hipGetLastError();
+}
+
+hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
+                           float* loss_rows, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  return hipGetLastError();
+}
+
+}  // namespace lce

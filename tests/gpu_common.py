@@ -1,0 +1,141 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI, and compare with the fp64 oracle to the stated
+tolerances.
+
+Tolerances (one per input dtype; bf16 inputs accumulate in fp32):
+  loss            |dL| / |L|                      f32 1e-5   bf16 5e-3
+  per-row loss    max |d loss_n| / max |loss_n|   f32 1e-5   bf16 5e-3
+  each gradient   max |dG| / max |G_ref|          f32 1e-4   bf16 2e-2
+  n_valid, n_bad  bit-exact
+  argmax          bit-exact where the oracle's top-2 gap exceeds
+                  1e-4 * max(1, |row max|); elsewhere the GPU's class must
+                  lie within that margin of the row max (a valid near-tie).
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+from linear_cross_entropy_chunk_amd import CrossEntropyInplace, LinearCrossEntropy
+
+TOL = {"f32": {"loss": 1e-5, "grad": 1e-4}, "bf16": {"loss": 5e-3, "grad": 2e-2}}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+ARGMAX_MARGIN = 1e-4
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu() -> None:
+    assert torch.cuda.is_available(), "the GPU tests need an MI355X"
+
+
+def to_dev(a, dt: str):
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(TORCH_DT[dt])
+
+
+def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0,
+            acc_policy: str = "accurate", ignore_index: int = -100, grads: str = "xwb",
+            argmax: bool = True, upstream=None, grad_scale: float = 1.0, bias: bool | None = None,
+            repeat: int = 1) -> dict | list:
+    X, W, b, t = case["X"], case["W"], case["b"], case["t"]
+    if bias is False:
+        b = None
+    N, D = X.shape
+    V = W.shape[0]
+    op = LinearCrossEntropy(N, D, V, TORCH_DT[dt], bias=b is not None, reduction=reduction,
+                            ignore_index=ignore_index, chunk_rows=chunk_rows,
+                            acc_policy=acc_policy, grad_x="x" in grads, grad_w="w" in grads,
+                            grad_b=("b" in grads) and b is not None, argmax=argmax)
+    Xd, Wd, bd = to_dev(X, dt), to_dev(W, dt), to_dev(b, dt)
+    td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
+    ud = None if upstream is None else torch.from_numpy(
+        np.ascontiguousarray(upstream, dtype=np.float32)).to("cuda")
+    results = []
+    for _ in range(repeat):
+        out = op(Xd, Wd, td, bd, grad_output=ud, grad_scale=grad_scale)
+        torch.cuda.synchronize()
+        res = {}
+        for k, v in out.items():
+            res[k] = v.cpu().numpy() if v.dtype in (torch.int32, torch.int64) else \
+                v.float().cpu().numpy().astype(np.float64)
+        res["chunk_rows"] = op.chunk_rows
+        results.append(res)
+    return results[0] if repeat == 1 else results
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def check_loss(got, ref, dt: str, reduction: str) -> float:
+    if reduction == "none":
+        e = rel_err(got, ref)
+    else:
+        got, ref = float(np.asarray(got).reshape(-1)[0]), float(ref)
+        e = abs(got - ref) / max(abs(ref), 1e-6)
+    assert e <= TOL[dt]["loss"], f"loss error {e:.3e} > {TOL[dt]['loss']}"
+    return e
+
+
+def check_grad(got, ref, dt: str, name: str) -> float:
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    e = rel_err(got, ref)
+    assert e <= TOL[dt]["grad"], f"{name} error {e:.3e} > {TOL[dt]['grad']}"
+    return e
+
+
+def check_argmax(got, ref, gap, rowmax, z_at_got) -> int:
+    """Exact where the oracle's top-2 gap is clear; a valid near-max class
+    elsewhere.  Returns the number of near-tie rows."""
+    margin = ARGMAX_MARGIN * np.maximum(1.0, np.abs(rowmax))
+    clear = gap > margin
+    bad = np.nonzero(clear & (got != ref))[0]
+    assert bad.size == 0, f"argmax differs on clear rows {bad[:10]}"
+    near = ~clear
+    if near.any():
+        assert np.all(z_at_got[near] >= rowmax[near] - margin[near])
+    return int(near.sum())
+
+
+def check_all(gpu: dict, ref: dict, dt: str, reduction: str, z=None, grads="xwb") -> dict:
+    errs = {"loss": check_loss(gpu["loss"], ref["loss"], dt, reduction)}
+    assert int(gpu["n_valid"][0]) == ref["n_valid"]
+    assert int(gpu["n_bad"][0]) == ref["n_bad"]
+    for key, flag in (("grad_X", "x"), ("grad_W", "w"), ("grad_b", "b")):
+        if key in gpu and flag in grads:
+            errs[key] = check_grad(gpu[key], ref[key], dt, key)
+    if "argmax" in gpu and z is not None and z.shape[0]:
+        zs = np.sort(z, axis=1)
+        gap = zs[:, -1] - zs[:, -2] if z.shape[1] > 1 else np.full(z.shape[0], np.inf)
+        z_at = z[np.arange(z.shape[0]), gpu["argmax"]]
+        check_argmax(gpu["argmax"], ref["argmax"], gap, zs[:, -1], z_at)
+    return errs
+
+
+def run_ce(z: np.ndarray, t: np.ndarray, *, reduction: str = "mean", ignore_index: int = -100,
+           grad_scale: float = 1.0):
+    zd = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to("cuda")
+    td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
+    op = CrossEntropyInplace(z.shape[0], z.shape[1], reduction=reduction,
+                             ignore_index=ignore_index)
+    loss, nv = op(zd, td, grad_scale)
+    torch.cuda.synchronize()
+    return (loss.cpu().numpy().astype(np.float64), int(nv.cpu()[0]),
+            zd.cpu().numpy().astype(np.float64))
+
+
+__all__ = ["TOL", "log", "require_gpu", "run_gpu", "check_all", "check_loss", "check_grad",
+           "check_argmax", "rel_err", "run_ce", "oracle"]

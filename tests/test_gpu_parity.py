@@ -1,0 +1,199 @@
+"""GPU parity of the chunked fused path against the fp64 oracle, element by
+element, at sizes the oracle finishes in seconds: the tiny fp32 and mid bf16
+workloads, every chunk size from 1 row to all rows, ragged vocabularies,
+every reduction, the degenerate cases (all rows ignored, no rows, targets out
+of range, ignore_index inside the class range), output subsets, determinism
+and both grad_W accumulation policies."""
+import math
+
+import numpy as np
+import pytest
+
+import lce_inputs as li
+from gpu_common import check_all, check_grad, check_loss, log, oracle, rel_err, require_gpu, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(case, reduction="mean", ignore_index=-100, upstream=None, grad_scale=1.0, bias=True):
+    return oracle.linear_cross_entropy(case["X"], case["W"], case["b"] if bias else None,
+                                       case["t"], ignore_index=ignore_index, reduction=reduction,
+                                       upstream=upstream, grad_scale=grad_scale)
+
+
+def _z(case, bias=True):
+    return oracle.logits(case["X"], case["W"], case["b"] if bias else None)
+
+
+def test_tiny_f32_workload():
+    """N=256, D=64, V=1000, fp32, bias, 26 ignored rows, mean, 64-row chunks."""
+    require_gpu()
+    cfg = li.TINY_F32
+    case = li.lce_inputs(cfg)
+    log(f"tiny-f32 N={cfg.N} D={cfg.D} V={cfg.V} chunk={cfg.chunk_rows}")
+    gpu = run_gpu(case, "f32", reduction="mean", chunk_rows=cfg.chunk_rows)
+    assert gpu["chunk_rows"] == 64
+    errs = check_all(gpu, _ref(case), "f32", "mean", z=_z(case))
+    log(f"tiny-f32 errors {errs}")
+
+
+def test_mid_bf16_workload():
+    """N=4096, D=2048, V=32000, bf16, no bias, 205 ignored rows, mean,
+    1024-row chunks, fp32 accumulation."""
+    require_gpu()
+    cfg = li.MID_BF16
+    case = li.lce_inputs(cfg)
+    log(f"mid-bf16 N={cfg.N} D={cfg.D} V={cfg.V} chunk={cfg.chunk_rows}")
+    gpu = run_gpu(case, "bf16", reduction="mean", chunk_rows=cfg.chunk_rows)
+    ref = _ref(case, bias=False)
+    errs = check_all(gpu, ref, "bf16", "mean", z=_z(case, bias=False))
+    assert int(gpu["n_valid"][0]) == cfg.N - 205
+    log(f"mid-bf16 errors {errs}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk_rows", [1, 3, 64, 300, -1, 0])
+def test_any_chunk_size_gives_the_unchunked_result(dt, chunk_rows):
+    require_gpu()
+    case = li.small_case(300, 64, 1000, dtype=dt, seed=3, ignore_frac=0.1)
+    log(f"chunks dt={dt} chunk_rows={chunk_rows}")
+    gpu = run_gpu(case, dt, chunk_rows=chunk_rows)
+    check_all(gpu, _ref(case), dt, "mean", z=_z(case))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 7, 255, 257, 1000, 2049])
+def test_ragged_vocab(dt, V):
+    require_gpu()
+    case = li.small_case(130, 32, V, dtype=dt, seed=V, ignore_frac=0.1)
+    log(f"ragged V={V} dt={dt}")
+    gpu = run_gpu(case, dt, chunk_rows=50)
+    check_all(gpu, _ref(case), dt, "mean", z=_z(case))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_reductions(dt, reduction):
+    require_gpu()
+    case = li.small_case(333, 128, 777, dtype=dt, seed=5, ignore_frac=0.15)
+    log(f"reduction={reduction} dt={dt}")
+    if reduction == "none":
+        fwd = run_gpu(case, dt, reduction="none", chunk_rows=100)
+        ref = _ref(case, "none")
+        check_loss(fwd["loss"], ref["loss"], dt, "none")
+        assert "grad_W" not in fwd
+        bwd = run_gpu(case, dt, reduction="none", chunk_rows=100, upstream=case["u"])
+        ref = _ref(case, "none", upstream=case["u"])
+        check_all(bwd, ref, dt, "none", z=_z(case))
+    else:
+        gpu = run_gpu(case, dt, reduction=reduction, chunk_rows=100, grad_scale=0.75)
+        check_all(gpu, _ref(case, reduction, grad_scale=0.75), dt, reduction, z=_z(case))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ignore_index_inside_class_range(dt):
+    require_gpu()
+    case = li.small_case(200, 64, 50, dtype=dt, seed=9, ignore_frac=0.0)
+    log(f"ignore_index=7 dt={dt}")
+    gpu = run_gpu(case, dt, ignore_index=7, chunk_rows=64)
+    ref = _ref(case, ignore_index=7)
+    check_all(gpu, ref, dt, "mean", z=_z(case))
+    ign = case["t"] == 7
+    assert ign.any() and np.all(gpu["grad_X"][ign] == 0.0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_all_rows_ignored(dt):
+    require_gpu()
+    case = li.small_case(100, 32, 300, dtype=dt, seed=11, ignore_frac=1.0)
+    log(f"all ignored dt={dt}")
+    gm = run_gpu(case, dt, reduction="mean", chunk_rows=40)
+    assert math.isnan(gm["loss"][0]) and int(gm["n_valid"][0]) == 0
+    for k in ("grad_X", "grad_W", "grad_b"):
+        assert np.all(np.isnan(gm[k])), k
+    gs = run_gpu(case, dt, reduction="sum", chunk_rows=40)
+    assert gs["loss"][0] == 0.0
+    for k in ("grad_X", "grad_W", "grad_b"):
+        assert np.all(gs[k] == 0.0), k
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_empty_batch(dt):
+    require_gpu()
+    case = li.small_case(0, 32, 300, dtype=dt, seed=12)
+    gm = run_gpu(case, dt, reduction="mean")
+    assert math.isnan(gm["loss"][0]) and int(gm["n_valid"][0]) == 0
+    assert gm["grad_X"].shape == (0, 32)
+    assert np.all(gm["grad_W"] == 0.0) and np.all(gm["grad_b"] == 0.0)
+    gs = run_gpu(case, dt, reduction="sum")
+    assert gs["loss"][0] == 0.0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_out_of_range_targets_are_counted(dt):
+    require_gpu()
+    case = li.small_case(150, 32, 100, dtype=dt, seed=13, ignore_frac=0.1)
+    t = case["t"].copy()
+    t[[3, 40, 99]] = [100, -5, 10**12]
+    case = {**case, "t": t}
+    gpu = run_gpu(case, dt, chunk_rows=64)
+    ref = _ref(case)
+    assert ref["n_bad"] == 3 and int(gpu["n_bad"][0]) == 3
+    check_all(gpu, ref, dt, "mean", z=_z(case))
+    assert np.all(gpu["grad_X"][[3, 40, 99]] == 0.0)
+
+
+@pytest.mark.parametrize("grads", ["", "x", "w", "b", "xw", "wb"])
+def test_output_subsets(grads):
+    require_gpu()
+    case = li.small_case(260, 64, 600, dtype="bf16", seed=14)
+    gpu = run_gpu(case, "bf16", chunk_rows=128, grads=grads, argmax=False)
+    ref = _ref(case)
+    check_all(gpu, ref, "bf16", "mean", grads=grads)
+    for key, flag in (("grad_X", "x"), ("grad_W", "w"), ("grad_b", "b")):
+        assert (key in gpu) == (flag in grads)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_runs_are_bit_identical(dt):
+    require_gpu()
+    case = li.small_case(700, 128, 3000, dtype=dt, seed=15)
+    a, b = run_gpu(case, dt, chunk_rows=256, repeat=2)
+    for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax", "n_valid"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_accurate_and_compact_policies():
+    """Both grad_W accumulation policies meet the bf16 tolerance; accurate
+    rounds once, so its grad_W error is not larger than compact's."""
+    require_gpu()
+    case = li.small_case(2048, 256, 4000, dtype="bf16", seed=16)
+    ref = _ref(case)
+    acc = run_gpu(case, "bf16", chunk_rows=128, acc_policy="accurate")
+    cmp_ = run_gpu(case, "bf16", chunk_rows=128, acc_policy="compact")
+    ea = check_all(acc, ref, "bf16", "mean")
+    ec = check_all(cmp_, ref, "bf16", "mean")
+    log(f"grad_W error accurate {ea['grad_W']:.3e} compact {ec['grad_W']:.3e}")
+    assert ea["grad_W"] <= ec["grad_W"] * 1.05
+
+
+def test_zero_weight_closed_form_on_gpu():
+    """W = 0, b = 0: loss = log V exactly (to fp32), argmax = 0 on every row,
+    grad_X = 0 exactly."""
+    require_gpu()
+    case = li.small_case(300, 64, 1000, dtype="bf16", seed=17, bias=True)
+    case = {**case, "W": np.zeros_like(case["W"]), "b": np.zeros_like(case["b"])}
+    gpu = run_gpu(case, "bf16", chunk_rows=128)
+    assert abs(gpu["loss"][0] - math.log(1000)) <= 1e-6 * math.log(1000)
+    assert np.all(gpu["argmax"] == 0)
+    assert np.all(gpu["grad_X"] == 0.0)
+
+
+def test_row_sums_of_grads_vanish():
+    """Every dL row sums to 0, so sum_v grad_b[v] and sum_v grad_W[v, :] vanish
+    up to rounding, on the GPU outputs themselves."""
+    require_gpu()
+    case = li.small_case(512, 64, 2000, dtype="f32", seed=18)
+    gpu = run_gpu(case, "f32", reduction="sum", chunk_rows=128)
+    assert abs(gpu["grad_b"].sum()) <= 1e-4 * np.abs(gpu["grad_b"]).sum()
+    assert np.all(np.abs(gpu["grad_W"].sum(0)) <= 1e-4 * np.abs(gpu["grad_W"]).sum(0))
