@@ -1,0 +1,189 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle evaluates the plain definition on sampled
+outputs: per-row loss, argmax and grad_X on sampled rows (each depends on its
+row only), grad_W / grad_b on sampled classes (sums over every row, so the
+oracle walks all rows in blocks), and the mean loss over all rows; plus
+properties that hold at any size (every dL row sums to zero)."""
+import numpy as np
+import pytest
+import torch
+
+import lce_inputs as li
+from gpu_common import TOL, check_argmax, log, oracle, rel_err, require_gpu
+from linear_cross_entropy_chunk_amd import CrossEntropyInplace, LinearCrossEntropy
+
+pytestmark = pytest.mark.gpu
+
+ROW_BLOCK = 512
+
+
+def _sample_rows(N, t, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, k, replace=False).tolist())
+    rows |= {0, 1, N - 1, N - 2}
+    ign = np.nonzero(t == -100)[0]
+    if ign.size:
+        rows |= set(ign[:3].tolist())
+    return np.array(sorted(rows))
+
+
+def _sample_cols(V, t, k=24, seed=1):
+    rng = np.random.default_rng(seed)
+    cols = set(rng.choice(V, k, replace=False).tolist()) | {0, 1, 2, V - 1}
+    valid = t[t >= 0]
+    if valid.size:   # the most frequent target classes carry the one-hot terms
+        vals, cnt = np.unique(valid, return_counts=True)
+        cols |= set(vals[np.argsort(-cnt)[:4]].tolist())
+    return np.array(sorted(cols))
+
+
+def _run_fused(cfg, inputs, upstream=None, reduction=None):
+    dt = torch.bfloat16
+    dev = torch.device("cuda", 0)
+    X = torch.from_numpy(inputs["X"]).to(dev).to(dt)
+    W = torch.from_numpy(inputs["W"]).to(dev).to(dt)
+    b = None if inputs["b"] is None else torch.from_numpy(inputs["b"]).to(dev).to(dt)
+    t = torch.from_numpy(inputs["t"]).to(dev)
+    op = LinearCrossEntropy(cfg.N, cfg.D, cfg.V, dt, bias=b is not None,
+                            reduction=reduction or cfg.reduction, chunk_rows=cfg.chunk_rows,
+                            acc_policy="accurate", argmax=True, device=dev)
+    u = None if upstream is None else torch.from_numpy(upstream).to(dev)
+    out = op(X, W, t, b, grad_output=u)
+    torch.cuda.synchronize()
+    res = {k: (v.cpu().numpy() if v.dtype in (torch.int32, torch.int64)
+               else v.float().cpu().numpy().astype(np.float64)) for k, v in out.items()}
+    res["chunk_rows"] = op.chunk_rows
+    del X, W, b, t, out, op
+    torch.cuda.empty_cache()
+    return res
+
+
+def _oracle_all_rows(inputs, g, cols, W64):
+    """Walk all rows in blocks: per-row lse / loss, grad_W and grad_b on the
+    sampled classes."""
+    N = inputs["X"].shape[0]
+    gw = np.zeros((len(cols), inputs["X"].shape[1]))
+    gb = np.zeros(len(cols))
+    loss_rows = np.zeros(N)
+    for r0 in range(0, N, ROW_BLOCK):
+        sl = slice(r0, min(N, r0 + ROW_BLOCK))
+        r = oracle.row_block(inputs["X"][sl], W64, inputs["b"], inputs["t"][sl], g[sl], cols)
+        loss_rows[sl] = r["loss_rows"]
+        gw += r["grad_W_cols"]
+        gb += r["grad_b_cols"]
+        if (r0 // ROW_BLOCK) % 8 == 0:
+            log(f"  oracle rows {r0}..{sl.stop} of {N}")
+    return loss_rows, gw, gb
+
+
+def _check_rows(gpu, inputs, rows, g, W64, tol, key_loss="loss_rows"):
+    r = oracle.row_block(inputs["X"][rows], W64, inputs["b"], inputs["t"][rows], g[rows],
+                         grad_x=True, return_z=True)
+    e_gx = rel_err(gpu["grad_X"][rows], r["grad_X"])
+    assert e_gx <= tol["grad"], f"grad_X rows error {e_gx:.3e}"
+    z_at = r["z"][np.arange(len(rows)), gpu["argmax"][rows]]
+    near = check_argmax(gpu["argmax"][rows], r["argmax"], r["top2_gap"], r["rowmax"], z_at)
+    return r, e_gx, near
+
+
+@pytest.mark.timeout(900)
+def test_large_vocab_full_size():
+    """N=8192, D=4096, V=128256 bf16, Zipf targets, 410 ignored, mean,
+    2048-row chunks, fp32 grad_W accumulation (the benchmark's launch)."""
+    require_gpu()
+    cfg = li.LARGE_VOCAB_BF16
+    log(f"{cfg.name}: generating inputs")
+    inputs = li.lce_inputs(cfg)
+    gpu = _run_fused(cfg, inputs)
+    assert gpu["chunk_rows"] == 2048
+    log("GPU done; oracle")
+    valid, bad, nv, nb = oracle.target_masks(inputs["t"], cfg.V, -100)
+    assert int(gpu["n_valid"][0]) == nv == cfg.N - 410 and int(gpu["n_bad"][0]) == nb == 0
+    g = oracle.row_weights(valid, "mean")
+    W64 = inputs["W"].astype(np.float64)
+    tol = TOL["bf16"]
+    rows = _sample_rows(cfg.N, inputs["t"])
+    _, e_gx, near = _check_rows(gpu, inputs, rows, g, W64, tol)
+    ign = inputs["t"] == -100
+    assert np.all(gpu["grad_X"][ign] == 0.0)
+    cols = _sample_cols(cfg.V, inputs["t"])
+    loss_rows, gw, gb = _oracle_all_rows(inputs, g, cols, W64)
+    L = oracle.reduce_loss(loss_rows, nv, "mean")
+    e_loss = abs(gpu["loss"][0] - L) / abs(L)
+    e_gw = rel_err(gpu["grad_W"][cols], gw)
+    log(f"loss {gpu['loss'][0]:.6f} vs {L:.6f} (rel {e_loss:.2e}); grad_X rows {e_gx:.2e}; "
+        f"grad_W cols {e_gw:.2e}; argmax near-ties {near}")
+    assert e_loss <= tol["loss"]
+    assert e_gw <= tol["grad"]
+    # every dL row sums to zero, so the class sum of grad_W vanishes
+    colsum = np.abs(gpu["grad_W"].sum(axis=0))
+    assert np.all(colsum <= 2e-2 * np.abs(gpu["grad_W"]).sum(axis=0) + 1e-6)
+
+
+@pytest.mark.timeout(1100)
+def test_none_reduction_full_size():
+    """N=16384, D=4096, V=151936 bf16 with bias, reduction='none', chunk
+    rows from the aspect-ratio rule (512): the per-row loss of the forward,
+    then the backward recomputed from the inputs with an N(0,1) upstream."""
+    require_gpu()
+    cfg = li.NONE_BF16
+    log(f"{cfg.name}: generating inputs")
+    inputs = li.lce_inputs(cfg)
+    fwd = _run_fused(cfg, inputs)
+    assert fwd["chunk_rows"] == 512
+    bwd = _run_fused(cfg, inputs, upstream=inputs["u"])
+    log("GPU done; oracle")
+    valid, _, nv, _ = oracle.target_masks(inputs["t"], cfg.V, -100)
+    assert int(bwd["n_valid"][0]) == nv == cfg.N
+    g = oracle.row_weights(valid, "none", upstream=inputs["u"])
+    W64 = inputs["W"].astype(np.float64)
+    tol = TOL["bf16"]
+    rows = _sample_rows(cfg.N, inputs["t"])
+    r, e_gx, near = _check_rows(bwd, inputs, rows, g, W64, tol)
+    e_lr = rel_err(fwd["loss"][rows], r["loss_rows"])
+    assert e_lr <= tol["loss"], e_lr
+    np.testing.assert_array_equal(fwd["argmax"], bwd["argmax"])
+    cols = _sample_cols(cfg.V, inputs["t"])
+    loss_rows, gw, gb = _oracle_all_rows(inputs, g, cols, W64)
+    e_all = rel_err(fwd["loss"], loss_rows)
+    e_gw = rel_err(bwd["grad_W"][cols], gw)
+    e_gb = rel_err(bwd["grad_b"][cols], gb)
+    log(f"per-row loss {e_all:.2e}; grad_X rows {e_gx:.2e}; grad_W cols {e_gw:.2e}; "
+        f"grad_b cols {e_gb:.2e}; argmax near-ties {near}")
+    assert e_all <= tol["loss"] and e_gw <= tol["grad"] and e_gb <= tol["grad"]
+
+
+@pytest.mark.timeout(600)
+def test_standalone_ce_full_size():
+    """Logits [16384, 131072] fp32 ~ N(0,1), uniform targets, mean; the
+    gradient written in place."""
+    require_gpu()
+    cfg = li.CE_F32
+    log(f"{cfg.name}: generating inputs")
+    inputs = li.ce_inputs(cfg)
+    dev = torch.device("cuda", 0)
+    z = torch.from_numpy(inputs["logits"]).to(dev)
+    t = torch.from_numpy(inputs["t"]).to(dev)
+    op = CrossEntropyInplace(cfg.N, cfg.V, reduction="mean", device=dev)
+    loss, nv = op(z, t)
+    torch.cuda.synchronize()
+    rows = _sample_rows(cfg.N, inputs["t"], k=24)
+    got = z[torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    gpu_loss = float(loss.cpu()[0])
+    assert int(nv.cpu()[0]) == cfg.N
+    del z
+    torch.cuda.empty_cache()
+    log("GPU done; oracle")
+    zs = inputs["logits"]
+    ts = inputs["t"]
+    _, dl = oracle.softmax_cross_entropy(zs[rows], ts[rows], reduction="sum",
+                                         grad_scale=1.0 / cfg.N)
+    e_dl = rel_err(got, dl)
+    total = 0.0
+    for r0 in range(0, cfg.N, 1024):
+        sl = slice(r0, r0 + 1024)
+        total += oracle.softmax_cross_entropy(zs[sl], ts[sl], reduction="sum")[0]
+    L = total / cfg.N
+    e_loss = abs(gpu_loss - L) / abs(L)
+    log(f"loss {gpu_loss:.7f} vs {L:.7f} (rel {e_loss:.2e}); gradient rows {e_dl:.2e}")
+    assert e_loss <= TOL["f32"]["loss"] and e_dl <= TOL["f32"]["grad"]
