@@ -38,6 +38,9 @@ struct lce_handle {
   int n_vt;           // 256-class tiles
   int splits;         // split-K of the grad_X GEMM
   int k_split;
+  int64_t grp;        // chunks per grad_W group (dL^T staged together)
+  int64_t k_grp;      // columns of the dL^T / X^T staging buffers (grp * c_pad)
+  int64_t n_groups;
   bool want_x, want_w, want_b, want_argmax, want_any;
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
   // workspace offsets (bytes)
@@ -114,7 +117,18 @@ void plan(lce_handle* h) {
   h->want_b = d.flags & LCE_GRAD_B;
   h->want_argmax = d.flags & LCE_ARGMAX;
   h->want_any = h->want_x || h->want_w || h->want_b;
-  h->w_acc32 = h->want_w && h->bf16 && d.acc_policy == LCE_ACCURATE;
+
+  // grad_W groups.  The dL^T of `grp` consecutive chunks is staged and one
+  // GEMM with K = grp * c_pad rows forms their grad_W contribution, so the
+  // accumulator is touched once per group instead of once per chunk.  ACCURATE
+  // stages up to as many bytes as the fp32 V x D accumulator it saves (K up to
+  // 4 D / element size); COMPACT keeps one chunk per group (least memory).
+  const int64_t k_max = 4 * d.D / h->esize;
+  h->grp = d.acc_policy == LCE_ACCURATE ? std::max<int64_t>(1, k_max / h->c_pad) : 1;
+  h->grp = std::max<int64_t>(1, std::min<int64_t>(h->grp, std::max<int64_t>(h->n_chunks, 1)));
+  h->k_grp = h->grp * h->c_pad;
+  h->n_groups = h->n_chunks ? cdiv64(h->n_chunks, h->grp) : 0;
+  h->w_acc32 = h->want_w && h->bf16 && d.acc_policy == LCE_ACCURATE && h->n_groups > 1;
 
   // split-K for grad_X = dL . W: aim at >= 512 workgroups, >= 1024 K per split.
   const int64_t tiles = cdiv64(h->c, lce::kTile) * cdiv64(d.D, lce::kTile);
@@ -132,9 +146,9 @@ void plan(lce_handle* h) {
     return need ? at : static_cast<size_t>(-1);
   };
   h->o_T = take(c * Vp * es, h->want_any);
-  h->o_dLt = take(Vp * c * es, h->want_w);
+  h->o_dLt = take(Vp * h->k_grp * es, h->want_w);
   h->o_Wt = take(D * Vp * es, h->want_x);
-  h->o_Xt = take(D * c * es, h->want_w);
+  h->o_Xt = take(D * h->k_grp * es, h->want_w);
   h->o_mp = take(h->n_vt * c * 4, true);
   h->o_sp = take(h->n_vt * c * 4, true);
   h->o_ip = take(h->n_vt * c * 4, h->want_argmax);
@@ -345,42 +359,53 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                              h->want_argmax ? io->argmax + row0 : nullptr, s));
     if (!grads) continue;
 
-    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, T, Vp, want_w ? dLt : nullptr, cp, mp, cp, lse, g + row0,
-                                  tc + row0, rows, rows_pad, V, static_cast<int>(Vp),
-                                  want_b ? gbp : nullptr, s));
+    const int64_t jj = ck % h->grp;               // position inside the grad_W group
+    char* dLt_j = static_cast<char*>(dLt) + jj * cp * es;
+    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, T, Vp, want_w ? dLt_j : nullptr,
+                                  h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
+                                  V, static_cast<int>(Vp), want_b ? gbp : nullptr, s));
     if (want_x) {
+      // grad_X[rows] = dL . W, as (W^T)[D][V] against dL[rows][V]: the
+      // transposed store writes grad_X rows with contiguous vectors.
       lce::GemmNT gx{};
-      gx.A = T; gx.lda = Vp;
-      gx.B = Wt; gx.ldb = Vp;
-      gx.M = rows; gx.N = D; gx.K = static_cast<int>(Vp);
+      gx.A = Wt; gx.lda = Vp;
+      gx.B = T; gx.ldb = Vp;
+      gx.M = D; gx.N = rows; gx.K = static_cast<int>(Vp);
       gx.splits = h->splits; gx.k_split = h->k_split;
       gx.split_stride = static_cast<int64_t>(rows) * D;
       gx.C = gxp; gx.ldc = D; gx.Cin = nullptr;
       gx.mode = lce::EpiMode::kStoreF32;
-      gx.group_m = 8;
+      gx.group_m = static_cast<int>(cdiv64(D, lce::kTile));
       LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(bf16, gx, s));
       LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(bf16, gxp, h->splits, gx.split_stride, rows, D,
                               static_cast<char*>(io->grad_X) + row0 * d.D * es, s));
     }
     if (want_w) {
-      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, Xc, D, rows, D, Xt, cp, rows_pad, s));
-      lce::GemmNT gw{};
-      gw.A = dLt; gw.lda = cp;
-      gw.B = Xt; gw.ldb = cp;
-      gw.M = V; gw.N = D; gw.K = rows_pad;
-      gw.splits = 1; gw.k_split = rows_pad; gw.split_stride = 0;
-      gw.ldc = D;
-      gw.group_m = 4;
-      if (h->w_acc32) {
-        if (first && last) { gw.C = io->grad_W; gw.mode = lce::EpiMode::kStoreOut; }
-        else if (first) { gw.C = gw32; gw.mode = lce::EpiMode::kStoreF32; }
-        else if (!last) { gw.C = gw32; gw.mode = lce::EpiMode::kAccumF32; }
-        else { gw.C = io->grad_W; gw.Cin = gw32; gw.mode = lce::EpiMode::kFinalOut; }
-      } else {
-        gw.C = io->grad_W;
-        gw.mode = first ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
+      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, Xc, D, rows, D,
+                                                        static_cast<char*>(Xt) + jj * cp * es,
+                                                        h->k_grp, rows_pad, s));
+      if (jj + 1 == h->grp || last) {
+        // grad_W[V][D] += dL^T . X over the group's rows, as (X^T)[D][K]
+        // against (dL^T)[V][K] with the transposed store.
+        const int64_t gi = ck / h->grp;
+        const bool gfirst = gi == 0, glast = last;
+        lce::GemmNT gw{};
+        gw.A = Xt; gw.lda = h->k_grp;
+        gw.B = dLt; gw.ldb = h->k_grp;
+        gw.M = D; gw.N = V; gw.K = static_cast<int>(jj * cp + rows_pad);
+        gw.splits = 1; gw.k_split = gw.K; gw.split_stride = 0;
+        gw.ldc = D;
+        gw.group_m = static_cast<int>(cdiv64(D, lce::kTile));
+        if (h->w_acc32) {
+          if (gfirst) { gw.C = gw32; gw.mode = lce::EpiMode::kStoreF32; }
+          else if (!glast) { gw.C = gw32; gw.mode = lce::EpiMode::kAccumF32; }
+          else { gw.C = io->grad_W; gw.Cin = gw32; gw.mode = lce::EpiMode::kFinalOut; }
+        } else {
+          gw.C = io->grad_W;
+          gw.mode = gfirst ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
+        }
+        LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(bf16, gw, s));
       }
-      LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(bf16, gw, s));
     }
     if (want_b)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(bf16, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,

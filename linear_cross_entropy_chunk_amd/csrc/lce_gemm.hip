@@ -50,12 +50,6 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
 }
 __device__ __forceinline__ float to_f32(float f) { return f; }
 
-template <typename T> __device__ __forceinline__ T from_f32(float f);
-template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
-template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) {
-  // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -199,6 +193,39 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 }
 
 // ---------------------------------------------------------------- plain GEMM
+// The output is stored transposed, C[n * ldc + m]: lane l holds 4
+// consecutive m (registers 4q..4q+3) of column n, so every store (and every
+// load of the accumulate modes) is one 16-byte (fp32) or 8-byte (bf16)
+// vector.  M must be a multiple of 4.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { typedef f32x4_t type; };
+template <> struct Vec4<uint16_t> { typedef bf16x4_t type; };
+
+template <typename T>
+__device__ __forceinline__ f32x4_t load4(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  } else {
+    const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+    return f32x4_t{static_cast<float>(v[0]), static_cast<float>(v[1]),
+                   static_cast<float>(v[2]), static_cast<float>(v[3])};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4_t v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4_t*>(p) = v;
+  } else {
+    bf16x4_t o;
+    o[0] = static_cast<__bf16>(v[0]);
+    o[1] = static_cast<__bf16>(v[1]);
+    o[2] = static_cast<__bf16>(v[2]);
+    o[3] = static_cast<__bf16>(v[3]);
+    *reinterpret_cast<bf16x4_t*>(p) = o;
+  }
+}
+
 template <typename T, int kMode>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
@@ -220,32 +247,33 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
   const int nb = tn * kTile + wn * 128 + (lane & 31);
   const int64_t ldc = g.ldc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int n = nb + 32 * j;
+    if (n >= g.N) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nb + 32 * j;
-      if (n >= g.N) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mb + 32 * i + 8 * (r >> 2) + (r & 3);
+      for (int q = 0; q < 4; ++q) {
+        const int m = mb + 32 * i + 8 * q;
         if (m >= g.M) continue;
-        const int64_t off = static_cast<int64_t>(m) * ldc + n;
-        const float v = acc[i][j][r];
+        const int64_t off = static_cast<int64_t>(n) * ldc + m;
+        f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                     acc[i][j][4 * q + 3]};
         if constexpr (kMode == static_cast<int>(EpiMode::kStoreF32)) {
-          static_cast<float*>(g.C)[split * g.split_stride + off] = v;
+          store4(static_cast<float*>(g.C) + split * g.split_stride + off, v);
         } else if constexpr (kMode == static_cast<int>(EpiMode::kAccumF32)) {
           float* c = static_cast<float*>(g.C) + off;
-          *c = *c + v;
+          store4(c, load4(c) + v);
         } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
-          static_cast<T*>(g.C)[off] = from_f32<T>(static_cast<const float*>(g.Cin)[off] + v);
+          store4(static_cast<T*>(g.C) + off, load4(static_cast<const float*>(g.Cin) + off) + v);
         } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
-          static_cast<T*>(g.C)[off] = from_f32<T>(v);
+          store4(static_cast<T*>(g.C) + off, v);
         } else {
           T* c = static_cast<T*>(g.C) + off;
-          *c = from_f32<T>(to_f32(*c) + v);
+          store4(c, load4(c) + v);
         }
       }
-    }
+  }
 }
 
 // ------------------------------------------------- logits + softmax stats

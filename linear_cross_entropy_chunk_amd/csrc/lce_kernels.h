@@ -23,8 +23,9 @@ enum class EpiMode : int {
 };
 
 // ---- GEMM (lce_gemm.hip) -------------------------------------------------
-// C[m, n] = sum_k A[m, k] * B[n, k]; A is [M][lda], B is [N][ldb], both with
-// K contiguous ("NT").  K is split into `splits` ranges of k_split elements
+// P[m, n] = sum_k A[m, k] * B[n, k]; A is [M][lda], B is [N][ldb], both with
+// K contiguous ("NT").  The result is stored transposed, C[n * ldc + m]
+// (M a multiple of 4).  K is split into `splits` ranges of k_split elements
 // (a multiple of the stage depth); split s writes C + s * split_stride.
 struct GemmNT {
   const void* A; int64_t lda;
