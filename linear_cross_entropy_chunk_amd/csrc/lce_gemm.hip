@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace lce {
 namespace {
 
@@ -36,9 +38,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kStageBytes = kTile * kStageRowBytes;          // 32 KiB
-constexpr int kLdsOperandBytes = 2 * 2 * kStageBytes;        // 128 KiB
+// Wave layout of a 256 x 256 tile: kWavesM x kWavesN waves, each owning a
+// (256 / kWavesM) x (256 / kWavesN) sub-tile of 32 x 32 accumulator blocks.
+#ifndef LCE_WAVES_N
+#define LCE_WAVES_N 4
+#endif
+constexpr int kWavesM = 2;
+constexpr int kWavesN = LCE_WAVES_N;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveN = kTile / kWavesN;      // columns per wave
+constexpr int kJ = kWaveN / 32;               // 32-column blocks per wave
+constexpr int kCopies = 16 / kWaves;          // 16-row copy blocks per wave per operand
+constexpr int kLdsOperandBytes = 128 * 1024;                 // operand ring
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Elt;
@@ -100,96 +112,209 @@ __device__ __forceinline__ void mfma_step<float>(f32x16_t& acc, i32x4_t a, i32x4
 
 // Accumulator layout of a 32 x 32 MFMA block, lane l, register r:
 //   column = l & 31, row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
-// Wave (wm, wn) owns rows wm*128 + 32 i + ..., columns wn*128 + 32 j + ...
+// Wave (wm, wn) owns rows wm*128 + 32 i + ..., columns wn*kWaveN + 32 j + ...
+
+// Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, dword3 =
+// 0x00020000).  Loads whose per-lane offset is at or past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int range = bytes > 0x7ffff000LL * 2 ? -1 : static_cast<int>(static_cast<uint32_t>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, 0x00020000);
+}
+constexpr int kOutOfRange = 0x7fffffff;
+
+// ------------------------------------------------------------- main loop
+// K is walked in stages of 64 bytes per row (32 bf16 or 16 fp32).  Both
+// operands of a stage (2 x 256 rows x 64 bytes = 32 KiB) are copied from
+// global memory straight into LDS with buffer_load_dwordx4 ... lds: each wave
+// instruction moves 16 rows x 64 bytes, lane i's 16 bytes landing at LDS byte
+// 16 i of the instruction's 1 KiB block.  Four stages form a ring, filled
+// three stages ahead of the MFMAs, with no staging registers and no LDS write
+// instructions.
+//
+// LDS chunk swizzle: the 16-byte chunk with logical index c of row r sits at
+// physical chunk c ^ ((r >> 2) & 3).  gfx950 serves a ds_read_b128 16 lanes
+// (256 bytes) per cycle; the fragment reads put 16 consecutive rows at one
+// logical chunk in such a group, and with 64-byte rows this swizzle spreads
+// them over all 16 bank groups.  The copy applies the inverse on the global
+// side: lane i of a copy instruction fetches logical chunk (i & 3) ^ swz(row).
+namespace sched {   // instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100, kDsWrite = 0x200;
+}
+
+// gfx9 s_waitcnt immediates: vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; expcnt and lgkmcnt at their maxima mean "do not wait".
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+constexpr int kWaitVm0 = waitcnt_vm(0);
+
+constexpr int kStages = 4;
+constexpr int kRowBytes = 64;
+// copies a wave leaves in flight for the two stages after the current one
+constexpr int kWaitVmLater = waitcnt_vm(2 * 2 * kCopies);                                  // per stage row
+constexpr int kOpStageBytes = kTile * kRowBytes;              // 16 KiB per operand
+constexpr int kStageBytesDma = 2 * kOpStageBytes;             // 32 KiB per stage
+static_assert(kStages * kStageBytesDma <= kLdsOperandBytes, "LDS ring");
+
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+
+// One 16-byte-per-lane copy from a buffer straight into LDS at `lds` (M0) +
+// 16 * lane.  Issued as inline asm so the compiler does not track it: its
+// waits for LDS copies would cover every copy in flight (including the ones
+// just issued for later stages), serializing the ring.  The main loop waits
+// for the copies itself; vector memory operations complete in issue order,
+// so any wait the compiler inserts for its own loads stays correct (at worst
+// stronger than needed).
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset,
+                                              uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+}
 
 // C tile [m0, m0+256) x [n0, n0+256) += A[m0.., k_begin..k_end) . B[n0.., ...]^T
-template <typename T>
+//
+// Rows past M (N) read as zero (each copy's descriptor covers only the
+// tile's existing rows).  With kKTail, 16-byte chunks at or past k_end read
+// as zero too (their offsets are sent out of range).
+template <typename T, bool kKTail>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
                                          int k_begin, int k_end, char* __restrict__ lds,
-                                         f32x16_t (&acc)[4][4]) {
-  constexpr int kVec = Elt<T>::kVec;
-  constexpr int kBK = kStageRowBytes / static_cast<int>(sizeof(T));
+                                         f32x16_t (&acc)[4][kJ]) {
+  constexpr int kEs = static_cast<int>(sizeof(T));
+  constexpr int kBK = kRowBytes / kEs;                 // K elements per stage
+  constexpr int kVec = 16 / kEs;                       // elements per 16-byte chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy bases in SGPRs
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
+    for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16_t{0};
 
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   if (nk <= 0) return;
 
-  // Global -> register mapping: thread t loads chunk (t & 7) of rows
-  // (t >> 3) + 32 i, i = 0..7, for each operand.
-  const int ch = tid & 7;
-  const int r0 = tid >> 3;
-  const T* pa = A + static_cast<int64_t>(m0 + r0) * lda + ch * kVec;
-  const T* pb = B + static_cast<int64_t>(n0 + r0) * ldb + ch * kVec;
-  const int64_t sa = 32 * lda, sb = 32 * ldb;
-  const int st_off = r0 * kStageRowBytes + ((ch ^ (r0 & 7)) << 4);
-
-  i32x4_t ga[8], gb[8];
-  auto gload = [&](int k0) {
-    const bool kin = (k0 + ch * kVec) < k_end;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + static_cast<int64_t>(m0) * lda,
+                                              static_cast<int64_t>(min(M - m0, kTile)) * lda * kEs);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<int64_t>(n0) * ldb,
+                                              static_cast<int64_t>(min(N - n0, kTile)) * ldb * kEs);
+  // Copy mapping: wave w issues instructions j < kCopies per operand per
+  // stage, covering rows 16 (kCopies w + j) .. +16; lane i takes row
+  // 16 (kCopies w + j) + i / 4, physical chunk i & 3.
+  const int crow = lane >> 2;                      // row inside the 16-row block
+  const int pchunk = lane & 3;
+  int va[kCopies], vb[kCopies];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ga[i] = i32x4_t{0, 0, 0, 0};
-      gb[i] = i32x4_t{0, 0, 0, 0};
-      if (kin && m0 + r0 + 32 * i < M)
-        ga[i] = *reinterpret_cast<const i32x4_t*>(pa + i * sa + k0);
-      if (kin && n0 + r0 + 32 * i < N)
-        gb[i] = *reinterpret_cast<const i32x4_t*>(pb + i * sb + k0);
+  for (int j = 0; j < kCopies; ++j) {
+    const int row = 16 * (kCopies * wave + j) + crow;
+    const int lchunk = pchunk ^ swz(row);
+    va[j] = (row * static_cast<int>(lda) + lchunk * kVec) * kEs;
+    vb[j] = (row * static_cast<int>(ldb) + lchunk * kVec) * kEs;
+  }
+  auto copy_stage = [&](int st, int buf) {
+    const int k0 = k_begin + st * kBK;
+    const int koff = k0 * kEs;
+    char* sa = lds + buf * kStageBytesDma;
+    char* sb = sa + kOpStageBytes;
+    bool kin = true;
+    if constexpr (kKTail) kin = (k0 + (pchunk ^ swz(crow)) * kVec) < k_end;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      const int blk = (kCopies * wave + j) * 1024;
+      int oa = va[j] + koff, ob = vb[j] + koff;
+      if constexpr (kKTail) {
+        // the logical chunk of this lane is the same for every j (rows 16 apart)
+        oa = kin ? oa : kOutOfRange;
+        ob = kin ? ob : kOutOfRange;
+      }
+      copy16_to_lds(ra, oa, lds_addr(sa + blk));
+      copy16_to_lds(rb, ob, lds_addr(sb + blk));
     }
   };
-  auto sstore = [&](int stage) {
-    char* la = lds + stage * (2 * kStageBytes);
-    char* lb = la + kStageBytes;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<i32x4_t*>(la + st_off + i * 32 * kStageRowBytes) = ga[i];
-      *reinterpret_cast<i32x4_t*>(lb + st_off + i * 32 * kStageRowBytes) = gb[i];
-    }
-  };
 
-  // Fragment reads: lane l reads row (l & 31) of each 32-row block at chunk
-  // (2 kk + (l >> 5)) of the stage, swizzled by (row & 7) = (l & 7).
+  // Fragment reads: lane l reads row (l & 31) of each 32-row block at logical
+  // chunk (2 kk + (l >> 5)), kk = 0, 1.  Rows 32 i + (l & 31) share the
+  // swizzle of (l & 31).
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
-  const int fsw = lane & 7;
-  const int a_row = (wm * 128 + frow) * kStageRowBytes;
-  const int b_row = (wn * 128 + frow) * kStageRowBytes;
+  const int fsw = swz(frow);
+  const int a_row = (wm * 128 + frow) * kRowBytes;
+  const int b_row = (wn * kWaveN + frow) * kRowBytes;
+  i32x4_t af[2][4], bf[2][kJ];
+  auto fread = [&](const char* sa, const char* sb, int kk, int buf) {
+    const int c = ((2 * kk + fhalf) ^ fsw) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[buf][i] = *reinterpret_cast<const i32x4_t*>(sa + a_row + i * 32 * kRowBytes + c);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      bf[buf][j] = *reinterpret_cast<const i32x4_t*>(sb + b_row + j * 32 * kRowBytes + c);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) mfma_step<T>(acc[i][j], af[buf][i], bf[buf][j]);
+  };
+  constexpr int kMfmaPer = sizeof(T) == 2 ? 1 : 4;
 
-  gload(k_begin);
-  sstore(0);
+  // Ping-pong schedule.  The waves form two groups of four, one wave of
+  // each group per SIMD (wave w runs on SIMD w % 4).  Every wave runs the
+  // same loop -- compute stage kt from registers | barrier | read stage
+  // kt + 1 into registers and issue its copies of stage kt + 4 | barrier --
+  // but group 1 takes one extra barrier before the loop (and group 0 one
+  // after it), which shifts group 1 by one phase: in every phase one wave
+  // per SIMD issues MFMAs while the other reads LDS and issues copies.
+  //
+  // Numbering the common barriers B1, B2, ...: group 0 reads stage s in
+  // (B(2s-1), B(2s)) and group 1 in (B(2s), B(2s+1)), so stage s must be
+  // whole by B(2s-1).  Each wave waits, at the end of iteration kt's memory
+  // phase, until its own copies up to stage kt + 2 have landed (copies
+  // complete in issue order); group 0 passes that point before B(2kt+2),
+  // group 1 before B(2kt+3) = B(2(kt+2)-1).  The prologue covers stages 0
+  // and 1.  Stage s + 4 reuses the buffer of stage s once both groups hold
+  // stage s in registers: group 0 copies after B(2s+1), group 1 after
+  // B(2s+2), and the barriers wait for all LDS reads issued before them.
+  const int group = wave >> 2;
+  constexpr int kPerStage = 2 * kCopies;            // copies per wave per stage
+  static_assert(kWaves == 8, "the ping-pong schedule needs two groups of four waves");
+
+#pragma unroll
+  for (int st = 0; st < kStages; ++st) copy_stage(min(st, nk - 1), st);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage));
   __syncthreads();
+  fread(lds, lds + kOpStageBytes, 0, 0);
+  fread(lds, lds + kOpStageBytes, 1, 1);
+  if (group == 1) __syncthreads();
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(k_begin + (kt + 1) * kBK);
-    const char* la = lds + cur * (2 * kStageBytes);
-    const char* lb = la + kStageBytes;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = ((2 * kk + fhalf) ^ fsw) << 4;
-      i32x4_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const i32x4_t*>(la + a_row + i * 32 * kStageRowBytes + c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const i32x4_t*>(lb + b_row + j * 32 * kStageRowBytes + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_step<T>(acc[i][j], af[i], bf[j]);
-    }
-    if (more) sstore(cur ^ 1);
+    // compute phase
+    __builtin_amdgcn_s_setprio(1);
+    mfmas(0);
+    mfmas(1);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
+    // memory phase
+    const int nxt = min(kt + 1, nk - 1);
+    const char* sn = lds + (nxt % kStages) * kStageBytesDma;
+    fread(sn, sn + kOpStageBytes, 0, 0);
+    fread(sn, sn + kOpStageBytes, 1, 1);
+    copy_stage(min(kt + kStages, nk - 1), kt % kStages);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage));
     __syncthreads();
   }
+  if (group == 0) __syncthreads();
+  // Drain the copies still in flight before the LDS is reused.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- plain GEMM
@@ -226,7 +351,7 @@ __device__ __forceinline__ void store4(T* p, f32x4_t v) {
   }
 }
 
-template <typename T, int kMode>
+template <typename T, int kMode, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   const int tiles_m = cdiv(g.M, kTile), tiles_n = cdiv(g.N, kTile);
@@ -237,17 +362,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
   tile_coords(logical - split * per_split, tiles_m, tiles_n, g.group_m, tm, tn);
   const int kb = split * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
-  f32x16_t acc[4][4];
-  mainloop<T>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
-              static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, kb, ke, lds, acc);
+  f32x16_t acc[4][kJ];
+  mainloop<T, kKTail>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
+                      static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, kb, ke, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int mb = tm * kTile + wm * 128 + 4 * (lane >> 5);
-  const int nb = tn * kTile + wn * 128 + (lane & 31);
+  const int nb = tn * kTile + wn * kWaveN + (lane & 31);
   const int64_t ldc = g.ldc;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kJ; ++j) {
     const int n = nb + 32 * j;
     if (n >= g.N) continue;
 #pragma unroll
@@ -277,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
 }
 
 // ------------------------------------------------- logits + softmax stats
-template <typename T, bool kStoreT, bool kArgmax>
+template <typename T, bool kStoreT, bool kArgmax, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   __shared__ float red_m[2][kTile];
@@ -289,37 +414,50 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   int tm, tn;
   tile_coords(logical, tiles_m, tiles_n, 4, tm, tn);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][kJ];
   // M = classes (rows of W), N = chunk rows (rows of X), K = D.
-  mainloop<T>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V,
-              static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0, a.D, lds, acc);
+  mainloop<T, kKTail>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V,
+                      static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0, a.D, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int frow = lane & 31, fhalf = lane >> 5;
   const int vbase = tm * kTile + wm * 128;               // class of (i=0, r=0, half 0)
   const int vlane = vbase + 4 * fhalf;                   // + 32 i + 8 (r >> 2) + (r & 3)
-  const int ncol = wn * 128 + frow;                      // + 32 j, within the tile
-  const int nbase = tn * kTile + ncol;
+  const int ncol = wn * kWaveN + frow;                   // + 32 j, within the tile
   const T* bias = static_cast<const T*>(a.bias);
 
-  // 1. bias, and -inf for classes beyond V.
+  // The epilogue walks the four 32-column blocks j one at a time so that
+  // only 64 accumulators per lane are live in VGPRs.  Each block uses its own
+  // slots of the cross-wave exchange arrays.
+  T* Tm = static_cast<T*>(a.T);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < kJ; ++j) {
+    // Blocks not yet processed stay in the accumulator registers: without
+    // this the register allocator copies every accumulator to VGPRs at the
+    // loop exit and spills.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = vlane + 32 * i + 8 * (r >> 2) + (r & 3);
-      const bool in = v < a.V;
-      const float bb = (in && bias) ? to_f32(bias[v]) : 0.0f;
+    for (int jj = j + 1; jj < kJ; ++jj)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j][r] = in ? acc[i][j][r] + bb : -INFINITY;
-    }
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    const int nc = ncol + 32 * j;           // column inside the tile
+    const int n = tn * kTile + nc;          // chunk row
+    const bool nin = n < a.rows;
 
-  // 2. target logit: the lane holding class tc[n] of column n writes zt[n].
+    // 1. bias, and -inf for classes beyond V.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = nbase + 32 * j;
-    if (n < a.rows) {
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vlane + 32 * i + 8 * (r >> 2) + (r & 3);
+        const bool in = v < a.V;
+        const float bb = (in && bias) ? to_f32(bias[v]) : 0.0f;
+        acc[i][j][r] = in ? acc[i][j][r] + bb : -INFINITY;
+      }
+
+    // 2. target logit: the lane holding class tc[n] of column n writes zt[n].
+    if (nin) {
       const int t = a.tc[n];
       const int off = t - vbase;
       if (t >= 0 && off >= 0 && off < 128 && ((off >> 2) & 1) == fhalf) {
@@ -332,13 +470,8 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
         a.zt[n] = val;
       }
     }
-  }
 
-  // 3. column max (and lowest class attaining it) over the tile's 256 classes.
-  float cmax[4];
-  int cidx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
+    // 3. column max (and lowest class attaining it) over the tile's classes.
     float mx = -INFINITY;
     int mi = 0x7fffffff;
 #pragma unroll
@@ -351,35 +484,30 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
           if constexpr (kArgmax) mi = vlane + 32 * i + 8 * (r >> 2) + (r & 3);
         }
       }
-    const float om = __shfl_xor(mx, 32);
-    const int oi = __shfl_xor(mi, 32);
-    if (om > mx || (om == mx && oi < mi)) {
-      mx = om;
-      mi = oi;
+    {
+      const float om = __shfl_xor(mx, 32);
+      const int oi = __shfl_xor(mi, 32);
+      if (om > mx || (om == mx && oi < mi)) {
+        mx = om;
+        mi = oi;
+      }
     }
-    cmax[j] = mx;
-    cidx[j] = mi;
     if (fhalf == 0) {
-      red_m[wm][ncol + 32 * j] = mx;
-      red_i[wm][ncol + 32 * j] = mi;
+      red_m[wm][nc] = mx;
+      red_i[wm][nc] = mi;
     }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float om = red_m[wm ^ 1][ncol + 32 * j];
-    const int oi = red_i[wm ^ 1][ncol + 32 * j];
-    if (om > cmax[j] || (om == cmax[j] && oi < cidx[j])) {
-      cmax[j] = om;
-      cidx[j] = oi;
+    __syncthreads();
+    {
+      const float om = red_m[wm ^ 1][nc];
+      const int oi = red_i[wm ^ 1][nc];
+      if (om > mx || (om == mx && oi < mi)) {
+        mx = om;
+        mi = oi;
+      }
     }
-  }
 
-  // 4. e = exp(z - tile max) in place, column sums.
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float mx = cmax[j];
-    float s = 0.0f;
+    // 4. e = exp(z - tile max) in place, column sums.
+    float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -387,54 +515,46 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
         // (z - max) first: the maximum maps to exactly 1.
         const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - mx) * kLog2e);
         acc[i][j][r] = e;
-        s += e;
+        sum += e;
       }
-    s += __shfl_xor(s, 32);
-    if (fhalf == 0) red_s[wm][ncol + 32 * j] = s;
-  }
-  __syncthreads();
+    sum += __shfl_xor(sum, 32);
+    if (fhalf == 0) red_s[wm][nc] = sum;
+    __syncthreads();
 
-  // 5. per-(row, class tile) statistics.
-  if (wm == 0 && fhalf == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nbase + 32 * j;
-      if (n < a.rows) {
-        const int64_t o = static_cast<int64_t>(tm) * a.ldp + n;
-        a.m_part[o] = cmax[j];
-        a.s_part[o] = red_s[0][ncol + 32 * j] + red_s[1][ncol + 32 * j];
-        if constexpr (kArgmax) a.i_part[o] = cidx[j];
-      }
+    // 5. per-(row, class tile) statistics.
+    if (wm == 0 && fhalf == 0 && nin) {
+      const int64_t o = static_cast<int64_t>(tm) * a.ldp + n;
+      a.m_part[o] = mx;
+      a.s_part[o] = red_s[0][nc] + red_s[1][nc];
+      if constexpr (kArgmax) a.i_part[o] = mi;
     }
-  }
 
-  // 6. the exp tile T[n][v], 4 consecutive classes per store.
-  if constexpr (kStoreT) {
-    T* Tm = static_cast<T*>(a.T);
+    // 6. the exp tile T[n][v], 4 consecutive classes per store.
+    if constexpr (kStoreT) {
+      if (nin) {
+        T* row = Tm + static_cast<int64_t>(n) * a.ldt;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nbase + 32 * j;
-      if (n >= a.rows) continue;
-      T* row = Tm + static_cast<int64_t>(n) * a.ldt;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int v0 = vlane + 32 * i + 8 * q;
-          if constexpr (sizeof(T) == 2) {
-            bf16x4_t pk;
-            pk[0] = static_cast<__bf16>(acc[i][j][4 * q + 0]);
-            pk[1] = static_cast<__bf16>(acc[i][j][4 * q + 1]);
-            pk[2] = static_cast<__bf16>(acc[i][j][4 * q + 2]);
-            pk[3] = static_cast<__bf16>(acc[i][j][4 * q + 3]);
-            *reinterpret_cast<bf16x4_t*>(row + v0) = pk;
-          } else {
-            f32x4_t pk = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
-                          acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            *reinterpret_cast<f32x4_t*>(row + v0) = pk;
+          for (int q = 0; q < 4; ++q) {
+            const int v0 = vlane + 32 * i + 8 * q;
+            if constexpr (sizeof(T) == 2) {
+              bf16x4_t pk;
+              pk[0] = static_cast<__bf16>(acc[i][j][4 * q + 0]);
+              pk[1] = static_cast<__bf16>(acc[i][j][4 * q + 1]);
+              pk[2] = static_cast<__bf16>(acc[i][j][4 * q + 2]);
+              pk[3] = static_cast<__bf16>(acc[i][j][4 * q + 3]);
+              *reinterpret_cast<bf16x4_t*>(row + v0) = pk;
+            } else {
+              f32x4_t pk = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              *reinterpret_cast<f32x4_t*>(row + v0) = pk;
+            }
           }
-        }
+      }
     }
+    // keep the blocks apart so only one block's values are live at a time
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -443,14 +563,26 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   const int tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile) * g.splits;
   if (tiles <= 0) return hipSuccess;
   const dim3 grid(tiles), block(kThreads);
+  constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
+  // Every split range and K must be whole stages on this path.
+  if (g.K % kBK != 0 || g.k_split % kBK != 0) return hipErrorInvalidValue;
   switch (g.mode) {
-    case EpiMode::kStoreF32: k_gemm_nt<T, 0><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kAccumF32: k_gemm_nt<T, 1><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kFinalOut: k_gemm_nt<T, 2><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kStoreOut: k_gemm_nt<T, 3><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kAccumOut: k_gemm_nt<T, 4><<<grid, block, 0, s>>>(g); break;
+    case EpiMode::kStoreF32: k_gemm_nt<T, 0, false><<<grid, block, 0, s>>>(g); break;
+    case EpiMode::kAccumF32: k_gemm_nt<T, 1, false><<<grid, block, 0, s>>>(g); break;
+    case EpiMode::kFinalOut: k_gemm_nt<T, 2, false><<<grid, block, 0, s>>>(g); break;
+    case EpiMode::kStoreOut: k_gemm_nt<T, 3, false><<<grid, block, 0, s>>>(g); break;
+    case EpiMode::kAccumOut: k_gemm_nt<T, 4, false><<<grid, block, 0, s>>>(g); break;
   }
   return hipGetLastError();
+}
+
+template <typename T, bool kKTail>
+void launch_logits_k(const LogitsLse& a, dim3 grid, dim3 block, hipStream_t s) {
+  const bool st = a.T != nullptr, am = a.i_part != nullptr;
+  if (st && am) k_logits_lse<T, true, true, kKTail><<<grid, block, 0, s>>>(a);
+  else if (st) k_logits_lse<T, true, false, kKTail><<<grid, block, 0, s>>>(a);
+  else if (am) k_logits_lse<T, false, true, kKTail><<<grid, block, 0, s>>>(a);
+  else k_logits_lse<T, false, false, kKTail><<<grid, block, 0, s>>>(a);
 }
 
 template <typename T>
@@ -458,11 +590,9 @@ hipError_t launch_logits(const LogitsLse& a, hipStream_t s) {
   const int tiles = ((a.V + kTile - 1) / kTile) * ((a.rows + kTile - 1) / kTile);
   if (tiles <= 0) return hipSuccess;
   const dim3 grid(tiles), block(kThreads);
-  const bool st = a.T != nullptr, am = a.i_part != nullptr;
-  if (st && am) k_logits_lse<T, true, true><<<grid, block, 0, s>>>(a);
-  else if (st) k_logits_lse<T, true, false><<<grid, block, 0, s>>>(a);
-  else if (am) k_logits_lse<T, false, true><<<grid, block, 0, s>>>(a);
-  else k_logits_lse<T, false, false><<<grid, block, 0, s>>>(a);
+  constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
+  if (a.D % kBK == 0) launch_logits_k<T, false>(a, grid, block, s);
+  else launch_logits_k<T, true>(a, grid, block, s);
   return hipGetLastError();
 }
 

@@ -7,10 +7,8 @@
 
 namespace lce {
 
-// Square output tile of every GEMM launch (rows x cols of C per workgroup)
-// and the K depth, in bytes, of one LDS stage row.
+// Square output tile of every GEMM launch (rows x cols of C per workgroup).
 constexpr int kTile = 256;
-constexpr int kStageRowBytes = 128;
 // Rows per K4 finalize / transpose tile.
 constexpr int kSmallTile = 64;
 
