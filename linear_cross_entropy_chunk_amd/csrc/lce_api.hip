@@ -376,6 +376,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       gx.C = gxp; gx.ldc = D; gx.Cin = nullptr;
       gx.mode = lce::EpiMode::kStoreF32;
       gx.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along rows
+      gx.role = lce::GemmRole::kGradX;
       LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(bf16, gx, s));
       LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(bf16, gxp, h->splits, gx.split_stride, rows, D,
                               static_cast<char*>(io->grad_X) + row0 * d.D * es, s));
@@ -396,6 +397,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         gw.splits = 1; gw.k_split = gw.K; gw.split_stride = 0;
         gw.ldc = D;
         gw.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along V
+        gw.role = lce::GemmRole::kGradW;
         if (h->w_acc32) {
           if (gfirst) { gw.C = gw32; gw.mode = lce::EpiMode::kStoreF32; }
           else if (!glast) { gw.C = gw32; gw.mode = lce::EpiMode::kAccumF32; }

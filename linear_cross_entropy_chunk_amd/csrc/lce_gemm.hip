@@ -24,6 +24,7 @@
 // chunk loop body of the PyTorch module torch/nn/modules/linear_cross_entropy.py
 // (logits mm, bias add, row max subtraction, target gather, sumexp), fused.
 #include "lce_kernels.h"
+#include "lce_device.h"
 
 #include <math.h>
 
@@ -114,13 +115,8 @@ __device__ __forceinline__ void mfma_step<float>(f32x16_t& acc, i32x4_t a, i32x4
 //   column = l & 31, row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
 // Wave (wm, wn) owns rows wm*128 + 32 i + ..., columns wn*kWaveN + 32 j + ...
 
-// Raw buffer descriptor (gfx9 layout: base, stride 0, byte range, dword3 =
-// 0x00020000).  Loads whose per-lane offset is at or past `bytes` return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int range = bytes > 0x7ffff000LL * 2 ? -1 : static_cast<int>(static_cast<uint32_t>(bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, 0x00020000);
-}
-constexpr int kOutOfRange = 0x7fffffff;
+using dev::make_rsrc;
+using dev::kOutOfRange;
 
 // ------------------------------------------------------------- main loop
 // K is walked in stages of 64 bytes per row (32 bf16 or 16 fp32).  Both
@@ -141,9 +137,7 @@ namespace sched {   // instruction classes of __builtin_amdgcn_sched_group_barri
 constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100, kDsWrite = 0x200;
 }
 
-// gfx9 s_waitcnt immediates: vmcnt in bits [3:0] and [15:14], expcnt [6:4],
-// lgkmcnt [11:8]; expcnt and lgkmcnt at their maxima mean "do not wait".
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+using dev::waitcnt_vm;
 constexpr int kWaitVm0 = waitcnt_vm(0);
 
 constexpr int kStages = 4;
@@ -157,24 +151,8 @@ static_assert(kStages * kStageBytesDma <= kLdsOperandBytes, "LDS ring");
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
-}
-
-// One 16-byte-per-lane copy from a buffer straight into LDS at `lds` (M0) +
-// 16 * lane.  Issued as inline asm so the compiler does not track it: its
-// waits for LDS copies would cover every copy in flight (including the ones
-// just issued for later stages), serializing the ring.  The main loop waits
-// for the copies itself; vector memory operations complete in issue order,
-// so any wait the compiler inserts for its own loads stays correct (at worst
-// stronger than needed).
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset,
-                                              uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
-}
+using dev::copy16_to_lds;
+using dev::lds_addr;
 
 // C tile [m0, m0+256) x [n0, n0+256) += A[m0.., k_begin..k_end) . B[n0.., ...]^T
 //
@@ -352,7 +330,7 @@ __device__ __forceinline__ void store4(T* p, f32x4_t v) {
 }
 
 template <typename T, int kMode, bool kKTail>
-__global__ __launch_bounds__(kThreads) void k_gemm_nt(GemmNT g) {
+__device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   const int tiles_m = cdiv(g.M, kTile), tiles_n = cdiv(g.N, kTile);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -558,6 +536,16 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   }
 }
 
+// Two entry points with the same body so profiles tell the products apart.
+template <typename T, int kMode>
+__global__ __launch_bounds__(kThreads) void k_gemm_grad_x(GemmNT g) {
+  gemm_nt_tile<T, kMode, false>(g);
+}
+template <typename T, int kMode>
+__global__ __launch_bounds__(kThreads) void k_gemm_grad_w(GemmNT g) {
+  gemm_nt_tile<T, kMode, false>(g);
+}
+
 template <typename T>
 hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   const int tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile) * g.splits;
@@ -566,13 +554,20 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   // Every split range and K must be whole stages on this path.
   if (g.K % kBK != 0 || g.k_split % kBK != 0) return hipErrorInvalidValue;
+  const bool wgrad = g.role == GemmRole::kGradW;
+#define LCE_GEMM_CASE(mode)                                                   \
+  case EpiMode::mode:                                                         \
+    if (wgrad) k_gemm_grad_w<T, static_cast<int>(EpiMode::mode)><<<grid, block, 0, s>>>(g); \
+    else k_gemm_grad_x<T, static_cast<int>(EpiMode::mode)><<<grid, block, 0, s>>>(g);       \
+    break;
   switch (g.mode) {
-    case EpiMode::kStoreF32: k_gemm_nt<T, 0, false><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kAccumF32: k_gemm_nt<T, 1, false><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kFinalOut: k_gemm_nt<T, 2, false><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kStoreOut: k_gemm_nt<T, 3, false><<<grid, block, 0, s>>>(g); break;
-    case EpiMode::kAccumOut: k_gemm_nt<T, 4, false><<<grid, block, 0, s>>>(g); break;
+    LCE_GEMM_CASE(kStoreF32)
+    LCE_GEMM_CASE(kAccumF32)
+    LCE_GEMM_CASE(kFinalOut)
+    LCE_GEMM_CASE(kStoreOut)
+    LCE_GEMM_CASE(kAccumOut)
   }
+#undef LCE_GEMM_CASE
   return hipGetLastError();
 }
 

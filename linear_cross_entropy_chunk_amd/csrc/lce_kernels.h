@@ -25,6 +25,8 @@ enum class EpiMode : int {
 // K contiguous ("NT").  The result is stored transposed, C[n * ldc + m]
 // (M a multiple of 4).  K is split into `splits` ranges of k_split elements
 // (a multiple of the stage depth); split s writes C + s * split_stride.
+enum class GemmRole : int { kGradX = 0, kGradW = 1 };   // names the kernel in profiles
+
 struct GemmNT {
   const void* A; int64_t lda;
   const void* B; int64_t ldb;
@@ -34,6 +36,7 @@ struct GemmNT {
   const void* Cin;                // input of the accumulate modes (ld = ldc)
   EpiMode mode;
   int group_m;                    // tile-order grouping along M
+  GemmRole role;
 };
 hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
 

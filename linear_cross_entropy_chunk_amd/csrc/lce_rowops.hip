@@ -11,6 +11,7 @@
 // empty-mean NaN fill) and Liger-Kernel issue #343 (cross entropy computed
 // and its gradient written over the logits in one kernel).
 #include "lce_kernels.h"
+#include "lce_device.h"
 
 #include <math.h>
 
@@ -312,7 +313,11 @@ __global__ void k_fill_zero(i32x4_t* __restrict__ p, int64_t n16, char* __restri
 // One workgroup per row.  Pass 1 streams the row with 16-byte loads keeping
 // an online (max, sum of exp); pass 2 streams it again and overwrites it with
 // g_n (softmax - onehot).  The target logit is read before any overwrite.
+// Each thread keeps kCeUnroll independent 16-byte loads in flight, so a
+// workgroup has 1024 x 8 x 16 bytes outstanding: enough to cover the memory
+// latency at the per-CU share of HBM bandwidth.
 constexpr int kCeThreads = 1024;
+constexpr int kCeUnroll = 8;
 __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, int V,
                                                        const int* __restrict__ tc,
                                                        const float* __restrict__ g,
@@ -324,14 +329,25 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
   const int V4 = V >> 2;
   const int t = tc[n];
   float m = -INFINITY, s = 0.0f;
-  for (int i = threadIdx.x; i < V4; i += kCeThreads) {
-    const f32x4_t x = row[i];
-    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  for (int base = threadIdx.x; base < V4; base += kCeThreads * kCeUnroll) {
+    f32x4_t x[kCeUnroll];
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int i = base + u * kCeThreads;
+      x[u] = i < V4 ? row[i] : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u)
+      mx = fmaxf(mx, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
     if (mx > m) {
       s *= fast_exp(m - mx);
       m = mx;
     }
-    s += fast_exp(x[0] - m) + fast_exp(x[1] - m) + fast_exp(x[2] - m) + fast_exp(x[3] - m);
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u)
+      s += fast_exp(x[u][0] - m) + fast_exp(x[u][1] - m) + fast_exp(x[u][2] - m) +
+           fast_exp(x[u][3] - m);
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
@@ -358,14 +374,143 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
   __syncthreads();
   const float L = bcast[0];
   const float gn = g[n];
-  for (int i = threadIdx.x; i < V4; i += kCeThreads) {
-    const f32x4_t x = row[i];
-    f32x4_t y;
+  for (int base = threadIdx.x; base < V4; base += kCeThreads * kCeUnroll) {
+    f32x4_t x[kCeUnroll];
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int i = base + u * kCeThreads;
+      if (i < V4) x[u] = row[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int i = base + u * kCeThreads;
+      if (i >= V4) continue;
+      f32x4_t y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = gn * fast_exp(x[u][e] - L);
+        if (4 * i + e == t) y[e] -= gn;
+      }
+      __builtin_nontemporal_store(y, row + i);
+    }
+  }
+}
+
+// Single-read variant for long rows: the whole row stays on chip, kRegVec
+// 16-byte vectors per thread in registers plus a tail of up to kCeTailVec
+// vectors in LDS (copied there straight from memory), so the row is read from
+// HBM once and written once.  Max, then exp(x - max) in place with its sum,
+// then the gradient g (e / sum - onehot): one exponential per element.
+constexpr int kCeTailVec = 8192;                       // 128 KiB of LDS
+constexpr int kOnThreads = 512;                        // 2 waves per SIMD: 256 registers each
+template <int kRegVec>
+__global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict__ z, int V,
+                                                              const int* __restrict__ tc,
+                                                              const float* __restrict__ g,
+                                                              float* __restrict__ loss_rows) {
+  __shared__ __attribute__((aligned(16))) f32x4_t tail[kCeTailVec];
+  __shared__ float wred[kOnThreads / 64];
+  __shared__ float bcast[2];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4_t* row = reinterpret_cast<f32x4_t*>(z + static_cast<int64_t>(n) * V);
+  const int V4 = V >> 2;
+  const int nreg = min(V4, kOnThreads * kRegVec);       // vectors held in registers
+  const int ntail = V4 - nreg;                          // vectors held in LDS
+  const int t = tc[n];
+
+  // The tail, 1 KiB blocks of 64 vectors, one copy instruction each; lanes
+  // past the row end read as zero (and are never used).
+  const __amdgpu_buffer_rsrc_t rs = dev::make_rsrc(row, static_cast<int64_t>(V4) * 16);
+  for (int b = wave; b * 64 < ntail; b += kOnThreads / 64)
+    dev::copy16_to_lds(rs, (nreg + b * 64 + lane) * 16, dev::lds_addr(tail + b * 64));
+  // Register part: one lane offset, the vector stride in the scalar offset.
+  f32x4_t x[kRegVec];
+#pragma unroll
+  for (int u = 0; u < kRegVec; ++u) {
+    const int i = tid + u * kOnThreads;
+    const f32x4_t v = __builtin_bit_cast(
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, u * kOnThreads * 16, 0));
+    x[u] = i < nreg ? v : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+  float zt = 0.0f;
+  if (tid == 0 && t >= 0) zt = z[static_cast<int64_t>(n) * V + t];
+  __builtin_amdgcn_s_waitcnt(dev::waitcnt_vm(0));
+  __syncthreads();
+
+  auto block_max = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    if (lane == 0) wred[wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+      float r = wred[0];
+      for (int w = 1; w < kOnThreads / 64; ++w) r = fmaxf(r, wred[w]);
+      bcast[0] = r;
+    }
+    __syncthreads();
+    return bcast[0];
+  };
+  auto block_sum = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) wred[wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+      float r = 0.0f;
+      for (int w = 0; w < kOnThreads / 64; ++w) r += wred[w];
+      bcast[1] = r;
+    }
+    __syncthreads();
+    return bcast[1];
+  };
+
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kRegVec; ++u)
+    m = fmaxf(m, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+  for (int j = tid; j < ntail; j += kOnThreads) {
+    const f32x4_t v = tail[j];
+    m = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  }
+  const float M = block_max(m);
+
+  float s = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kRegVec; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      y[e] = gn * fast_exp(x[e] - L);
-      if (4 * i + e == t) y[e] -= gn;
+      x[u][e] = fast_exp(x[u][e] - M);       // -inf slots become 0
+      s += x[u][e];
     }
+  for (int j = tid; j < ntail; j += kOnThreads) {
+    f32x4_t v = tail[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = fast_exp(v[e] - M);
+      s += v[e];
+    }
+    tail[j] = v;
+  }
+  const float S = block_sum(s);
+  const float L = M + logf(S);
+  if (tid == 0) loss_rows[n] = t >= 0 ? L - zt : 0.0f;
+
+  const float gn = g[n];
+  const float scale = gn / S;
+#pragma unroll
+  for (int u = 0; u < kRegVec; ++u) {
+    const int i = tid + u * kOnThreads;
+    if (i >= nreg) continue;
+    f32x4_t y = x[u] * scale;
+    if (t >= 4 * i && t < 4 * i + 4) y[t - 4 * i] -= gn;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, y), rs, tid * 16,
+                                           u * kOnThreads * 16, 0);
+  }
+  for (int j = tid; j < ntail; j += kOnThreads) {
+    const int i = nreg + j;
+    f32x4_t y = tail[j] * scale;
+    if (t >= 4 * i && t < 4 * i + 4) y[t - 4 * i] -= gn;
     __builtin_nontemporal_store(y, row + i);
   }
 }
@@ -467,7 +612,13 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
                            float* loss_rows, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  // Rows of 64K..128K classes stay on chip (one HBM read); others stream twice.
+  const int V4 = V / 4;
+  auto fits = [&](int reg) { return V4 <= kOnThreads * reg + kCeTailVec; };
+  if (V4 >= 16384 && fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  else if (V4 >= 16384 && fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  else if (V4 >= 16384 && fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  else k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, loss_rows);
   return hipGetLastError();
 }
 

@@ -43,3 +43,27 @@ def test_ce_large_logits_and_all_ignored():
     t_all = np.full(16, -100)
     loss, nv, dl = run_ce(z, t_all)
     assert nv == 0 and math.isnan(loss[0]) and np.all(np.isnan(dl))
+
+
+@pytest.mark.parametrize("V", [65536, 100000, 131068, 131072])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_ce_long_rows_on_chip(V, reduction):
+    """Rows of 64K..128K classes take the single-read path (the row held in
+    registers and LDS); ragged lengths exercise its partial vectors."""
+    require_gpu()
+    rng = np.random.default_rng(V + 1)
+    N = 9
+    z = (rng.standard_normal((N, V)) * 2.0).astype(np.float32)
+    t = rng.integers(0, V, N)
+    t[4] = -100
+    t[0] = V - 1                      # the last class, inside the LDS tail
+    log(f"ce on-chip V={V} reduction={reduction}")
+    loss, nv, dl = run_ce(z, t, reduction=reduction)
+    ref_loss, ref_dl = oracle.softmax_cross_entropy(z, t, reduction=reduction)
+    assert nv == N - 1
+    if reduction == "none":
+        assert rel_err(loss, ref_loss) <= 1e-5
+    else:
+        assert abs(loss[0] - ref_loss) <= 1e-5 * abs(ref_loss)
+    assert rel_err(dl, ref_dl) <= 1e-4
+    assert np.all(dl[4] == 0.0)
