@@ -32,7 +32,7 @@ PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_cross_entropy_chunk_amd", "csrc", f)
-                  for f in ("lce_gemm.hip", "lce_rowops.hip", "lce_kernels.h")]
+                  for f in ("lce_gemm.hip", "lce_rowops.hip", "lce_kernels.h", "lce_device.h")]
 
 
 def log(msg: str) -> None:
@@ -240,6 +240,75 @@ def bench_ce(args) -> dict:
     return result
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """A plain device-to-device copy of `nbytes`: the achievable-bandwidth
+    yardstick, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
+    the others' (it moves exactly nbytes each way)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    return {"bytes_each_way": nbytes, "ms": ms, "gbs_read_plus_write": 2 * nbytes / ms / 1e6}
+
+
+# rocprofv3 kernel names of each timed kernel class
+KERNEL_NAMES = {"logits": "k_logits_lse", "gemm_x": "k_gemm_grad_x", "gemm_w": "k_gemm_grad_w",
+                "ce_rows": "k_ce_rows", "copy": "copyBuffer"}
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel class from two
+    rocprofv3 --pmc runs, scaled by the same counters of the calibration copy
+    (known bytes each way); written to the traffic file with the kernel
+    sources' hash, so a later kernel change invalidates them."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                for cls, sub in KERNEL_NAMES.items():
+                    if sub in r["Kernel_Name"]:
+                        vals.setdefault(cls, []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    known_kib = (1 << 30) / 1024.0
+    f_scale = known_kib / fetch["copy"] if fetch.get("copy") else None
+    w_scale = known_kib / write["copy"] if write.get("copy") else None
+    out = {}
+    for cls in fetch:
+        if cls == "copy" or cls not in write or not f_scale or not w_scale:
+            continue
+        rd = fetch[cls] * f_scale * 1024
+        wr = write[cls] * w_scale * 1024
+        out[cls] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                    "fetch_kib_raw": fetch[cls], "write_kib_raw": write[cls],
+                    "copy_scale_fetch": f_scale, "copy_scale_write": w_scale,
+                    "source_sha": kernel_source_sha(), "command": command}
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    data[workload] = out
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -254,7 +323,17 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class, not only the GEMMs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also time a plain 1 GiB device copy (bandwidth yardstick)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into the traffic file")
+    ap.add_argument("--counters-command", default="",
+                    help="the command that produced the counter CSVs (recorded)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        out = summarize_counters(*args.summarize_counters, args.workload, args.counters_command)
+        print(json.dumps(out, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"this build runs on one GPU only (--gpus {args.gpus} requested); the multi-GPU "
               "sharding is a design note, not an implementation", file=sys.stderr)
@@ -264,6 +343,9 @@ def main() -> int:
         print("bench.py needs the GPU", file=sys.stderr)
         return 1
     result = bench_ce(args) if args.workload == "ce-f32" else bench_lce(args)
+    if args.calibrate_copy:
+        result["copy_calibration"] = copy_calibration()
+        log(f"copy: {result['copy_calibration']['gbs_read_plus_write']:.0f} GB/s (read + write)")
     print(json.dumps(result), flush=True)
     return 0
 
