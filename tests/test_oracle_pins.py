@@ -5,7 +5,10 @@ central finite differences, invariants the definition implies, and special
 cases that reduce to an independent library routine (torch's CPU
 cross_entropy in float64).  CPU only.
 """
+import json
 import math
+import pathlib
+import re
 
 import numpy as np
 import pytest
@@ -15,6 +18,7 @@ import oracle
 from lce_inputs import small_case
 
 RED = ["mean", "sum", "none"]
+GOLDEN = pathlib.Path(__file__).parent / "golden"
 
 
 def _case(N=6, D=4, V=9, seed=0, ignore_frac=0.2, bias=True, **kw):
@@ -71,27 +75,26 @@ def test_two_classes_is_softplus():
         assert abs(r["loss"][n] - expect) <= 1e-14 * max(1.0, expect)
 
 
+def _closed_form(expr):
+    """Evaluate a fixture's closed-form expression in e (nothing else allowed)."""
+    assert re.fullmatch(r"[0-9e()+\-*/ .log]+", expr), expr
+    return eval(expr, {"__builtins__": {}}, {"log": math.log, "e": math.e})
+
+
 def test_hand_worked_example():
-    """X = I2, W = [[0,0],[1,0],[0,1]], b = 0, t = (1, 0): the logits are
-    (0,1,0) and (0,0,1), so loss = (log(2+e) - 1, log(2+e)); mean loss =
-    log(2+e) - 1/2; grad_b = (1/2)(softmax rows - onehot rows) summed."""
-    X = np.eye(2)
-    W = np.array([[0.0, 0.0], [1.0, 0.0], [0.0, 1.0]])
-    t = np.array([1, 0])
-    e = math.e
-    r = oracle.linear_cross_entropy(X, W, np.zeros(3), t, reduction="mean")
-    assert abs(r["loss"] - (math.log(2 + e) - 0.5)) < 1e-15
-    np.testing.assert_allclose(r["loss_rows"], [math.log(2 + e) - 1, math.log(2 + e)],
-                               rtol=1e-15)
-    p0 = np.array([1, e, 1]) / (2 + e)
-    p1 = np.array([1, 1, e]) / (2 + e)
-    gb = 0.5 * (p0 - [0, 1, 0]) + 0.5 * (p1 - [1, 0, 0])
-    np.testing.assert_allclose(r["grad_b"], gb, rtol=1e-14)
-    # grad_X[n] = sum_j dL[n, j] W[j]; grad_W[j] = sum_n dL[n, j] X[n]
-    d0, d1 = 0.5 * (p0 - [0, 1, 0]), 0.5 * (p1 - [1, 0, 0])
-    np.testing.assert_allclose(r["grad_X"], [d0 @ W, d1 @ W], rtol=1e-14, atol=1e-16)
-    np.testing.assert_allclose(r["grad_W"], np.stack([d0, d1], 1), rtol=1e-14, atol=1e-16)
-    assert list(r["argmax"]) == [1, 2]
+    """The 2x2x3 case worked by hand in tests/golden (its derivation and
+    sources are in the fixture)."""
+    fx = json.loads((GOLDEN / "hand_worked_example.json").read_text())
+    inp, exp = fx["inputs"], fx["expect"]
+    r = oracle.linear_cross_entropy(np.array(inp["X"], float), np.array(inp["W"], float),
+                                    np.array(inp["b"], float), np.array(inp["t"]),
+                                    reduction=inp["reduction"])
+    ev = np.vectorize(_closed_form, otypes=[float])
+    assert abs(r["loss"] - _closed_form(exp["loss"])) < 1e-15
+    np.testing.assert_allclose(r["loss_rows"], ev(exp["loss_rows"]), rtol=1e-15)
+    for k in ("grad_b", "grad_X", "grad_W"):
+        np.testing.assert_allclose(r[k], ev(np.array(exp[k])), rtol=1e-14, atol=1e-16)
+    assert list(r["argmax"]) == exp["argmax"]
 
 
 # -------------------------------------------------- an independent library
