@@ -22,15 +22,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // One 16-byte-per-lane copy from a buffer straight into LDS at `lds` (M0) +
-// 16 * lane.  Issued as inline asm so the compiler does not track it: its
-// waits for LDS copies would cover every copy in flight (including ones
-// issued for later use).  Callers wait for the copies themselves; vector
-// memory operations complete in issue order, so any wait the compiler
-// inserts for its own loads stays correct (at worst stronger than needed).
+// 16 * lane; the global address is base + voffset + soffset.  Issued as
+// inline asm so the compiler does not track it: its waits for LDS copies
+// would cover every copy in flight (including ones issued for later use).
+// Callers wait for the copies themselves; vector memory operations complete
+// in issue order, so any wait the compiler inserts for its own loads stays
+// correct (at worst stronger than needed).  The s_nop is the wait state the
+// ISA asks for between an SALU write of M0 and an LDS-DMA read of it.
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset,
-                                              uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+                                              uint32_t lds, int soffset = 0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
 }
 
 // gfx9 s_waitcnt immediates: vmcnt in bits [3:0] and [15:14], expcnt [6:4],

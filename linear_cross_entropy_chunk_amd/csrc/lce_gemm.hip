@@ -1,17 +1,20 @@
 // MFMA GEMM tiles for gfx950 (CDNA4).
 //
-// One workgroup of 256 threads (four 64-wide waves in a 2 x 2 grid) computes a
-// 256 x 256 tile of C = A . B^T where both operands keep K contiguous.  Each
-// wave owns a 128 x 128 sub-tile held as 4 x 4 accumulator blocks of the
-// 32 x 32 MFMA (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2f32 for
-// fp32), fp32 accumulation throughout.
+// One workgroup of 256 threads (four 64-wide waves, one per SIMD, in a 2 x 2
+// grid) computes a 256 x 256 tile of P = A . B^T where both operands keep K
+// contiguous.  Each wave owns a 128 x 128 sub-tile held as 4 x 4 accumulator
+// blocks of the 32 x 32 MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
+// v_mfma_f32_32x32x2f32 for fp32) in the 256 accumulation registers, fp32
+// accumulation throughout.
 //
-// K is walked in stages of 128 bytes per row (64 bf16 or 32 fp32).  A stage
-// of both operands (2 x 32 KiB) is loaded with 16-byte global loads into
-// registers one stage ahead of the MFMAs and written to the other half of a
-// double-buffered LDS ring, so one barrier per stage suffices.  Inside LDS the
-// eight 16-byte chunks of a row are XOR-swizzled by (row & 7), which makes the
-// MFMA fragment reads (32 rows at one chunk position) bank-conflict free.
+// K is walked in stages of 128 bytes per row (64 bf16 or 32 fp32).  Operand
+// tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds),
+// each instruction moving eight whole 128-byte rows, i.e. whole L2 lines.
+// The 160 KiB of LDS form five 32 KiB slots, one operand of one stage each:
+// stage s keeps A in slot 2s mod 5 and B in slot 2s + 1 mod 5, so while stage
+// s is consumed, B of stage s + 1 and A of stage s + 2 are in flight.  Copies
+// are spread over the MFMA stream (one every few MFMAs) to keep the per-CU
+// address unit below saturation, and there is one barrier per stage.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the block id is
 // remapped so each XCD walks a contiguous range of tiles, grouped along M, and
@@ -39,19 +42,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// Wave layout of a 256 x 256 tile: kWavesM x kWavesN waves, each owning a
-// (256 / kWavesM) x (256 / kWavesN) sub-tile of 32 x 32 accumulator blocks.
-#ifndef LCE_WAVES_N
-#define LCE_WAVES_N 4
-#endif
+// Wave layout of a 256 x 256 tile: kWavesM x kWavesN waves (one per SIMD),
+// each owning a 128 x 128 sub-tile of 32 x 32 accumulator blocks.
 constexpr int kWavesM = 2;
-constexpr int kWavesN = LCE_WAVES_N;
+constexpr int kWavesN = 2;
 constexpr int kWaves = kWavesM * kWavesN;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveN = kTile / kWavesN;      // columns per wave
 constexpr int kJ = kWaveN / 32;               // 32-column blocks per wave
-constexpr int kCopies = 16 / kWaves;          // 16-row copy blocks per wave per operand
-constexpr int kLdsOperandBytes = 128 * 1024;                 // operand ring
+constexpr int kRowBytes = 128;                // bytes per row per K stage
+constexpr int kSlotBytes = kTile * kRowBytes; // one operand of one stage: 32 KiB
+constexpr int kSlots = 5;
+constexpr int kLdsOperandBytes = kSlots * kSlotBytes;        // 160 KiB ring
+constexpr int kCopies = kTile / 8 / kWaves;   // 8-row copies per operand per wave per stage
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Elt;
@@ -119,64 +122,52 @@ using dev::make_rsrc;
 using dev::kOutOfRange;
 
 // ------------------------------------------------------------- main loop
-// K is walked in stages of 64 bytes per row (32 bf16 or 16 fp32).  Both
-// operands of a stage (2 x 256 rows x 64 bytes = 32 KiB) are copied from
-// global memory straight into LDS with buffer_load_dwordx4 ... lds: each wave
-// instruction moves 16 rows x 64 bytes, lane i's 16 bytes landing at LDS byte
-// 16 i of the instruction's 1 KiB block.  Four stages form a ring, filled
-// three stages ahead of the MFMAs, with no staging registers and no LDS write
-// instructions.
-//
-// LDS chunk swizzle: the 16-byte chunk with logical index c of row r sits at
-// physical chunk c ^ ((r >> 2) & 3).  gfx950 serves a ds_read_b128 16 lanes
-// (256 bytes) per cycle; the fragment reads put 16 consecutive rows at one
-// logical chunk in such a group, and with 64-byte rows this swizzle spreads
-// them over all 16 bank groups.  The copy applies the inverse on the global
-// side: lane i of a copy instruction fetches logical chunk (i & 3) ^ swz(row).
-namespace sched {   // instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100, kDsWrite = 0x200;
-}
-
-using dev::waitcnt_vm;
-constexpr int kWaitVm0 = waitcnt_vm(0);
-
-constexpr int kStages = 4;
-constexpr int kRowBytes = 64;
-// copies a wave leaves in flight for the two stages after the current one
-constexpr int kWaitVmLater = waitcnt_vm(2 * 2 * kCopies);                                  // per stage row
-constexpr int kOpStageBytes = kTile * kRowBytes;              // 16 KiB per operand
-constexpr int kStageBytesDma = 2 * kOpStageBytes;             // 32 KiB per stage
-static_assert(kStages * kStageBytesDma <= kLdsOperandBytes, "LDS ring");
-
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
-
+// LDS layout of a slot: row r of the 256-row operand tile at byte 128 r; its
+// 16-byte chunk with logical index c sits at physical chunk c ^ ((r >> 1) & 7).
+// A ds_read_b128 serves 16 lanes per cycle, and the fragment reads put 16
+// consecutive rows at one logical chunk in such a group: with 128-byte rows
+// the bank group of (r, p) is 8 (r & 1) + p, and the swizzle makes those 16
+// distinct.  The copy applies the inverse on the global side: lane i of a
+// copy instruction fetches logical chunk (i & 7) ^ swz(row) of row i / 8.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 using dev::copy16_to_lds;
 using dev::lds_addr;
+using dev::waitcnt_vm;
+constexpr int kWaitVm0 = waitcnt_vm(0);
 
-// C tile [m0, m0+256) x [n0, n0+256) += A[m0.., k_begin..k_end) . B[n0.., ...]^T
+// C tile [m0, m0+256) x [n0, n0+256) = A[m0.., k_begin..k_end) . B[n0.., ...]^T
 //
 // Rows past M (N) read as zero (each copy's descriptor covers only the
 // tile's existing rows).  With kKTail, 16-byte chunks at or past k_end read
 // as zero too (their offsets are sent out of range).
+//
+// Per stage s (four 16-k sub-steps, 16 MFMAs per wave each), every wave:
+//   sub-steps 0-2: MFMAs from registers; LDS reads of the next sub-step;
+//                  8 copies of A of stage s + 2 into slot 2s + 4 mod 5 (the
+//                  slot B of stage s - 1 left), one every six MFMAs;
+//   wait for its copies of stage s + 1 (all but the 8 just issued) and for
+//   its LDS reads; barrier: stage s + 1 is whole and stage s is fully read;
+//   sub-step 3:    MFMAs; LDS reads of sub-step 0 of stage s + 1; 8 copies
+//                  of B of stage s + 2 into slot 2s mod 5 (A of stage s).
+// A stage's B thus has about three sub-steps to land and its A about seven.
 template <typename T, bool kKTail>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
                                          int k_begin, int k_end, char* __restrict__ lds,
                                          f32x16_t (&acc)[4][kJ]) {
+  static_assert(kJ == 4 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
   constexpr int kEs = static_cast<int>(sizeof(T));
-  constexpr int kBK = kRowBytes / kEs;                 // K elements per stage
-  constexpr int kVec = 16 / kEs;                       // elements per 16-byte chunk
+  constexpr int kBK = kRowBytes / kEs;            // K elements per stage
+  constexpr int kVec = 16 / kEs;                  // elements per 16-byte chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy bases in SGPRs
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16_t{0};
-
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   if (nk <= 0) return;
 
@@ -184,112 +175,98 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
                                               static_cast<int64_t>(min(M - m0, kTile)) * lda * kEs);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<int64_t>(n0) * ldb,
                                               static_cast<int64_t>(min(N - n0, kTile)) * ldb * kEs);
-  // Copy mapping: wave w issues instructions j < kCopies per operand per
-  // stage, covering rows 16 (kCopies w + j) .. +16; lane i takes row
-  // 16 (kCopies w + j) + i / 4, physical chunk i & 3.
-  const int crow = lane >> 2;                      // row inside the 16-row block
-  const int pchunk = lane & 3;
+  // Copy j of a wave covers rows 8 (kCopies wave + j) .. + 8; lane i takes
+  // row + i / 8, physical chunk i & 7.  The stage's K offset travels in the
+  // instruction's scalar offset.
+  const int crow = lane >> 3, pchunk = lane & 7;
   int va[kCopies], vb[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
-    const int row = 16 * (kCopies * wave + j) + crow;
+    const int row = 8 * (kCopies * wave + j) + crow;
     const int lchunk = pchunk ^ swz(row);
     va[j] = (row * static_cast<int>(lda) + lchunk * kVec) * kEs;
     vb[j] = (row * static_cast<int>(ldb) + lchunk * kVec) * kEs;
   }
-  auto copy_stage = [&](int st, int buf) {
-    const int k0 = k_begin + st * kBK;
-    const int koff = k0 * kEs;
-    char* sa = lds + buf * kStageBytesDma;
-    char* sb = sa + kOpStageBytes;
-    bool kin = true;
-    if constexpr (kKTail) kin = (k0 + (pchunk ^ swz(crow)) * kVec) < k_end;
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) {
-      const int blk = (kCopies * wave + j) * 1024;
-      int oa = va[j] + koff, ob = vb[j] + koff;
-      if constexpr (kKTail) {
-        // the logical chunk of this lane is the same for every j (rows 16 apart)
-        oa = kin ? oa : kOutOfRange;
-        ob = kin ? ob : kOutOfRange;
-      }
-      copy16_to_lds(ra, oa, lds_addr(sa + blk));
-      copy16_to_lds(rb, ob, lds_addr(sb + blk));
+  auto copy = [&](int st, int slot, bool opb, int j) {
+    const int k0 = k_begin + min(st, nk - 1) * kBK;   // stages past the end repeat the last
+    int o = opb ? vb[j] : va[j];
+    if constexpr (kKTail) {
+      const int row = 8 * (kCopies * wave + j) + crow;
+      o = (k0 + (pchunk ^ swz(row)) * kVec) < k_end ? o : kOutOfRange;
     }
+    copy16_to_lds(opb ? rb : ra, o, lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024),
+                  __builtin_amdgcn_readfirstlane(k0 * kEs));
   };
 
   // Fragment reads: lane l reads row (l & 31) of each 32-row block at logical
-  // chunk (2 kk + (l >> 5)), kk = 0, 1.  Rows 32 i + (l & 31) share the
-  // swizzle of (l & 31).
-  const int frow = lane & 31;
-  const int fhalf = lane >> 5;
-  const int fsw = swz(frow);
+  // chunk 2 kk + (l >> 5) of sub-step kk.  Rows 32 x + (l & 31) share the
+  // swizzle of (l & 31).  Read r (0..7) of a sub-step: A block r / 2 if r is
+  // even, else B block r / 2.
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = swz(frow);
   const int a_row = (wm * 128 + frow) * kRowBytes;
   const int b_row = (wn * kWaveN + frow) * kRowBytes;
+  int coff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) coff[kk] = ((2 * kk + fhalf) ^ fsw) << 4;
   i32x4_t af[2][4], bf[2][kJ];
-  auto fread = [&](const char* sa, const char* sb, int kk, int buf) {
-    const int c = ((2 * kk + fhalf) ^ fsw) << 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[buf][i] = *reinterpret_cast<const i32x4_t*>(sa + a_row + i * 32 * kRowBytes + c);
-#pragma unroll
-    for (int j = 0; j < kJ; ++j)
-      bf[buf][j] = *reinterpret_cast<const i32x4_t*>(sb + b_row + j * 32 * kRowBytes + c);
+  auto read = [&](int sa, int sb, int kk, int set, int r) {
+    const int x = r >> 1;
+    if (r & 1)
+      bf[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sb * kSlotBytes + b_row + coff[kk] +
+                                                     x * 32 * kRowBytes);
+    else
+      af[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sa * kSlotBytes + a_row + coff[kk] +
+                                                     x * 32 * kRowBytes);
   };
-  auto mfmas = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) mfma_step<T>(acc[i][j], af[buf][i], bf[buf][j]);
-  };
-  constexpr int kMfmaPer = sizeof(T) == 2 ? 1 : 4;
 
-  // Ping-pong schedule.  The waves form two groups of four, one wave of
-  // each group per SIMD (wave w runs on SIMD w % 4).  Every wave runs the
-  // same loop -- compute stage kt from registers | barrier | read stage
-  // kt + 1 into registers and issue its copies of stage kt + 4 | barrier --
-  // but group 1 takes one extra barrier before the loop (and group 0 one
-  // after it), which shifts group 1 by one phase: in every phase one wave
-  // per SIMD issues MFMAs while the other reads LDS and issues copies.
-  //
-  // Numbering the common barriers B1, B2, ...: group 0 reads stage s in
-  // (B(2s-1), B(2s)) and group 1 in (B(2s), B(2s+1)), so stage s must be
-  // whole by B(2s-1).  Each wave waits, at the end of iteration kt's memory
-  // phase, until its own copies up to stage kt + 2 have landed (copies
-  // complete in issue order); group 0 passes that point before B(2kt+2),
-  // group 1 before B(2kt+3) = B(2(kt+2)-1).  The prologue covers stages 0
-  // and 1.  Stage s + 4 reuses the buffer of stage s once both groups hold
-  // stage s in registers: group 0 copies after B(2s+1), group 1 after
-  // B(2s+2), and the barriers wait for all LDS reads issued before them.
-  const int group = wave >> 2;
-  constexpr int kPerStage = 2 * kCopies;            // copies per wave per stage
-  static_assert(kWaves == 8, "the ping-pong schedule needs two groups of four waves");
-
+  // Prologue: stages 0 and 1 whole (slots 0-3), stage 0 landed.
 #pragma unroll
-  for (int st = 0; st < kStages; ++st) copy_stage(min(st, nk - 1), st);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage));
+  for (int j = 0; j < kCopies; ++j) { copy(0, 0, false, j); copy(0, 1, true, j); }
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) { copy(1, 2, false, j); copy(1, 3, true, j); }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
   __syncthreads();
-  fread(lds, lds + kOpStageBytes, 0, 0);
-  fread(lds, lds + kOpStageBytes, 1, 1);
-  if (group == 1) __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) read(0, 1, 0, 0, r);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // compute phase
-    __builtin_amdgcn_s_setprio(1);
-    mfmas(0);
-    mfmas(1);
-    __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
-    // memory phase
-    const int nxt = min(kt + 1, nk - 1);
-    const char* sn = lds + (nxt % kStages) * kStageBytesDma;
-    fread(sn, sn + kOpStageBytes, 0, 0);
-    fread(sn, sn + kOpStageBytes, 1, 1);
-    copy_stage(min(kt + kStages, nk - 1), kt % kStages);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage));
-    __syncthreads();
+  // One stage; r5 = s mod 5 is a compile-time constant so every slot index is.
+  // The order of MFMAs, LDS reads and copies is pinned with scheduling
+  // barriers: every slot of the MFMA stream carries at most one read and one
+  // copy.
+  auto stage = [&](auto rc, int kt) {
+    constexpr int r5 = decltype(rc)::value;
+    const int s = kt + r5;
+    if (s >= nk) return;                                   // uniform
+    constexpr int sa = (2 * r5) % kSlots, sb = (2 * r5 + 1) % kSlots;
+    constexpr int na = (2 * r5 + 2) % kSlots, nb = (2 * r5 + 3) % kSlots;
+    constexpr int ca = (2 * r5 + 4) % kSlots, cb = (2 * r5 + 5) % kSlots;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 48; ++t) {                         // sub-steps 0-2
+      const int kk = t >> 4, u = t & 15, set = kk & 1;
+      mfma_step<T>(acc[u >> 2][u & 3], af[set][u >> 2], bf[set][u & 3]);
+      if (t % 6 == 0) copy(s + 2, ca, false, t / 6);
+      if (u < 8) read(sa, sb, kk + 1, set ^ 1, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies) & ~0x0f00);   // vmcnt(8) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {                         // sub-step 3
+      mfma_step<T>(acc[u >> 2][u & 3], af[1][u >> 2], bf[1][u & 3]);
+      if (u % 2 == 0) copy(s + 2, cb, true, u / 2);
+      if (u < 8) read(na, nb, 0, 0, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += kSlots) {
+    stage(std::integral_constant<int, 0>{}, kt);
+    stage(std::integral_constant<int, 1>{}, kt);
+    stage(std::integral_constant<int, 2>{}, kt);
+    stage(std::integral_constant<int, 3>{}, kt);
+    stage(std::integral_constant<int, 4>{}, kt);
   }
-  if (group == 0) __syncthreads();
   // Drain the copies still in flight before the LDS is reused.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
@@ -383,9 +360,11 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
 template <typename T, bool kStoreT, bool kArgmax, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
-  __shared__ float red_m[2][kTile];
-  __shared__ int red_i[2][kTile];
-  __shared__ float red_s[2][kTile];
+  // cross-wave exchange of the epilogue, in the operand ring (free once the
+  // main loop has drained)
+  float (*red_m)[kTile] = reinterpret_cast<float (*)[kTile]>(lds);
+  int (*red_i)[kTile] = reinterpret_cast<int (*)[kTile]>(lds + 2 * kTile * 4);
+  float (*red_s)[kTile] = reinterpret_cast<float (*)[kTile]>(lds + 4 * kTile * 4);
 
   const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
