@@ -2,10 +2,12 @@
 //
 // One workgroup of 256 threads (four 64-wide waves, one per SIMD, in a 2 x 2
 // grid) computes a 256 x 256 tile of P = A . B^T where both operands keep K
-// contiguous.  Each wave owns a 128 x 128 sub-tile held as 4 x 4 accumulator
-// blocks of the 32 x 32 MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
-// v_mfma_f32_32x32x2f32 for fp32) in the 256 accumulation registers, fp32
-// accumulation throughout.
+// contiguous.  Each wave owns a 128 x 128 sub-tile held as 8 x 8 accumulator
+// blocks of the 16 x 16 MFMA (v_mfma_f32_16x16x32_bf16 for bf16,
+// v_mfma_f32_16x16x4f32 for fp32) in the 256 accumulation registers, fp32
+// accumulation throughout.  The 16 x 16 shape moves a quarter of the
+// accumulator bytes per flop of the 32 x 32 one; the chip runs these tiles
+// at its power limit, where that is worth several percent of clock.
 //
 // K is walked in stages of 128 bytes per row (64 bf16 or 32 fp32).  Operand
 // tiles go from global memory straight into LDS (buffer_load_dwordx4 ... lds),
@@ -13,8 +15,8 @@
 // The 160 KiB of LDS form five 32 KiB slots, one operand of one stage each:
 // stage s keeps A in slot 2s mod 5 and B in slot 2s + 1 mod 5, so while stage
 // s is consumed, B of stage s + 1 and A of stage s + 2 are in flight.  Copies
-// are spread over the MFMA stream (one every few MFMAs) to keep the per-CU
-// address unit below saturation, and there is one barrier per stage.
+// are spread over the MFMA stream to keep the per-CU address unit below
+// saturation, and there is one barrier per stage.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the block id is
 // remapped so each XCD walks a contiguous range of tiles, grouped along M, and
@@ -38,18 +40,20 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // Wave layout of a 256 x 256 tile: kWavesM x kWavesN waves (one per SIMD),
-// each owning a 128 x 128 sub-tile of 32 x 32 accumulator blocks.
+// each owning a 128 x 128 sub-tile of kI x kJ blocks of 16 x 16.
 constexpr int kWavesM = 2;
 constexpr int kWavesN = 2;
 constexpr int kWaves = kWavesM * kWavesN;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveN = kTile / kWavesN;      // columns per wave
-constexpr int kJ = kWaveN / 32;               // 32-column blocks per wave
+constexpr int kWaveM = kTile / kWavesM;       // rows per wave
+constexpr int kWaveN = kTile / kWavesN;       // columns per wave
+constexpr int kBlk = 16;                      // MFMA block edge
+constexpr int kI = kWaveM / kBlk;             // 8 row blocks per wave
+constexpr int kJ = kWaveN / kBlk;             // 8 column blocks per wave
 constexpr int kRowBytes = 128;                // bytes per row per K stage
 constexpr int kSlotBytes = kTile * kRowBytes; // one operand of one stage: 32 KiB
 constexpr int kSlots = 5;
@@ -57,15 +61,15 @@ constexpr int kLdsOperandBytes = kSlots * kSlotBytes;        // 160 KiB ring
 constexpr int kCopies = kTile / 8 / kWaves;   // 8-row copies per operand per wave per stage
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T> struct Elt;
-template <> struct Elt<uint16_t> { static constexpr int kVec = 8; };
-template <> struct Elt<float> { static constexpr int kVec = 4; };
+// Accumulator layout of a 16 x 16 MFMA block, lane l, register r:
+//   column = l & 15, row = 4 (l >> 4) + r.
+// Wave (wm, wn) owns rows wm * 128 + 16 i + ..., columns wn * 128 + 16 j + ...
+typedef f32x4_t Acc[kI][kJ];
 
 __device__ __forceinline__ float to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 __device__ __forceinline__ float to_f32(float f) { return f; }
-
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -91,32 +95,31 @@ __device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_
   tn = idx / gm;
 }
 
+// One pair of 16-byte fragments.  Lane l holds row l & 15 of its 16-row
+// block at the logical chunk 4 h + (l >> 4) of sub-step h.
+//   bf16: the chunk is k = 8 (l >> 4) .. + 7 of the sub-step, exactly the
+//         operand of v_mfma_f32_16x16x32_bf16.
+//   fp32: the chunk holds 4 consecutive k; MFMA p takes component p, so lane
+//         group q supplies k = 4 q + p and the four MFMAs cover the 16 k of
+//         the sub-step once, with A and B paired on the same k.
 template <typename T>
-__device__ __forceinline__ void mfma_step(f32x16_t& acc, i32x4_t a, i32x4_t b);
+__device__ __forceinline__ void mfma_step(f32x4_t& acc, i32x4_t a, i32x4_t b);
 
 template <>
-__device__ __forceinline__ void mfma_step<uint16_t>(f32x16_t& acc, i32x4_t a, i32x4_t b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+__device__ __forceinline__ void mfma_step<uint16_t>(f32x4_t& acc, i32x4_t a, i32x4_t b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
-// fp32: a 16-byte fragment holds 4 consecutive k of one row; MFMA q takes
-// component q.  Lanes 0-31 hold k = 8s + q and lanes 32-63 k = 8s + 4 + q, so
-// the four MFMAs together cover the 8 k of the sub-step exactly once, and A
-// and B pair the same k.
 template <>
-__device__ __forceinline__ void mfma_step<float>(f32x16_t& acc, i32x4_t a, i32x4_t b) {
+__device__ __forceinline__ void mfma_step<float>(f32x4_t& acc, i32x4_t a, i32x4_t b) {
   const f32x4_t fa = __builtin_bit_cast(f32x4_t, a);
   const f32x4_t fb = __builtin_bit_cast(f32x4_t, b);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[0], fb[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[1], fb[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[2], fb[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[3], fb[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[0], fb[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[1], fb[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[2], fb[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[3], fb[3], acc, 0, 0, 0);
 }
-
-// Accumulator layout of a 32 x 32 MFMA block, lane l, register r:
-//   column = l & 31, row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
-// Wave (wm, wn) owns rows wm*128 + 32 i + ..., columns wn*kWaveN + 32 j + ...
 
 using dev::make_rsrc;
 using dev::kOutOfRange;
@@ -142,21 +145,22 @@ constexpr int kWaitVm0 = waitcnt_vm(0);
 // tile's existing rows).  With kKTail, 16-byte chunks at or past k_end read
 // as zero too (their offsets are sent out of range).
 //
-// Per stage s (four 16-k sub-steps, 16 MFMAs per wave each), every wave:
-//   sub-steps 0-2: MFMAs from registers; LDS reads of the next sub-step;
-//                  8 copies of A of stage s + 2 into slot 2s + 4 mod 5 (the
-//                  slot B of stage s - 1 left), one every six MFMAs;
+// Per stage s (two sub-steps of 4 chunks, 64 MFMAs per wave each), every wave:
+//   sub-step 0 and the first half of sub-step 1: MFMAs from registers; the
+//     16 LDS reads of sub-step 1 (during sub-step 0); 8 copies of A of stage
+//     s + 2 into slot 2s + 4 mod 5 (the slot B of stage s - 1 left);
 //   wait for its copies of stage s + 1 (all but the 8 just issued) and for
 //   its LDS reads; barrier: stage s + 1 is whole and stage s is fully read;
-//   sub-step 3:    MFMAs; LDS reads of sub-step 0 of stage s + 1; 8 copies
-//                  of B of stage s + 2 into slot 2s mod 5 (A of stage s).
-// A stage's B thus has about three sub-steps to land and its A about seven.
+//   second half of sub-step 1: MFMAs; the 16 LDS reads of sub-step 0 of
+//     stage s + 1; 8 copies of B of stage s + 2 into slot 2s mod 5.
+// A stage's B thus has three quarters of a stage to land and its A about
+// seven quarters.
 template <typename T, bool kKTail>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
                                          int k_begin, int k_end, char* __restrict__ lds,
-                                         f32x16_t (&acc)[4][kJ]) {
-  static_assert(kJ == 4 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
+                                         Acc& acc) {
+  static_assert(kI == 8 && kJ == 8 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
   constexpr int kEs = static_cast<int>(sizeof(T));
   constexpr int kBK = kRowBytes / kEs;            // K elements per stage
   constexpr int kVec = 16 / kEs;                  // elements per 16-byte chunk
@@ -165,9 +169,9 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy bases in SGPRs
   const int wm = wave / kWavesN, wn = wave % kWavesN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16_t{0};
+    for (int j = 0; j < kJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   if (nk <= 0) return;
 
@@ -198,25 +202,28 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
                   __builtin_amdgcn_readfirstlane(k0 * kEs));
   };
 
-  // Fragment reads: lane l reads row (l & 31) of each 32-row block at logical
-  // chunk 2 kk + (l >> 5) of sub-step kk.  Rows 32 x + (l & 31) share the
-  // swizzle of (l & 31).  Read r (0..7) of a sub-step: A block r / 2 if r is
+  // Fragment reads: lane l reads row (l & 15) of each 16-row block at logical
+  // chunk 4 h + (l >> 4) of sub-step h.  Rows 16 x + (l & 15) share the
+  // swizzle of (l & 15).  Read r (0..15) of a sub-step: A block r / 2 if r is
   // even, else B block r / 2.
-  const int frow = lane & 31, fhalf = lane >> 5, fsw = swz(frow);
-  const int a_row = (wm * 128 + frow) * kRowBytes;
+  const int frow = lane & 15, fq = lane >> 4, fsw = swz(frow);
+  const int a_row = (wm * kWaveM + frow) * kRowBytes;
   const int b_row = (wn * kWaveN + frow) * kRowBytes;
-  int coff[4];
+  int coff[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) coff[kk] = ((2 * kk + fhalf) ^ fsw) << 4;
-  i32x4_t af[2][4], bf[2][kJ];
-  auto read = [&](int sa, int sb, int kk, int set, int r) {
+  for (int h = 0; h < 2; ++h) coff[h] = ((4 * h + fq) ^ fsw) << 4;
+  i32x4_t af[2][kI], bf[2][kJ];
+  auto read = [&](int sa, int sb, int h, int set, int r) {
     const int x = r >> 1;
     if (r & 1)
-      bf[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sb * kSlotBytes + b_row + coff[kk] +
-                                                     x * 32 * kRowBytes);
+      bf[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sb * kSlotBytes + b_row + coff[h] +
+                                                     x * kBlk * kRowBytes);
     else
-      af[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sa * kSlotBytes + a_row + coff[kk] +
-                                                     x * 32 * kRowBytes);
+      af[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sa * kSlotBytes + a_row + coff[h] +
+                                                     x * kBlk * kRowBytes);
+  };
+  auto mfma = [&](int set, int u) {     // u = 8 i + j
+    mfma_step<T>(acc[u >> 3][u & 7], af[set][u >> 3], bf[set][u & 7]);
   };
 
   // Prologue: stages 0 and 1 whole (slots 0-3), stage 0 landed.
@@ -227,7 +234,7 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 8; ++r) read(0, 1, 0, 0, r);
+  for (int r = 0; r < 16; ++r) read(0, 1, 0, 0, r);
 
   // One stage; r5 = s mod 5 is a compile-time constant so every slot index is.
   // The order of MFMAs, LDS reads and copies is pinned with scheduling
@@ -242,21 +249,20 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
     constexpr int ca = (2 * r5 + 4) % kSlots, cb = (2 * r5 + 5) % kSlots;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 48; ++t) {                         // sub-steps 0-2
-      const int kk = t >> 4, u = t & 15, set = kk & 1;
-      mfma_step<T>(acc[u >> 2][u & 3], af[set][u >> 2], bf[set][u & 3]);
-      if (t % 6 == 0) copy(s + 2, ca, false, t / 6);
-      if (u < 8) read(sa, sb, kk + 1, set ^ 1, u);
+    for (int t = 0; t < 96; ++t) {          // sub-step 0, first half of sub-step 1
+      mfma(t >> 6, t & 63);
+      if (t < 64 && t % 8 == 0) copy(s + 2, ca, false, t / 8);
+      if (t < 64 && t % 4 == 0) read(sa, sb, 1, 1, t / 4);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies) & ~0x0f00);   // vmcnt(8) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {                         // sub-step 3
-      mfma_step<T>(acc[u >> 2][u & 3], af[1][u >> 2], bf[1][u & 3]);
-      if (u % 2 == 0) copy(s + 2, cb, true, u / 2);
-      if (u < 8) read(na, nb, 0, 0, u);
+    for (int u = 32; u < 64; ++u) {         // second half of sub-step 1
+      mfma(1, u);
+      if (u % 4 == 0) copy(s + 2, cb, true, (u - 32) / 4);
+      if (u % 2 == 0) read(na, nb, 0, 0, (u - 32) / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -274,13 +280,10 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 
 // ---------------------------------------------------------------- plain GEMM
 // The output is stored transposed, C[n * ldc + m]: lane l holds 4
-// consecutive m (registers 4q..4q+3) of column n, so every store (and every
-// load of the accumulate modes) is one 16-byte (fp32) or 8-byte (bf16)
-// vector.  M must be a multiple of 4.
-template <typename T> struct Vec4;
-template <> struct Vec4<float> { typedef f32x4_t type; };
-template <> struct Vec4<uint16_t> { typedef bf16x4_t type; };
-
+// consecutive m (registers 0..3) of column n, so every store (and every load
+// of the accumulate modes) is one 16-byte (fp32) or 8-byte (bf16) vector, and
+// the four lane groups of a column cover 16 consecutive m.  M must be a
+// multiple of 4.
 template <typename T>
 __device__ __forceinline__ f32x4_t load4(const T* p) {
   if constexpr (sizeof(T) == 4) {
@@ -317,42 +320,39 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   tile_coords(logical - split * per_split, tiles_m, tiles_n, g.group_m, tm, tn);
   const int kb = split * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
-  f32x16_t acc[4][kJ];
+  Acc acc;
   mainloop<T, kKTail>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
                       static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, kb, ke, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const int mb = tm * kTile + wm * 128 + 4 * (lane >> 5);
-  const int nb = tn * kTile + wn * kWaveN + (lane & 31);
+  const int mb = tm * kTile + wm * kWaveM + 4 * (lane >> 4);
+  const int nb = tn * kTile + wn * kWaveN + (lane & 15);
   const int64_t ldc = g.ldc;
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const int n = nb + 32 * j;
+    const int n = nb + kBlk * j;
     if (n >= g.N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = mb + 32 * i + 8 * q;
-        if (m >= g.M) continue;
-        const int64_t off = static_cast<int64_t>(n) * ldc + m;
-        f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                     acc[i][j][4 * q + 3]};
-        if constexpr (kMode == static_cast<int>(EpiMode::kStoreF32)) {
-          store4(static_cast<float*>(g.C) + split * g.split_stride + off, v);
-        } else if constexpr (kMode == static_cast<int>(EpiMode::kAccumF32)) {
-          float* c = static_cast<float*>(g.C) + off;
-          store4(c, load4(c) + v);
-        } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
-          store4(static_cast<T*>(g.C) + off, load4(static_cast<const float*>(g.Cin) + off) + v);
-        } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
-          store4(static_cast<T*>(g.C) + off, v);
-        } else {
-          T* c = static_cast<T*>(g.C) + off;
-          store4(c, load4(c) + v);
-        }
+    for (int i = 0; i < kI; ++i) {
+      const int m = mb + kBlk * i;
+      if (m >= g.M) continue;
+      const int64_t off = static_cast<int64_t>(n) * ldc + m;
+      const f32x4_t v = acc[i][j];
+      if constexpr (kMode == static_cast<int>(EpiMode::kStoreF32)) {
+        store4(static_cast<float*>(g.C) + split * g.split_stride + off, v);
+      } else if constexpr (kMode == static_cast<int>(EpiMode::kAccumF32)) {
+        float* c = static_cast<float*>(g.C) + off;
+        store4(c, load4(c) + v);
+      } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
+        store4(static_cast<T*>(g.C) + off, load4(static_cast<const float*>(g.Cin) + off) + v);
+      } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
+        store4(static_cast<T*>(g.C) + off, v);
+      } else {
+        T* c = static_cast<T*>(g.C) + off;
+        store4(c, load4(c) + v);
       }
+    }
   }
 }
 
@@ -371,21 +371,31 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   int tm, tn;
   tile_coords(logical, tiles_m, tiles_n, 4, tm, tn);
 
-  f32x16_t acc[4][kJ];
+  Acc acc;
   // M = classes (rows of W), N = chunk rows (rows of X), K = D.
   mainloop<T, kKTail>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V,
                       static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0, a.D, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const int frow = lane & 31, fhalf = lane >> 5;
-  const int vbase = tm * kTile + wm * 128;               // class of (i=0, r=0, half 0)
-  const int vlane = vbase + 4 * fhalf;                   // + 32 i + 8 (r >> 2) + (r & 3)
-  const int ncol = wn * kWaveN + frow;                   // + 32 j, within the tile
+  const int c16 = lane & 15, q = lane >> 4;
+  const int vbase = tm * kTile + wm * kWaveM;             // class of (i = 0, q = 0, r = 0)
+  const int vlane = vbase + 4 * q;                        // + 16 i + r
+  const int ncol = wn * kWaveN + c16;                     // + 16 j, within the tile
+  const int nbase = tn * kTile + ncol;                    // chunk row of block j = 0
   const T* bias = static_cast<const T*>(a.bias);
+  const bool v_tail = tm * kTile + kTile > a.V;           // uniform: classes past V in this tile
 
-  // The epilogue walks the four 32-column blocks j one at a time so that
-  // only 64 accumulators per lane are live in VGPRs.  Each block uses its own
+  // Targets of the lane's eight columns, fetched once (-1: none / past the chunk).
+  int tcol[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int n = nbase + kBlk * j;
+    tcol[j] = n < a.rows ? a.tc[n] : -1;
+  }
+
+  // The epilogue walks the eight 16-column blocks j one at a time so that
+  // only 32 accumulators per lane are live in VGPRs.  Each block uses its own
   // slots of the cross-wave exchange arrays.
   T* Tm = static_cast<T*>(a.T);
   __builtin_amdgcn_sched_barrier(0);
@@ -397,59 +407,68 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 #pragma unroll
     for (int jj = j + 1; jj < kJ; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][jj]));
-    const int nc = ncol + 32 * j;           // column inside the tile
-    const int n = tn * kTile + nc;          // chunk row
+      for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    const int nc = ncol + kBlk * j;         // column inside the tile
+    const int n = nbase + kBlk * j;         // chunk row
     const bool nin = n < a.rows;
 
-    // 1. bias, and -inf for classes beyond V.
+    // 1. bias, and -inf for classes beyond V (both uniform branches).
+    if (bias) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = vlane + 32 * i + 8 * (r >> 2) + (r & 3);
-        const bool in = v < a.V;
-        const float bb = (in && bias) ? to_f32(bias[v]) : 0.0f;
-        acc[i][j][r] = in ? acc[i][j][r] + bb : -INFINITY;
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int v = vlane + kBlk * i + r;
+          acc[i][j][r] += v < a.V ? to_f32(bias[v]) : 0.0f;
+        }
+    }
+    if (v_tail) {
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = vlane + kBlk * i + r < a.V ? acc[i][j][r] : -INFINITY;
+    }
 
-    // 2. target logit: the lane holding class tc[n] of column n writes zt[n].
-    if (nin) {
-      const int t = a.tc[n];
-      const int off = t - vbase;
-      if (t >= 0 && off >= 0 && off < 128 && ((off >> 2) & 1) == fhalf) {
-        const int want = ((off >> 5) << 4) | (((off >> 3) & 3) << 2) | (off & 3);
+    // 2. target logit: the lane holding class tcol[j] of column n writes zt[n].
+    {
+      const int off = tcol[j] - vbase;
+      if (tcol[j] >= 0 && off >= 0 && off < kWaveM && ((off >> 2) & 3) == q) {
+        const int want = ((off >> 4) << 2) | (off & 3);
         float val = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) val = (i * 16 + r == want) ? acc[i][j][r] : val;
+          for (int r = 0; r < 4; ++r) val = (i * 4 + r == want) ? acc[i][j][r] : val;
         a.zt[n] = val;
       }
     }
 
-    // 3. column max (and lowest class attaining it) over the tile's classes.
+    // 3. column max (and lowest class attaining it) over the tile's classes:
+    //    in-lane, then over the four lane groups of the column, then over the
+    //    two waves along M.
     float mx = -INFINITY;
     int mi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const float z = acc[i][j][r];
         if (z > mx) {
           mx = z;
-          if constexpr (kArgmax) mi = vlane + 32 * i + 8 * (r >> 2) + (r & 3);
+          if constexpr (kArgmax) mi = vlane + kBlk * i + r;
         }
       }
-    {
-      const float om = __shfl_xor(mx, 32);
-      const int oi = __shfl_xor(mi, 32);
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      const float om = __shfl_xor(mx, sh);
+      const int oi = __shfl_xor(mi, sh);
       if (om > mx || (om == mx && oi < mi)) {
         mx = om;
         mi = oi;
       }
     }
-    if (fhalf == 0) {
+    if (q == 0) {
       red_m[wm][nc] = mx;
       red_i[wm][nc] = mi;
     }
@@ -466,20 +485,21 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     // 4. e = exp(z - tile max) in place, column sums.
     float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4; ++r) {
         // (z - max) first: the maximum maps to exactly 1.
         const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - mx) * kLog2e);
         acc[i][j][r] = e;
         sum += e;
       }
+    sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
-    if (fhalf == 0) red_s[wm][nc] = sum;
+    if (q == 0) red_s[wm][nc] = sum;
     __syncthreads();
 
     // 5. per-(row, class tile) statistics.
-    if (wm == 0 && fhalf == 0 && nin) {
+    if (wm == 0 && q == 0 && nin) {
       const int64_t o = static_cast<int64_t>(tm) * a.ldp + n;
       a.m_part[o] = mx;
       a.s_part[o] = red_s[0][nc] + red_s[1][nc];
@@ -491,23 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
       if (nin) {
         T* row = Tm + static_cast<int64_t>(n) * a.ldt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v0 = vlane + 32 * i + 8 * q;
-            if constexpr (sizeof(T) == 2) {
-              bf16x4_t pk;
-              pk[0] = static_cast<__bf16>(acc[i][j][4 * q + 0]);
-              pk[1] = static_cast<__bf16>(acc[i][j][4 * q + 1]);
-              pk[2] = static_cast<__bf16>(acc[i][j][4 * q + 2]);
-              pk[3] = static_cast<__bf16>(acc[i][j][4 * q + 3]);
-              *reinterpret_cast<bf16x4_t*>(row + v0) = pk;
-            } else {
-              f32x4_t pk = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
-                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              *reinterpret_cast<f32x4_t*>(row + v0) = pk;
-            }
-          }
+        for (int i = 0; i < kI; ++i) store4(row + vlane + kBlk * i, acc[i][j]);
       }
     }
     // keep the blocks apart so only one block's values are live at a time
