@@ -35,7 +35,7 @@ struct lce_handle {
   int64_t n_chunks;
   int64_t c_pad;      // c rounded up to 64 (row stride of dLt, Xt and partials)
   int64_t V_pad;      // V rounded up to 256 (row stride of T, Wt)
-  int n_vt;           // 256-class tiles
+  int n_vt;           // statistics blocks of kStatCols classes
   int splits;         // split-K of the grad_X GEMM
   int k_split;
   int64_t grp;        // chunks per grad_W group (dL^T staged together)
@@ -111,7 +111,7 @@ void plan(lce_handle* h) {
   h->n_chunks = h->c ? cdiv64(d.N, h->c) : 0;
   h->c_pad = round_up(std::max<int64_t>(h->c, 1), 64);
   h->V_pad = round_up(d.V, lce::kTile);
-  h->n_vt = static_cast<int>(h->V_pad / lce::kTile);
+  h->n_vt = static_cast<int>(h->V_pad / lce::kStatCols);
   h->want_x = d.flags & LCE_GRAD_X;
   h->want_w = d.flags & LCE_GRAD_W;
   h->want_b = d.flags & LCE_GRAD_B;

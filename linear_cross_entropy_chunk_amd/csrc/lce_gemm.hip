@@ -357,15 +357,14 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
 }
 
 // ------------------------------------------------- logits + softmax stats
+// Each wave reduces its own 128 classes (kStatCols): the statistics block of
+// wave (wm) of tile tm is 2 tm + wm, so the epilogue needs no cross-wave
+// exchange and no barrier.
+static_assert(kWaveM == kStatCols, "one statistics block per wave");
+
 template <typename T, bool kStoreT, bool kArgmax, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
-  // cross-wave exchange of the epilogue, in the operand ring (free once the
-  // main loop has drained)
-  float (*red_m)[kTile] = reinterpret_cast<float (*)[kTile]>(lds);
-  int (*red_i)[kTile] = reinterpret_cast<int (*)[kTile]>(lds + 2 * kTile * 4);
-  float (*red_s)[kTile] = reinterpret_cast<float (*)[kTile]>(lds + 4 * kTile * 4);
-
   const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   int tm, tn;
@@ -381,10 +380,10 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   const int c16 = lane & 15, q = lane >> 4;
   const int vbase = tm * kTile + wm * kWaveM;             // class of (i = 0, q = 0, r = 0)
   const int vlane = vbase + 4 * q;                        // + 16 i + r
-  const int ncol = wn * kWaveN + c16;                     // + 16 j, within the tile
-  const int nbase = tn * kTile + ncol;                    // chunk row of block j = 0
+  const int nbase = tn * kTile + wn * kWaveN + c16;       // chunk row of block j = 0
+  const int64_t kblk = static_cast<int64_t>(vbase / kStatCols) * a.ldp;
   const T* bias = static_cast<const T*>(a.bias);
-  const bool v_tail = tm * kTile + kTile > a.V;           // uniform: classes past V in this tile
+  const bool v_tail = vbase + kWaveM > a.V;               // uniform: classes past V in this wave
 
   // Targets of the lane's eight columns, fetched once (-1: none / past the chunk).
   int tcol[kJ];
@@ -395,8 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   }
 
   // The epilogue walks the eight 16-column blocks j one at a time so that
-  // only 32 accumulators per lane are live in VGPRs.  Each block uses its own
-  // slots of the cross-wave exchange arrays.
+  // only 32 accumulators per lane are live in VGPRs.
   T* Tm = static_cast<T*>(a.T);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -408,7 +406,6 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     for (int jj = j + 1; jj < kJ; ++jj)
 #pragma unroll
       for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
-    const int nc = ncol + kBlk * j;         // column inside the tile
     const int n = nbase + kBlk * j;         // chunk row
     const bool nin = n < a.rows;
 
@@ -444,9 +441,8 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
       }
     }
 
-    // 3. column max (and lowest class attaining it) over the tile's classes:
-    //    in-lane, then over the four lane groups of the column, then over the
-    //    two waves along M.
+    // 3. column max (and lowest class attaining it) over the wave's 128
+    //    classes: in-lane, then over the four lane groups of the column.
     float mx = -INFINITY;
     int mi = 0x7fffffff;
 #pragma unroll
@@ -468,47 +464,32 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
         mi = oi;
       }
     }
-    if (q == 0) {
-      red_m[wm][nc] = mx;
-      red_i[wm][nc] = mi;
-    }
-    __syncthreads();
-    {
-      const float om = red_m[wm ^ 1][nc];
-      const int oi = red_i[wm ^ 1][nc];
-      if (om > mx || (om == mx && oi < mi)) {
-        mx = om;
-        mi = oi;
-      }
-    }
 
-    // 4. e = exp(z - tile max) in place, column sums.
+    // 4. e = exp(z - block max) in place, column sums.  A block wholly past
+    //    V (max -inf) stores e = 0 and sum 0.
+    const float ref = mx == -INFINITY ? 0.0f : mx;
     float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // (z - max) first: the maximum maps to exactly 1.
-        const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - mx) * kLog2e);
+        const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - ref) * kLog2e);
         acc[i][j][r] = e;
         sum += e;
       }
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
-    if (q == 0) red_s[wm][nc] = sum;
-    __syncthreads();
 
-    // 5. per-(row, class tile) statistics.
-    if (wm == 0 && q == 0 && nin) {
-      const int64_t o = static_cast<int64_t>(tm) * a.ldp + n;
-      a.m_part[o] = mx;
-      a.s_part[o] = red_s[0][nc] + red_s[1][nc];
-      if constexpr (kArgmax) a.i_part[o] = mi;
-    }
-
-    // 6. the exp tile T[n][v], 4 consecutive classes per store.
-    if constexpr (kStoreT) {
-      if (nin) {
+    if (nin) {
+      // 5. per-(row, statistics block) partials.
+      if (q == 0) {
+        a.m_part[kblk + n] = mx;
+        a.s_part[kblk + n] = sum;
+        if constexpr (kArgmax) a.i_part[kblk + n] = mi;
+      }
+      // 6. the exp tile T[n][v], 4 consecutive classes per store.
+      if constexpr (kStoreT) {
         T* row = Tm + static_cast<int64_t>(n) * a.ldt;
 #pragma unroll
         for (int i = 0; i < kI; ++i) store4(row + vlane + kBlk * i, acc[i][j]);

@@ -9,6 +9,9 @@ namespace lce {
 
 // Square output tile of every GEMM launch (rows x cols of C per workgroup).
 constexpr int kTile = 256;
+// Classes per softmax-statistics partial of the logits epilogue (one wave's
+// share of a tile's classes).
+constexpr int kStatCols = 128;
 // Rows per K4 finalize / transpose tile.
 constexpr int kSmallTile = 64;
 
@@ -42,11 +45,11 @@ hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
 
 // Logits GEMM with the fused softmax-statistics epilogue.  Computes, for the
 // chunk's rows n < rows and classes v < V, z[n, v] = X[n] . W[v] + b[v]; per
-// 256-class tile k it writes the tile max m_part[k][n], the tile sum of
-// exp(z - m_part) s_part[k][n], the lowest class index attaining the tile max
-// i_part[k][n] (if i_part != null), z[n, tc[n]] into zt[n] (tc[n] < 0: none),
-// and when T != null, T[n][v] = exp(z[n, v] - m_part[k][n]) rounded to the
-// element type, for v < V_pad (0 beyond V).
+// block k of kStatCols classes it writes the block max m_part[k][n], the block
+// sum of exp(z - m_part) s_part[k][n], the lowest class index attaining the
+// block max i_part[k][n] (if i_part != null), z[n, tc[n]] into zt[n]
+// (tc[n] < 0: none), and when T != null, T[n][v] = exp(z[n, v] - m_part[k][n])
+// rounded to the element type, for v < V_pad (0 beyond V).
 struct LogitsLse {
   const void* X; int64_t ldx;     // chunk rows [rows][D]
   const void* W; int64_t ldw;     // [V][D]
@@ -54,7 +57,7 @@ struct LogitsLse {
   const int* tc;                  // [rows]
   int rows, V, D;
   void* T; int64_t ldt;           // [rows_pad][V_pad] or null
-  float* m_part; float* s_part; int* i_part; int64_t ldp;   // [n_vt][ldp]
+  float* m_part; float* s_part; int* i_part; int64_t ldp;   // [V_pad / kStatCols][ldp]
   float* zt;                      // [rows]
 };
 hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s);
@@ -69,14 +72,14 @@ hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index,
                         int* tc, float* g, int64_t* counts, int64_t* n_valid_out,
                         int64_t* n_bad_out, hipStream_t s);
 
-// Row combine over the n_vt class tiles of a chunk: lse[n] (chunk-local),
+// Row combine over the n_vt statistics blocks of a chunk: lse[n] (chunk-local),
 // loss_rows[n] = lse - zt (0 if tc < 0), argmax_out[n] if non-null.
 hipError_t row_combine(const float* m_part, const float* s_part, const int* i_part,
                        int64_t ldp, int n_vt, const float* zt, const int* tc,
                        int rows, float* lse, float* loss_rows, int* argmax_out,
                        hipStream_t s);
 
-// In-place finalize: T[n][v] <- dL = g_n (T * exp(m_part[v/256][n] - lse_n)
+// In-place finalize: T[n][v] <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
 // - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V);
 // optionally writes dLt[v][n] (ld = ldlt) and per-64-row column partials
 // gb_part[n/64][v] (ld = V_pad).

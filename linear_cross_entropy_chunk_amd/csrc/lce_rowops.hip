@@ -98,26 +98,29 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 }
 
 // ------------------------------------------------------------ row combine
-// 32 rows x 8 parts per workgroup; part p folds class tiles p, p + 8, ...
-__global__ __launch_bounds__(256) void k_row_combine(
+// kCombRows rows x kCombParts parts per workgroup; part p folds statistics
+// blocks p, p + kCombParts, ... of its row (an online max / rescaled sum),
+// then part 0 merges the parts in a fixed order.
+constexpr int kCombRows = 8, kCombParts = 32;
+__global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     int rows, float* __restrict__ lse, float* __restrict__ loss_rows, int* __restrict__ amax) {
-  __shared__ float sm[8][32], ss[8][32];
-  __shared__ int sk[8][32];
-  const int r = threadIdx.x & 31, p = threadIdx.x >> 5;
-  const int n = blockIdx.x * 32 + r;
+  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
+  __shared__ int sk[kCombParts][kCombRows];
+  const int r = threadIdx.x % kCombRows, p = threadIdx.x / kCombRows;
+  const int n = blockIdx.x * kCombRows + r;
   float m = -INFINITY, s = 0.0f;
   int kb = 0x7fffffff;
   if (n < rows) {
-    for (int k = p; k < n_vt; k += 8) {
+    for (int k = p; k < n_vt; k += kCombParts) {
       const float mk = mp[k * ldp + n];
       const float sk_ = sp[k * ldp + n];
       if (mk > m) {
         s = s * expf(m - mk) + sk_;
         m = mk;
         kb = k;
-      } else {
+      } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
         s += sk_ * expf(mk - m);
       }
     }
@@ -128,24 +131,24 @@ __global__ __launch_bounds__(256) void k_row_combine(
   __syncthreads();
   if (p == 0 && n < rows) {
     float M = sm[0][r];
-    for (int q = 1; q < 8; ++q) M = fmaxf(M, sm[q][r]);
+    for (int q = 1; q < kCombParts; ++q) M = fmaxf(M, sm[q][r]);
     float S = 0.0f;
     int K = 0x7fffffff;
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kCombParts; ++q) {
       if (sm[q][r] > -INFINITY) S += ss[q][r] * expf(sm[q][r] - M);
       if (sm[q][r] == M && sk[q][r] < K) K = sk[q][r];
     }
     const float L = M + logf(S);
     lse[n] = L;
     loss_rows[n] = tc[n] >= 0 ? L - zt[n] : 0.0f;
-    // K stays unset only if every tile maximum is NaN; read tile 0 then.
+    // K stays unset only if every block maximum is NaN; read block 0 then.
     if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
   }
 }
 
 // ------------------------------------------------------- in-place finalize
-// 64 rows x 64 classes per workgroup; the 64 classes sit in one 256-class
-// statistics tile.  Writes dL over T, dL^T into dLt, and column partials.
+// 64 rows x 64 classes per workgroup; the 64 classes sit in one statistics
+// block of kStatCols classes.  Writes dL over T, dL^T into dLt, and column partials.
 template <typename T>
 __global__ __launch_bounds__(256) void k_finalize(
     T* __restrict__ Tm, int64_t ldt, T* __restrict__ dLt, int64_t ldlt,
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void k_finalize(
   __shared__ float sc[64], gg[64];
   __shared__ int tt[64];
   const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  const int k = v0 >> 8;
+  const int k = v0 / kStatCols;
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int n = n0 + tid;
@@ -532,7 +535,7 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
                        int n_vt, const float* zt, const int* tc, int rows, float* lse,
                        float* loss_rows, int* argmax_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine<<<cdiv_u(rows, 32), 256, 0, s>>>(m_part, s_part, i_part, ldp, n_vt, zt, tc, rows,
+  k_row_combine<<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(m_part, s_part, i_part, ldp, n_vt, zt, tc, rows,
                                                  lse, loss_rows, argmax_out);
   return hipGetLastError();
 }
