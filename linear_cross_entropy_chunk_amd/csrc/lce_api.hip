@@ -147,7 +147,8 @@ void plan(lce_handle* h) {
   };
   h->o_T = take(c * Vp * es, h->want_any);
   h->o_dLt = take(Vp * h->k_grp * es, h->want_w);
-  h->o_Wt = take(D * Vp * es, h->want_x);
+  // bf16 grad_X reads W in place (k-major operand); fp32 uses a transposed copy
+  h->o_Wt = take(D * Vp * es, h->want_x && !h->bf16);
   h->o_Xt = take(D * h->k_grp * es, h->want_w);
   h->o_mp = take(h->n_vt * c * 4, true);
   h->o_sp = take(h->n_vt * c * 4, true);
@@ -333,7 +334,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     return LCE_OK;
   }
 
-  if (want_x) LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
+  if (want_x && !bf16)
+    LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
 
   const char* Xb = static_cast<const char*>(io->X);
   for (int64_t ck = 0; ck < h->n_chunks; ++ck) {
@@ -365,10 +367,16 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                                   h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
                                   V, static_cast<int>(Vp), want_b ? gbp : nullptr, s));
     if (want_x) {
-      // grad_X[rows] = dL . W, as (W^T)[D][V] against dL[rows][V]: the
-      // transposed store writes grad_X rows with contiguous vectors.
+      // grad_X[rows] = dL . W, with M = D against dL[rows][V] (K = V): the
+      // transposed store writes grad_X rows with contiguous vectors.  bf16
+      // reads W[V][D] itself as a k-major operand (rows past V read as 0);
+      // fp32 reads the transposed copy W^T[D][V_pad].
       lce::GemmNT gx{};
-      gx.A = Wt; gx.lda = Vp;
+      if (bf16) {
+        gx.A = io->W; gx.lda = D; gx.a_kmajor = true; gx.a_krows = V;
+      } else {
+        gx.A = Wt; gx.lda = Vp;
+      }
       gx.B = T; gx.ldb = Vp;
       gx.M = D; gx.N = rows; gx.K = static_cast<int>(Vp);
       gx.splits = h->splits; gx.k_split = h->k_split;

@@ -139,11 +139,38 @@ using dev::lds_addr;
 using dev::waitcnt_vm;
 constexpr int kWaitVm0 = waitcnt_vm(0);
 
+// A k-major operand (stored [K][ld], its M or N index contiguous, bf16)
+// keeps a stage in a slot as 64 k-rows of 512 bytes (256 columns); the
+// 16-byte chunk c of k-row r sits at physical chunk c ^ trswz(r).  Fragments
+// come from ds_read_b64_tr_b16: within each group of 16 lanes, source lane s
+// supplies 4 consecutive columns of one k-row and output lane l receives
+// column l & 3 of source lanes 4e + l / 4 (e = 0..3), i.e. four consecutive k
+// of one column -- two such reads give the 16x16x32 operand of a lane
+// (column l & 15, k = 8 (l >> 4) .. + 7).  A 16-lane group reads 32 bytes from
+// each of four consecutive k-rows and two groups go per cycle; trswz spreads
+// those eight 32-byte pieces over all 64 banks.
+__device__ __forceinline__ int trswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  lds_char_t* base = reinterpret_cast<lds_char_t*>(static_cast<uintptr_t>(dev::lds_addr(lds_p)));
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(base));
+  const i16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(base + 4 * 512));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(i32x4_t, v);
+}
+
 // C tile [m0, m0+256) x [n0, n0+256) = A[m0.., k_begin..k_end) . B[n0.., ...]^T
 //
 // Rows past M (N) read as zero (each copy's descriptor covers only the
-// tile's existing rows).  With kKTail, 16-byte chunks at or past k_end read
-// as zero too (their offsets are sent out of range).
+// tile's existing rows); so do k-rows of a k-major operand past its valid
+// rows.  With kKTail, 16-byte chunks at or past k_end read as zero too
+// (their offsets are sent out of range; K-contiguous operands only).
 //
 // Per stage s (two sub-steps of 4 chunks, 64 MFMAs per wave each), every wave:
 //   sub-step 0 and the first half of sub-step 1: MFMAs from registers; the
@@ -155,12 +182,16 @@ constexpr int kWaitVm0 = waitcnt_vm(0);
 //     stage s + 1; 8 copies of B of stage s + 2 into slot 2s mod 5.
 // A stage's B thus has three quarters of a stage to land and its A about
 // seven quarters.
-template <typename T, bool kKTail>
+template <typename T, bool kKTail, bool kATr, bool kBTr>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
+                                         int a_krows,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
+                                         int b_krows,
                                          int k_begin, int k_end, char* __restrict__ lds,
                                          Acc& acc) {
   static_assert(kI == 8 && kJ == 8 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
+  static_assert(!(kATr || kBTr) || sizeof(T) == 2, "k-major operands are bf16 only");
+  static_assert(!(kKTail && (kATr || kBTr)), "k tails apply to K-contiguous operands");
   constexpr int kEs = static_cast<int>(sizeof(T));
   constexpr int kBK = kRowBytes / kEs;            // K elements per stage
   constexpr int kVec = 16 / kEs;                  // elements per 16-byte chunk
@@ -175,52 +206,100 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   if (nk <= 0) return;
 
+  // K-contiguous operand: one descriptor over the tile's rows.  Copy j of a
+  // wave covers rows 8 (kCopies wave + j) .. + 8; lane i takes row + i / 8,
+  // physical chunk i & 7.  The stage's K offset travels in the instruction's
+  // scalar offset.
+  // k-major operand: copy j covers k-rows 2 (kCopies wave + j) .. + 2 of the
+  // stage; lane i takes k-row + i / 32, physical chunk i & 31.  The
+  // descriptor is rebased on the stage's first k-row.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + static_cast<int64_t>(m0) * lda,
                                               static_cast<int64_t>(min(M - m0, kTile)) * lda * kEs);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<int64_t>(n0) * ldb,
                                               static_cast<int64_t>(min(N - n0, kTile)) * ldb * kEs);
-  // Copy j of a wave covers rows 8 (kCopies wave + j) .. + 8; lane i takes
-  // row + i / 8, physical chunk i & 7.  The stage's K offset travels in the
-  // instruction's scalar offset.
-  const int crow = lane >> 3, pchunk = lane & 7;
+  auto lane_off = [&](bool tr, int64_t ld, int j) {
+    if (tr) {
+      const int r = 2 * (kCopies * wave + j) + (lane >> 5);
+      return (r * static_cast<int>(ld) + (((lane & 31) ^ trswz(r)) << 3)) * kEs;
+    }
+    const int row = 8 * (kCopies * wave + j) + (lane >> 3);
+    return (row * static_cast<int>(ld) + (((lane & 7) ^ swz(row)) * kVec)) * kEs;
+  };
   int va[kCopies], vb[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
-    const int row = 8 * (kCopies * wave + j) + crow;
-    const int lchunk = pchunk ^ swz(row);
-    va[j] = (row * static_cast<int>(lda) + lchunk * kVec) * kEs;
-    vb[j] = (row * static_cast<int>(ldb) + lchunk * kVec) * kEs;
+    va[j] = lane_off(kATr, lda, j);
+    vb[j] = lane_off(kBTr, ldb, j);
   }
   auto copy = [&](int st, int slot, bool opb, int j) {
     const int k0 = k_begin + min(st, nk - 1) * kBK;   // stages past the end repeat the last
-    int o = opb ? vb[j] : va[j];
-    if constexpr (kKTail) {
-      const int row = 8 * (kCopies * wave + j) + crow;
-      o = (k0 + (pchunk ^ swz(row)) * kVec) < k_end ? o : kOutOfRange;
+    const uint32_t dst = lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024);
+    const bool tr = opb ? kBTr : kATr;
+    if (tr) {
+      const T* base = opb ? B + n0 : A + m0;
+      const int64_t ld = opb ? ldb : lda;
+      const int krows = opb ? b_krows : a_krows;
+      const int64_t left = (static_cast<int64_t>(max(krows - k0, 0)) * ld - (opb ? n0 : m0)) * kEs;
+      // the descriptor must live in SGPRs: make its fields visibly uniform
+      const uint64_t addr = reinterpret_cast<uint64_t>(base + static_cast<int64_t>(k0) * ld);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+      const int64_t bytes = max<int64_t>(left, 0);
+      const int range = __builtin_amdgcn_readfirstlane(
+          bytes > 0x7ffff000LL * 2 ? -1 : static_cast<int>(static_cast<uint32_t>(bytes)));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, range, 0x00020000);
+      copy16_to_lds(rs, opb ? vb[j] : va[j], dst);
+    } else {
+      int o = opb ? vb[j] : va[j];
+      if constexpr (kKTail) {
+        const int row = 8 * (kCopies * wave + j) + (lane >> 3);
+        o = (k0 + ((lane & 7) ^ swz(row)) * kVec) < k_end ? o : kOutOfRange;
+      }
+      copy16_to_lds(opb ? rb : ra, o, dst, __builtin_amdgcn_readfirstlane(k0 * kEs));
     }
-    copy16_to_lds(opb ? rb : ra, o, lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024),
-                  __builtin_amdgcn_readfirstlane(k0 * kEs));
   };
 
-  // Fragment reads: lane l reads row (l & 15) of each 16-row block at logical
-  // chunk 4 h + (l >> 4) of sub-step h.  Rows 16 x + (l & 15) share the
-  // swizzle of (l & 15).  Read r (0..15) of a sub-step: A block r / 2 if r is
-  // even, else B block r / 2.
+  // Fragment reads of a K-contiguous operand: lane l reads row (l & 15) of
+  // each 16-row block at logical chunk 4 h + (l >> 4) of sub-step h.  Rows
+  // 16 x + (l & 15) share the swizzle of (l & 15).
+  // Fragment reads of a k-major operand: see trswz; lane l (group g = l / 16,
+  // s = l & 15) reads k-rows 32 h + 8 g + 4 rd + s / 4 (rd = 0, 1) at columns
+  // 16 x + 4 (s & 3) .. + 3 of its wave's 128.
+  // Read r (0..15) of a sub-step: A block r / 2 if r is even, else B block r / 2.
   const int frow = lane & 15, fq = lane >> 4, fsw = swz(frow);
-  const int a_row = (wm * kWaveM + frow) * kRowBytes;
-  const int b_row = (wn * kWaveN + frow) * kRowBytes;
   int coff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) coff[h] = ((4 * h + fq) ^ fsw) << 4;
+  auto tr_off = [&](int wpos, int x) {   // byte offset of block x, sub-step 0, rd 0
+    const int s4 = lane & 15;
+    const int krow = 8 * fq + (s4 >> 2);
+    const int lc = 16 * wpos + 2 * x + ((s4 & 3) >> 1);
+    return krow * 512 + ((lc ^ trswz(krow)) << 4) + (s4 & 1) * 8;
+  };
+  int ta[kATr ? kI : 1], tb[kBTr ? kJ : 1];
+#pragma unroll
+  for (int x = 0; x < (kATr ? kI : 1); ++x) ta[x] = kATr ? tr_off(wm, x) : 0;
+#pragma unroll
+  for (int x = 0; x < (kBTr ? kJ : 1); ++x) tb[x] = kBTr ? tr_off(wn, x) : 0;
+  const int a_row = (wm * kWaveM + frow) * kRowBytes;
+  const int b_row = (wn * kWaveN + frow) * kRowBytes;
   i32x4_t af[2][kI], bf[2][kJ];
   auto read = [&](int sa, int sb, int h, int set, int r) {
     const int x = r >> 1;
-    if (r & 1)
-      bf[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sb * kSlotBytes + b_row + coff[h] +
-                                                     x * kBlk * kRowBytes);
-    else
-      af[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sa * kSlotBytes + a_row + coff[h] +
-                                                     x * kBlk * kRowBytes);
+    if (r & 1) {
+      if constexpr (kBTr)
+        bf[set][x] = read_tr_pair(lds + sb * kSlotBytes + tb[x] + h * 32 * 512);
+      else
+        bf[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sb * kSlotBytes + b_row + coff[h] +
+                                                       x * kBlk * kRowBytes);
+    } else {
+      if constexpr (kATr)
+        af[set][x] = read_tr_pair(lds + sa * kSlotBytes + ta[x] + h * 32 * 512);
+      else
+        af[set][x] = *reinterpret_cast<const i32x4_t*>(lds + sa * kSlotBytes + a_row + coff[h] +
+                                                       x * kBlk * kRowBytes);
+    }
   };
   auto mfma = [&](int set, int u) {     // u = 8 i + j
     mfma_step<T>(acc[u >> 3][u & 7], af[set][u >> 3], bf[set][u & 7]);
@@ -309,7 +388,7 @@ __device__ __forceinline__ void store4(T* p, f32x4_t v) {
   }
 }
 
-template <typename T, int kMode, bool kKTail>
+template <typename T, int kMode, bool kATr, bool kBTr>
 __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   const int tiles_m = cdiv(g.M, kTile), tiles_n = cdiv(g.N, kTile);
@@ -321,8 +400,9 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   const int kb = split * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   Acc acc;
-  mainloop<T, kKTail>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
-                      static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, kb, ke, lds, acc);
+  mainloop<T, false, kATr, kBTr>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M, g.a_krows,
+                                 static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, g.b_krows,
+                                 kb, ke, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -372,8 +452,9 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 
   Acc acc;
   // M = classes (rows of W), N = chunk rows (rows of X), K = D.
-  mainloop<T, kKTail>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V,
-                      static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0, a.D, lds, acc);
+  mainloop<T, kKTail, false, false>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V, 0,
+                                    static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0,
+                                    0, a.D, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -501,13 +582,31 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 }
 
 // Two entry points with the same body so profiles tell the products apart.
-template <typename T, int kMode>
+template <typename T, int kMode, bool kATr, bool kBTr>
 __global__ __launch_bounds__(kThreads) void k_gemm_grad_x(GemmNT g) {
-  gemm_nt_tile<T, kMode, false>(g);
+  gemm_nt_tile<T, kMode, kATr, kBTr>(g);
 }
-template <typename T, int kMode>
+template <typename T, int kMode, bool kATr, bool kBTr>
 __global__ __launch_bounds__(kThreads) void k_gemm_grad_w(GemmNT g) {
-  gemm_nt_tile<T, kMode, false>(g);
+  gemm_nt_tile<T, kMode, kATr, kBTr>(g);
+}
+
+template <typename T, bool kATr, bool kBTr>
+void launch_gemm_l(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
+  const bool wgrad = g.role == GemmRole::kGradW;
+#define LCE_GEMM_CASE(mode)                                                                    \
+  case EpiMode::mode:                                                                          \
+    if (wgrad) k_gemm_grad_w<T, static_cast<int>(EpiMode::mode), kATr, kBTr><<<grid, block, 0, s>>>(g); \
+    else k_gemm_grad_x<T, static_cast<int>(EpiMode::mode), kATr, kBTr><<<grid, block, 0, s>>>(g);       \
+    break;
+  switch (g.mode) {
+    LCE_GEMM_CASE(kStoreF32)
+    LCE_GEMM_CASE(kAccumF32)
+    LCE_GEMM_CASE(kFinalOut)
+    LCE_GEMM_CASE(kStoreOut)
+    LCE_GEMM_CASE(kAccumOut)
+  }
+#undef LCE_GEMM_CASE
 }
 
 template <typename T>
@@ -518,20 +617,15 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   // Every split range and K must be whole stages on this path.
   if (g.K % kBK != 0 || g.k_split % kBK != 0) return hipErrorInvalidValue;
-  const bool wgrad = g.role == GemmRole::kGradW;
-#define LCE_GEMM_CASE(mode)                                                   \
-  case EpiMode::mode:                                                         \
-    if (wgrad) k_gemm_grad_w<T, static_cast<int>(EpiMode::mode)><<<grid, block, 0, s>>>(g); \
-    else k_gemm_grad_x<T, static_cast<int>(EpiMode::mode)><<<grid, block, 0, s>>>(g);       \
-    break;
-  switch (g.mode) {
-    LCE_GEMM_CASE(kStoreF32)
-    LCE_GEMM_CASE(kAccumF32)
-    LCE_GEMM_CASE(kFinalOut)
-    LCE_GEMM_CASE(kStoreOut)
-    LCE_GEMM_CASE(kAccumOut)
+  if constexpr (sizeof(T) == 2) {
+    if (g.a_kmajor && g.b_kmajor) launch_gemm_l<T, true, true>(g, grid, block, s);
+    else if (g.a_kmajor) launch_gemm_l<T, true, false>(g, grid, block, s);
+    else if (g.b_kmajor) return hipErrorInvalidValue;
+    else launch_gemm_l<T, false, false>(g, grid, block, s);
+  } else {
+    if (g.a_kmajor || g.b_kmajor) return hipErrorInvalidValue;
+    launch_gemm_l<T, false, false>(g, grid, block, s);
   }
-#undef LCE_GEMM_CASE
   return hipGetLastError();
 }
 

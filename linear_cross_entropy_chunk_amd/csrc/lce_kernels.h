@@ -24,10 +24,12 @@ enum class EpiMode : int {
 };
 
 // ---- GEMM (lce_gemm.hip) -------------------------------------------------
-// P[m, n] = sum_k A[m, k] * B[n, k]; A is [M][lda], B is [N][ldb], both with
-// K contiguous ("NT").  The result is stored transposed, C[n * ldc + m]
-// (M a multiple of 4).  K is split into `splits` ranges of k_split elements
-// (a multiple of the stage depth); split s writes C + s * split_stride.
+// P[m, n] = sum_k A(m, k) B(n, k).  A is stored either [M][lda] with K
+// contiguous, or k-major [K][lda] with M contiguous (a_kmajor, bf16 only);
+// B likewise with N.  Rows of a k-major operand at or past a_krows (b_krows)
+// read as zero.  The result is stored transposed, C[n * ldc + m] (M a
+// multiple of 4).  K is split into `splits` ranges of k_split elements (a
+// multiple of the stage depth); split s writes C + s * split_stride.
 enum class GemmRole : int { kGradX = 0, kGradW = 1 };   // names the kernel in profiles
 
 struct GemmNT {
@@ -40,6 +42,8 @@ struct GemmNT {
   EpiMode mode;
   int group_m;                    // tile-order grouping along M
   GemmRole role;
+  bool a_kmajor, b_kmajor;        // operand layouts (see above)
+  int a_krows, b_krows;           // valid k rows of a k-major operand
 };
 hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
 
