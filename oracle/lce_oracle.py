@@ -66,23 +66,35 @@ def corrected_targets(t: np.ndarray, valid: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Step 2: per-row weights.  [LCE] ``_ChunkContext.neg_weight_target``: the
-# unmasked rows get weight 1 (no class weights); "mean" divides by
-# d = sum of unmasked weights and uses NaN as the divisor when d == 0, "sum"
-# negates, and the reduction='none' backward folds the per-row upstream
-# gradient in.  g below is the negation of that tensor, so dL = g (P - Y).
+# Step 2: per-row weights.  [LCE] ``_ChunkContext.neg_weight_target``: an
+# unmasked row weighs weight[target] with per-class weights (1 without them),
+# a masked row 0; "mean" divides by d = sum of the unmasked row weights and
+# uses NaN as the divisor when d == 0, "sum" negates, and the reduction='none'
+# backward folds the per-row upstream gradient in.  g below is the negation of
+# that tensor, so dL = g (P - Y).
 # --------------------------------------------------------------------------
-def row_weights(valid: np.ndarray, reduction: str, grad_scale: float = 1.0,
-                upstream: np.ndarray | None = None) -> np.ndarray:
-    """g[N] in float64.
+def class_row_weights(valid: np.ndarray, tc: np.ndarray,
+                      class_weight: np.ndarray | None = None) -> np.ndarray:
+    """w[N] in float64: class_weight[t_n] (1 without class weights) on valid
+    rows, 0 elsewhere."""
+    if class_weight is None:
+        return valid.astype(np.float64)
+    cw = np.asarray(class_weight, np.float64)
+    return np.where(valid, cw[tc], 0.0)
 
-    mean: grad_scale / n_valid on valid rows, 0 elsewhere; NaN on every row
-          when n_valid == 0 (the pages divide by NaN there).
-    sum:  grad_scale on valid rows.
-    none: upstream[n] on valid rows (the backward of the per-row loss)."""
+
+def row_weights(valid: np.ndarray, reduction: str, grad_scale: float = 1.0,
+                upstream: np.ndarray | None = None, *, tc: np.ndarray | None = None,
+                class_weight: np.ndarray | None = None) -> np.ndarray:
+    """g[N] in float64, with w = class_row_weights(valid, tc, class_weight):
+
+    mean: grad_scale * w / sum(w); NaN on every row when sum(w) == 0 (the
+          pages divide by NaN there).
+    sum:  grad_scale * w.
+    none: upstream[n] * w (the backward of the per-row loss)."""
     if reduction not in REDUCTIONS:
         raise ValueError(reduction)
-    w = valid.astype(np.float64)
+    w = class_row_weights(valid, tc, class_weight)
     if reduction == "mean":
         d = w.sum()
         return w * grad_scale / (d if d != 0 else np.nan)
@@ -123,22 +135,25 @@ def logsumexp_rows(z: np.ndarray) -> np.ndarray:
 # accumulate the same terms ("output +=" / "output -=").
 # --------------------------------------------------------------------------
 def row_losses(z: np.ndarray, lse: np.ndarray, tc: np.ndarray,
-               valid: np.ndarray) -> np.ndarray:
+               valid: np.ndarray, w: np.ndarray | None = None) -> np.ndarray:
+    """w[n] (lse_n - z[n, t_n]) on valid rows, 0 elsewhere; w = 1 when None."""
     n = np.arange(z.shape[0])
     zt = z[n, tc] if z.shape[0] else np.zeros(0)
-    return np.where(valid, lse - zt, 0.0)
+    loss = np.where(valid, lse - zt, 0.0)
+    return loss if w is None else w * loss
 
 
-def reduce_loss(loss_rows: np.ndarray, n_valid: int, reduction: str):
-    """mean: sum / n_valid (NaN when n_valid == 0, including N == 0, as the
-    pages fill the output with NaN for an empty mean); sum: the sum; none:
-    the per-row vector."""
+def reduce_loss(loss_rows: np.ndarray, denom, reduction: str):
+    """mean: sum / denom, denom the sum of the unmasked row weights (the
+    count n_valid without class weights); NaN when denom == 0, including
+    N == 0, as the pages fill the output with NaN for an empty mean.  sum:
+    the sum; none: the per-row vector."""
     if reduction == "none":
         return loss_rows
     s = float(np.sum(loss_rows))
     if reduction == "sum":
         return s
-    return s / n_valid if n_valid else float("nan")
+    return s / denom if denom else float("nan")
 
 
 # --------------------------------------------------------------------------
@@ -178,49 +193,54 @@ def argmax_rows(z: np.ndarray) -> np.ndarray:
 
 def linear_cross_entropy(X, W, b, t, *, ignore_index: int = -100,
                          reduction: str = "mean", grad_scale: float = 1.0,
-                         upstream=None) -> dict:
+                         upstream=None, class_weight=None) -> dict:
     """The whole method on full arrays, unchunked.
 
     Returns loss (float for mean/sum, float64[N] for none), loss_rows,
-    grad_X, grad_W, grad_b, lse, argmax, n_valid, n_bad and g.
+    grad_X, grad_W, grad_b, lse, argmax, n_valid, n_bad, g and w (the
+    per-row class weights).
 
     For reduction='none' with ``upstream`` given, the gradients are the
     backward of sum_n upstream[n] * loss_n ([LCE] reduction='none' backward,
     which recomputes the chunk loop with the upstream gradient folded into
     the row weights); with ``upstream`` None they are the gradients of
-    sum_n loss_n."""
+    sum_n loss_n.  ``class_weight`` ([V]) weighs each row by the weight of
+    its target class, in the loss and in its denominator for mean."""
     X = np.asarray(X)
     W = np.asarray(W)
     V = W.shape[0]
     valid, bad, n_valid, n_bad = target_masks(t, V, ignore_index)
     tc = corrected_targets(t, valid)
+    w = class_row_weights(valid, tc, class_weight)
     z = logits(X, W, b)
     lse = logsumexp_rows(z)
-    loss_rows = row_losses(z, lse, tc, valid)
-    loss = reduce_loss(loss_rows, n_valid, reduction)
-    g = row_weights(valid, reduction, grad_scale, upstream)
+    loss_rows = row_losses(z, lse, tc, valid, w)
+    loss = reduce_loss(loss_rows, w.sum(), reduction)
+    g = row_weights(valid, reduction, grad_scale, upstream, tc=tc, class_weight=class_weight)
     dL = dlogits(z, lse, tc, g)
     gX, gW, gb = linear_grads(dL, X, W)
     return {"loss": loss, "loss_rows": loss_rows, "grad_X": gX,
             "grad_W": gW, "grad_b": gb, "lse": lse, "argmax": argmax_rows(z),
-            "n_valid": n_valid, "n_bad": n_bad, "g": g, "dL": dL}
+            "n_valid": n_valid, "n_bad": n_bad, "g": g, "w": w, "dL": dL}
 
 
 def softmax_cross_entropy(z, t, *, ignore_index: int = -100,
-                          reduction: str = "mean", grad_scale: float = 1.0):
+                          reduction: str = "mean", grad_scale: float = 1.0,
+                          class_weight=None):
     """Standalone CE on given logits ([LIG]): returns (loss, dL) where dL is
     what the in-place kernel writes over the logits buffer: the gradient of
     grad_scale * loss for mean / sum, of sum_n grad_scale * loss_n for none."""
     z = np.asarray(z, np.float64)
     V = z.shape[1]
-    valid, _, n_valid, _ = target_masks(t, V, ignore_index)
+    valid, _, _, _ = target_masks(t, V, ignore_index)
     tc = corrected_targets(t, valid)
+    w = class_row_weights(valid, tc, class_weight)
     lse = logsumexp_rows(z)
-    loss = reduce_loss(row_losses(z, lse, tc, valid), n_valid, reduction)
+    loss = reduce_loss(row_losses(z, lse, tc, valid, w), w.sum(), reduction)
     # 'none': the gradient of sum_n grad_scale * loss_n (the same upstream
     # value on every row).
     up = np.full(z.shape[0], grad_scale) if reduction == "none" else None
-    g = row_weights(valid, reduction, grad_scale, up)
+    g = row_weights(valid, reduction, grad_scale, up, tc=tc, class_weight=class_weight)
     return loss, dlogits(z, lse, tc, g)
 
 

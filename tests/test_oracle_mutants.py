@@ -31,6 +31,23 @@ def _pin_torch(reduction="mean", ignore_index=-100):
             and np.allclose(r["grad_b"], b.grad.numpy(), rtol=1e-10, atol=1e-14))
 
 
+def _pin_torch_class_weight(reduction="mean"):
+    """Per-class weights against torch's cross_entropy(weight=...)."""
+    c = small_case(13, 5, 9, seed=26, ignore_frac=0.25)
+    cw = np.random.default_rng(27).uniform(0.2, 3.0, 9)
+    X = torch.tensor(c["X"], dtype=torch.float64, requires_grad=True)
+    W = torch.tensor(c["W"], dtype=torch.float64, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(X @ W.T, torch.tensor(c["t"]),
+                                             weight=torch.tensor(cw), reduction=reduction)
+    u = torch.tensor(c["u"], dtype=torch.float64)
+    (loss * u).sum().backward() if reduction == "none" else loss.backward()
+    r = oracle.linear_cross_entropy(c["X"], c["W"], None, c["t"], reduction=reduction,
+                                    upstream=c["u"], class_weight=cw)
+    return (np.allclose(r["loss"], loss.detach().numpy(), rtol=1e-12)
+            and np.allclose(r["grad_X"], X.grad.numpy(), rtol=1e-10, atol=1e-14)
+            and np.allclose(r["grad_W"], W.grad.numpy(), rtol=1e-10, atol=1e-14))
+
+
 def _pin_zero_weight():
     c = small_case(10, 4, 7, seed=22, ignore_frac=0.2, bias=False)
     r = oracle.linear_cross_entropy(c["X"], np.zeros((7, 4)), None, c["t"])
@@ -64,6 +81,7 @@ def _pin_bad_targets():
 def _all_pins():
     return (all(_pin_torch(red, ii) for red in ("mean", "sum", "none")
                 for ii in (-100, 2))
+            and all(_pin_torch_class_weight(red) for red in ("mean", "sum", "none"))
             and _pin_zero_weight() and _pin_all_ignored() and _pin_argmax()
             and _pin_bad_targets())
 
@@ -102,15 +120,28 @@ def _m_lse_no_shift_back(z):
     return np.log(np.exp(z - m[:, None]).sum(axis=1))
 
 
-def _m_mean_over_N(valid, reduction, grad_scale=1.0, upstream=None):
+def _m_mean_over_N(valid, reduction, grad_scale=1.0, upstream=None, **kw):
     if reduction == "mean":
-        return valid.astype(np.float64) * grad_scale / len(valid)
-    return _ORIG["row_weights"](valid, reduction, grad_scale, upstream)
+        w = lo.class_row_weights(valid, kw.get("tc"), kw.get("class_weight"))
+        return w * grad_scale / len(valid)
+    return _ORIG["row_weights"](valid, reduction, grad_scale, upstream, **kw)
 
 
-def _m_ignore_weights(valid, reduction, grad_scale=1.0, upstream=None):
-    w = _ORIG["row_weights"](np.ones_like(valid), reduction, grad_scale, upstream)
-    return w
+def _m_ignore_weights(valid, reduction, grad_scale=1.0, upstream=None, **kw):
+    return _ORIG["row_weights"](np.ones_like(valid), reduction, grad_scale, upstream, **kw)
+
+
+def _m_mean_over_count(valid, reduction, grad_scale=1.0, upstream=None, **kw):
+    """Class weights in the numerator, the row count as the denominator."""
+    if reduction == "mean":
+        w = lo.class_row_weights(valid, kw.get("tc"), kw.get("class_weight"))
+        return w * grad_scale / valid.sum()
+    return _ORIG["row_weights"](valid, reduction, grad_scale, upstream, **kw)
+
+
+def _m_class_weight_dropped(valid, reduction, grad_scale=1.0, upstream=None, **kw):
+    kw = dict(kw, class_weight=None)
+    return _ORIG["row_weights"](valid, reduction, grad_scale, upstream, **kw)
 
 
 def _m_mask_after_correction(t, V, ignore_index):
@@ -129,9 +160,14 @@ def _m_argmax_last(z):
     return (z.shape[1] - 1 - z[:, ::-1].argmax(axis=1)).astype(np.int64)
 
 
-def _m_loss_target_index_off_by_one(z, lse, tc, valid):
+def _m_loss_target_index_off_by_one(z, lse, tc, valid, w=None):
     n = np.arange(z.shape[0])
-    return np.where(valid, lse - z[n, np.minimum(tc + 1, z.shape[1] - 1)], 0.0)
+    loss = np.where(valid, lse - z[n, np.minimum(tc + 1, z.shape[1] - 1)], 0.0)
+    return loss if w is None else w * loss
+
+
+def _m_loss_unweighted(z, lse, tc, valid, w=None):
+    return _ORIG["row_losses"](z, lse, tc, valid)
 
 
 _ORIG = {k: getattr(lo, k) for k in ("dlogits", "linear_grads", "logsumexp_rows",
@@ -151,6 +187,9 @@ MUTANTS = [
     ("logits", _m_bias_dropped),
     ("argmax_rows", _m_argmax_last),
     ("row_losses", _m_loss_target_index_off_by_one),
+    ("row_weights", _m_mean_over_count),
+    ("row_weights", _m_class_weight_dropped),
+    ("row_losses", _m_loss_unweighted),
 ]
 
 
@@ -160,6 +199,6 @@ def test_pins_reject_mutant(monkeypatch, name, mutant):
     with np.errstate(all="ignore"):
         try:
             ok = _all_pins()
-        except Exception:
-            ok = False
+        except (FloatingPointError, ValueError, IndexError, ZeroDivisionError):
+            ok = False       # a numerical failure in the mutant is a rejection too
     assert not ok, f"pins did not catch mutant {mutant.__name__}"

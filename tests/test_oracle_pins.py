@@ -345,3 +345,106 @@ def test_row_block_agrees_with_full():
         gb += r["grad_b_cols"]
     np.testing.assert_allclose(gw, full["grad_W"][cols], rtol=1e-12, atol=1e-16)
     np.testing.assert_allclose(gb, full["grad_b"][cols], rtol=1e-12, atol=1e-16)
+
+
+# ------------------------------------------------------- per-class weights
+# [LCE] _ChunkContext.neg_weight_target: a row weighs weight[target]; mean
+# divides by the sum of the unmasked row weights (NaN when it is 0).
+def _cw(V, seed=31):
+    return np.random.default_rng(seed).uniform(0.2, 3.0, V)
+
+
+@pytest.mark.parametrize("reduction", RED)
+@pytest.mark.parametrize("ignore_index", [-100, 3])
+def test_class_weights_match_torch(reduction, ignore_index):
+    c = small_case(23, 6, 11, seed=32, ignore_frac=0.2, ignore_index=ignore_index)
+    cw = _cw(11)
+    X = torch.tensor(c["X"], dtype=torch.float64, requires_grad=True)
+    W = torch.tensor(c["W"], dtype=torch.float64, requires_grad=True)
+    b = torch.tensor(c["b"], dtype=torch.float64, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(X @ W.T + b, torch.tensor(c["t"]), weight=torch.tensor(cw),
+                                             ignore_index=ignore_index, reduction=reduction)
+    u = torch.tensor(c["u"], dtype=torch.float64)
+    (loss * u).sum().backward() if reduction == "none" else loss.backward()
+    r = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], ignore_index=ignore_index,
+                                    reduction=reduction, upstream=c["u"], class_weight=cw)
+    np.testing.assert_allclose(r["loss"], loss.detach().numpy(), rtol=1e-13)
+    np.testing.assert_allclose(r["grad_X"], X.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["grad_W"], W.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["grad_b"], b.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("reduction", RED)
+def test_unit_class_weights_change_nothing(reduction):
+    c = _case(N=12, D=5, V=8, seed=33)
+    a = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction=reduction)
+    w = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction=reduction,
+                                    class_weight=np.ones(8))
+    for k in ("loss", "grad_X", "grad_W", "grad_b"):
+        np.testing.assert_array_equal(a[k], w[k])
+
+
+def test_mean_is_invariant_to_scaling_the_class_weights():
+    c = _case(N=14, D=5, V=9, seed=34)
+    cw = _cw(9)
+    a = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], class_weight=cw)
+    s = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], class_weight=cw * 7.5)
+    assert abs(a["loss"] - s["loss"]) <= 1e-14 * abs(a["loss"])
+    for k in ("grad_X", "grad_W", "grad_b"):
+        np.testing.assert_allclose(a[k], s[k], rtol=1e-13, atol=1e-16)
+
+
+def test_weighted_sum_is_the_weighted_row_losses():
+    """sum with class weights = sum_n w[t_n] loss_n of the unweighted rows,
+    and mean divides that by sum_n w[t_n] over counted rows."""
+    c = _case(N=15, D=4, V=7, seed=35)
+    cw = _cw(7)
+    rows = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction="none")
+    valid, _, _, _ = oracle.target_masks(c["t"], 7, -100)
+    wrow = np.where(valid, cw[np.where(valid, c["t"], 0)], 0.0)
+    s = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction="sum", class_weight=cw)
+    m = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction="mean", class_weight=cw)
+    assert abs(s["loss"] - float(np.dot(wrow, rows["loss"]))) < 1e-12
+    assert abs(m["loss"] - s["loss"] / wrow.sum()) < 1e-13
+
+
+def test_zero_total_class_weight():
+    """mean: every counted row weighs 0 -> NaN loss and gradients (the pages
+    divide by NaN when the weight sum is 0); sum: loss 0, gradients 0."""
+    c = _case(N=10, D=4, V=6, seed=36)
+    cw = np.zeros(6)
+    m = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], class_weight=cw)
+    assert math.isnan(m["loss"]) and np.all(np.isnan(m["grad_X"]))
+    s = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], reduction="sum", class_weight=cw)
+    assert s["loss"] == 0.0 and np.all(s["grad_X"] == 0.0) and np.all(s["grad_W"] == 0.0)
+
+
+def test_weighted_mean_finite_differences():
+    c = _case(N=5, D=3, V=7, seed=37)
+    cw = _cw(7)
+    r = oracle.linear_cross_entropy(c["X"], c["W"], c["b"], c["t"], class_weight=cw)
+    X = c["X"].astype(np.float64)
+    for (i, j) in [(0, 0), (2, 1), (4, 2)]:
+        h = 1e-6 * max(1.0, abs(X[i, j]))
+        Xp, Xm = X.copy(), X.copy()
+        Xp[i, j] += h
+        Xm[i, j] -= h
+        lp = oracle.linear_cross_entropy(Xp, c["W"], c["b"], c["t"], class_weight=cw)["loss"]
+        lm = oracle.linear_cross_entropy(Xm, c["W"], c["b"], c["t"], class_weight=cw)["loss"]
+        assert abs((lp - lm) / (2 * h) - r["grad_X"][i, j]) <= 1e-7 * max(1.0, abs(r["grad_X"][i, j]))
+
+
+@pytest.mark.parametrize("reduction", RED)
+def test_standalone_ce_class_weights_match_torch(reduction):
+    rng = np.random.default_rng(38)
+    z = rng.standard_normal((17, 13))
+    t = rng.integers(0, 13, 17)
+    t[[2, 9]] = -100
+    cw = _cw(13, 39)
+    zt = torch.tensor(z, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(zt, torch.tensor(t), weight=torch.tensor(cw),
+                                             reduction=reduction)
+    (loss.sum() * 1.5).backward()
+    l, dl = oracle.softmax_cross_entropy(z, t, reduction=reduction, grad_scale=1.5, class_weight=cw)
+    np.testing.assert_allclose(l, loss.detach().numpy(), rtol=1e-13)
+    np.testing.assert_allclose(dl, zt.grad.numpy(), rtol=1e-12, atol=1e-15)
