@@ -134,6 +134,15 @@ typedef struct {
                                 scalar loss, folded into the gradients
                                 (1.0 for a plain backward) */
   int32_t reserved;          /* set to 0 */
+  const float* class_weight; /* [V] fp32 per-class weights, or NULL.  The
+                                PyTorch module source
+                                torch/nn/modules/linear_cross_entropy.py,
+                                _ChunkContext's negative target weight: a
+                                counted row weighs class_weight[target] in
+                                its loss and gradient (NONE: loss[n] is the
+                                weighted row loss); MEAN divides by the sum
+                                of the counted rows' weights, NaN when that
+                                sum is 0.  NULL weighs every class 1. */
 } lce_io;
 
 /* Validate `d`, resolve the chunk size and build a handle.  Host only.
@@ -179,12 +188,14 @@ LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
 
 /* Standalone softmax cross-entropy on precomputed fp32 logits [N, V]
  * (row-major, row stride V, 16-byte aligned, V % 4 == 0), enqueued on
- * `stream`.  Writes the loss (MEAN / SUM: loss[1]; NONE: loss[N]) and
+ * `stream` (Liger-Kernel issue #343: the loss, with the gradient written over
+ * the logits).  Writes the loss (MEAN / SUM: loss[1]; NONE: loss[N]) and
  * overwrites `logits` in place with the gradient g_n (softmax - onehot), g_n
  * as for lce_forward_backward with grad_output = grad_scale on every counted
- * row for NONE.  n_valid may be NULL.  Errors: INVALID_ARG, UNSUPPORTED,
- * WORKSPACE, HIP. */
-LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets, int64_t N,
+ * row for NONE.  class_weight ([V] fp32 or NULL) weighs rows as in lce_io.
+ * n_valid may be NULL.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets,
+                          const float* class_weight, int64_t N,
                           int64_t V, int64_t ignore_index, int32_t reduction,
                           float grad_scale, float* loss, int64_t* n_valid,
                           void* workspace, size_t ws_bytes, void* stream);

@@ -9,7 +9,7 @@ therefore fixed by (seed, key, block size) alone, blocks can be drawn in
 parallel threads, and any block can be redrawn on its own.
 
 Stream keys: 0 X, 1 W, 2 b, 3 targets, 4 ignore-row permutation,
-5 upstream per-row gradient, 6 standalone-CE logits.
+5 upstream per-row gradient, 6 standalone-CE logits, 7 per-class weights.
 
 bf16 tensors are returned as float32 arrays whose values are exactly
 representable in bf16 (rounded to nearest-even from the float32 draw), so a
@@ -26,7 +26,7 @@ import numpy as np
 
 IGNORE_INDEX = -100
 
-KEY_X, KEY_W, KEY_B, KEY_T, KEY_IGN, KEY_U, KEY_LOGITS = range(7)
+KEY_X, KEY_W, KEY_B, KEY_T, KEY_IGN, KEY_U, KEY_LOGITS, KEY_CW = range(8)
 
 # Elements per generator block (rows per block = BLOCK_ELEMS // row_length).
 BLOCK_ELEMS = 1 << 22
@@ -163,6 +163,17 @@ def upstream_grad(N: int, seed: int) -> np.ndarray:
     """Per-row upstream gradient for reduction='none' backward, N(0,1) fp32."""
     return np.random.default_rng([seed, KEY_U, 0]).standard_normal(
         N, dtype=np.float32)
+
+
+def class_weights(V: int, seed: int, zero_frac: float = 0.0) -> np.ndarray:
+    """Per-class weights, float32 uniform in [0.25, 2); a ``zero_frac``
+    share of the classes (a seeded choice) gets weight 0."""
+    rng = np.random.default_rng([seed, KEY_CW, 0])
+    w = rng.uniform(0.25, 2.0, V).astype(np.float32)
+    n0 = int(round(zero_frac * V))
+    if n0:
+        w[rng.permutation(V)[:n0]] = 0.0
+    return w
 
 
 def lce_inputs(cfg: LceConfig, rows: slice | None = None) -> dict:

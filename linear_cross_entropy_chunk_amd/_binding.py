@@ -40,7 +40,7 @@ class lce_io(ctypes.Structure):
                 ("grad_output", c_void_p), ("loss", c_void_p), ("grad_X", c_void_p),
                 ("grad_W", c_void_p), ("grad_b", c_void_p), ("argmax", c_void_p),
                 ("n_valid", c_void_p), ("n_bad", c_void_p), ("grad_scale", c_float),
-                ("reserved", c_int32)]
+                ("reserved", c_int32), ("class_weight", c_void_p)]
 
 
 class LceError(RuntimeError):
@@ -69,8 +69,9 @@ def lib() -> ctypes.CDLL:
         L.lce_forward_backward.argtypes = [c_void_p, POINTER(lce_io), c_void_p, c_size_t, c_void_p]
         L.lce_destroy.argtypes = [c_void_p]
         L.lce_ce_workspace_size.argtypes = [c_int64, c_int64, POINTER(c_size_t)]
-        L.lce_ce_inplace.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
-                                     c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.lce_ce_inplace.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                     c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                     c_void_p]
         L.lce_timing_enable.argtypes = [c_void_p, c_uint32]
         L.lce_timing_read.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int64)]
         L.lce_status_string.argtypes = [c_int32]
@@ -145,10 +146,11 @@ def lce_ce_workspace_size(N: int, V: int) -> int:
     return n.value
 
 
-def lce_ce_inplace(logits: int, targets: int, N: int, V: int, ignore_index: int, reduction: int,
-                   grad_scale: float, loss: int, n_valid: int, workspace: int, ws_bytes: int,
-                   stream: int) -> None:
-    _check(lib().lce_ce_inplace(c_void_p(logits), c_void_p(targets), N, V, ignore_index,
+def lce_ce_inplace(logits: int, targets: int, class_weight: int | None, N: int, V: int,
+                   ignore_index: int, reduction: int, grad_scale: float, loss: int,
+                   n_valid: int, workspace: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().lce_ce_inplace(c_void_p(logits), c_void_p(targets),
+                                c_void_p(class_weight or None), N, V, ignore_index,
                                 reduction, grad_scale, c_void_p(loss), c_void_p(n_valid or None),
                                 c_void_p(workspace), ws_bytes, c_void_p(stream)),
            "lce_ce_inplace")

@@ -4,7 +4,8 @@ PyTorch supplies device memory (outputs and the workspace) and the stream
 (torch's current stream); the computation itself runs entirely in liblce.so.
 The argument checks mirror the pages' Python validation that a C pointer
 cannot carry: the target dtype (int64, a TypeError on the pages) and the bias
-shape (a RuntimeError on the pages).
+shape (a RuntimeError on the pages). Per-class weights, when given, are one
+float32 value per class on the problem's device.
 """
 from __future__ import annotations
 
@@ -23,6 +24,13 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
+
+
+def _check_class_weight(w, V: int, device: torch.device) -> None:
+    if w is not None and (w.dtype != torch.float32 or tuple(w.shape) != (V,)
+                          or not w.is_contiguous() or w.device != device):
+        raise RuntimeError(f"class_weight must be a contiguous float32 tensor of shape ({V},) "
+                           f"on {device}")
 
 
 def _device(device) -> torch.device:
@@ -91,8 +99,9 @@ class LinearCrossEntropy:
             out["argmax"] = torch.empty(N, dtype=torch.int32, device=dev)
         return out
 
-    def check_inputs(self, X, W, t, b=None, grad_output=None) -> None:
+    def check_inputs(self, X, W, t, b=None, grad_output=None, class_weight=None) -> None:
         N, D, V = self.shape
+        _check_class_weight(class_weight, V, self.device)
         if t.dtype != torch.int64:
             raise TypeError(f"target dtype must be torch.int64, got {t.dtype}")
         if b is not None and tuple(b.shape) != (V,):
@@ -112,25 +121,26 @@ class LinearCrossEntropy:
             raise RuntimeError("grad_output must be a float32 tensor of shape (N,)")
 
     def make_io(self, X, W, t, b=None, *, out: dict, grad_output=None,
-                grad_scale: float = 1.0) -> B.lce_io:
+                grad_scale: float = 1.0, class_weight=None) -> B.lce_io:
         return B.lce_io(X=_ptr(X), W=_ptr(W), b=_ptr(b), targets=_ptr(t),
                         grad_output=_ptr(grad_output), loss=_ptr(out.get("loss")),
                         grad_X=_ptr(out.get("grad_X")), grad_W=_ptr(out.get("grad_W")),
                         grad_b=_ptr(out.get("grad_b")), argmax=_ptr(out.get("argmax")),
                         n_valid=_ptr(out.get("n_valid")), n_bad=_ptr(out.get("n_bad")),
-                        grad_scale=grad_scale, reserved=0)
+                        grad_scale=grad_scale, reserved=0, class_weight=_ptr(class_weight))
 
     def run_io(self, io: B.lce_io) -> None:
         B.lce_forward_backward(self.handle, io, self.workspace.data_ptr(), self.ws_bytes,
                                _stream())
 
     def __call__(self, X, W, t, b=None, *, grad_output=None, grad_scale: float = 1.0,
-                 out: dict | None = None) -> dict:
-        self.check_inputs(X, W, t, b, grad_output)
+                 class_weight=None, out: dict | None = None) -> dict:
+        self.check_inputs(X, W, t, b, grad_output, class_weight)
         grads = self.reduction != "none" or grad_output is not None
         if out is None:
             out = self.make_outputs(grads)
-        io = self.make_io(X, W, t, b, out=out, grad_output=grad_output, grad_scale=grad_scale)
+        io = self.make_io(X, W, t, b, out=out, grad_output=grad_output, grad_scale=grad_scale,
+                          class_weight=class_weight)
         self.run_io(io)
         return out
 
@@ -139,7 +149,7 @@ def linear_cross_entropy(X, W, t, b=None, *, reduction: str = "mean", ignore_ind
                          chunk_rows: int = 0, acc_policy: str = "accurate",
                          grad_output=None, grad_scale: float = 1.0, argmax: bool = False,
                          grad_x: bool = True, grad_w: bool = True,
-                         grad_b: bool | None = None) -> dict:
+                         grad_b: bool | None = None, class_weight=None) -> dict:
     """One-shot chunked forward+backward; returns loss, gradients, counts."""
     N, D = X.shape
     V = W.shape[0]
@@ -147,7 +157,8 @@ def linear_cross_entropy(X, W, t, b=None, *, reduction: str = "mean", ignore_ind
                             ignore_index=ignore_index, chunk_rows=chunk_rows,
                             acc_policy=acc_policy, grad_x=grad_x, grad_w=grad_w,
                             grad_b=grad_b, argmax=argmax, device=X.device)
-    return op(X, W, t, b, grad_output=grad_output, grad_scale=grad_scale)
+    return op(X, W, t, b, grad_output=grad_output, grad_scale=grad_scale,
+              class_weight=class_weight)
 
 
 class CrossEntropyInplace:
@@ -167,13 +178,16 @@ class CrossEntropyInplace:
                                 device=self.device)
         self.n_valid = torch.empty(1, dtype=torch.int64, device=self.device)
 
-    def __call__(self, logits: torch.Tensor, t: torch.Tensor, grad_scale: float = 1.0):
+    def __call__(self, logits: torch.Tensor, t: torch.Tensor, grad_scale: float = 1.0,
+                 class_weight=None):
+        _check_class_weight(class_weight, self.V, self.device)
         if t.dtype != torch.int64:
             raise TypeError(f"target dtype must be torch.int64, got {t.dtype}")
         if (logits.dtype != torch.float32 or not logits.is_contiguous()
                 or tuple(logits.shape) != (self.N, self.V)):
             raise RuntimeError("logits must be a contiguous float32 tensor of shape (N, V)")
-        B.lce_ce_inplace(logits.data_ptr(), t.data_ptr(), self.N, self.V, self.ignore_index,
+        B.lce_ce_inplace(logits.data_ptr(), t.data_ptr(), _ptr(class_weight), self.N, self.V,
+                         self.ignore_index,
                          _REDUCTIONS[self.reduction], grad_scale, self.loss.data_ptr(),
                          self.n_valid.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
                          _stream())
@@ -181,7 +195,7 @@ class CrossEntropyInplace:
 
 
 def cross_entropy_inplace(logits, t, *, reduction: str = "mean", ignore_index: int = -100,
-                          grad_scale: float = 1.0):
+                          grad_scale: float = 1.0, class_weight=None):
     op = CrossEntropyInplace(logits.shape[0], logits.shape[1], reduction=reduction,
                              ignore_index=ignore_index, device=logits.device)
-    return op(logits, t, grad_scale)
+    return op(logits, t, grad_scale, class_weight)

@@ -45,7 +45,7 @@ struct lce_handle {
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
-      o_gw32, o_gbp, o_gb32, o_lrows, o_cnt, total;
+      o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, total;
   TimingPool timing;
 };
 
@@ -162,7 +162,8 @@ void plan(lce_handle* h) {
   h->o_gbp = take((c / 64) * Vp * 4, h->want_b);
   h->o_gb32 = take(Vp * 4, h->want_b);
   h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
-  h->o_cnt = take(2 * 8, true);
+  h->o_wrow = take(std::max<int64_t>(N, 1) * 4, true);
+  h->o_cnt = take(3 * 8, true);       // n_valid, n_bad, row-weight sum (double)
   h->total = o;
 }
 
@@ -322,10 +323,12 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   float* gbp = at<float>(workspace, h->o_gbp);
   float* gb32 = at<float>(workspace, h->o_gb32);
   float* lrows = at<float>(workspace, h->o_lrows);
+  float* wrow = at<float>(workspace, h->o_wrow);
   int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
 
   LCE_LAUNCH(h, LCE_K_PREP, lce::prep_targets(io->targets, N, V, d.ignore_index, d.reduction, io->grad_scale,
-                            io->grad_output, tc, g, cnt, io->n_valid, io->n_bad, s));
+                            io->grad_output, io->class_weight, tc, g, wrow, cnt, io->n_valid,
+                            io->n_bad, s));
 
   if (N == 0) {
     if (want_w) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_W, static_cast<size_t>(d.V) * d.D * es, s));
@@ -357,7 +360,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(bf16, la, s));
 
     float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
-    LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0, rows, lse, loss_rows,
+    LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
+                             io->class_weight ? wrow + row0 : nullptr, rows, lse, loss_rows,
                              h->want_argmax ? io->argmax + row0 : nullptr, s));
     if (!grads) continue;
 
@@ -428,13 +432,14 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
 lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes) {
   if (!bytes || N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
   const int64_t n = std::max<int64_t>(N, 1);
-  *bytes = align_up(n * 4) * 3 + align_up(16);
+  *bytes = align_up(n * 4) * 4 + align_up(24);
   return LCE_OK;
 }
 
-lce_status lce_ce_inplace(float* logits, const int64_t* targets, int64_t N, int64_t V,
-                          int64_t ignore_index, int32_t reduction, float grad_scale, float* loss,
-                          int64_t* n_valid, void* workspace, size_t ws_bytes, void* stream) {
+lce_status lce_ce_inplace(float* logits, const int64_t* targets, const float* class_weight,
+                          int64_t N, int64_t V, int64_t ignore_index, int32_t reduction,
+                          float grad_scale, float* loss, int64_t* n_valid, void* workspace,
+                          size_t ws_bytes, void* stream) {
   if (N < 0 || V < 1 || reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
   if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
   if (!loss) return LCE_ERR_INVALID_ARG;
@@ -450,15 +455,16 @@ lce_status lce_ce_inplace(float* logits, const int64_t* targets, int64_t N, int6
   int* tc = reinterpret_cast<int*>(ws);
   float* g = reinterpret_cast<float*>(ws + align_up(n * 4));
   float* lrows = reinterpret_cast<float*>(ws + 2 * align_up(n * 4));
-  int64_t* cnt = reinterpret_cast<int64_t*>(ws + 3 * align_up(n * 4));
+  float* wrow = reinterpret_cast<float*>(ws + 3 * align_up(n * 4));
+  int64_t* cnt = reinterpret_cast<int64_t*>(ws + 4 * align_up(n * 4));
   const bool none = reduction == LCE_NONE;
   // Per-row weights: 'none' takes grad_scale on every counted row, which is
   // the weight the 'sum' reduction gives.
   LCE_HIP(lce::prep_targets(targets, static_cast<int>(N), static_cast<int>(V), ignore_index,
-                            none ? LCE_SUM : reduction, grad_scale, nullptr, tc, g, cnt, n_valid,
-                            nullptr, s));
+                            none ? LCE_SUM : reduction, grad_scale, nullptr, class_weight, tc, g,
+                            wrow, cnt, n_valid, nullptr, s));
   LCE_HIP(lce::ce_inplace_rows(logits, static_cast<int>(N), static_cast<int>(V), tc, g,
-                               none ? loss : lrows, s));
+                               class_weight ? wrow : nullptr, none ? loss : lrows, s));
   if (!none) LCE_HIP(lce::loss_reduce(lrows, static_cast<int>(N), cnt, reduction, loss, s));
   return LCE_OK;
 }

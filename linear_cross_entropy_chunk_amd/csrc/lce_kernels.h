@@ -68,20 +68,25 @@ hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s);
 
 // ---- row-wise kernels (lce_rowops.hip) -------------------------------------
 // Target preparation: counts rows, forms corrected targets and row weights.
-//   tc[n] = t[n] if 0 <= t[n] < V and t[n] != ignore_index, else -1
-//   g[n]  = per-row weight of the reduction (see lce.h)
-// counts[0] = n_valid, counts[1] = n_bad (also copied to the optional outs).
+//   tc[n]   = t[n] if 0 <= t[n] < V and t[n] != ignore_index, else -1
+//   w[n]    = class_weight[tc[n]] (1 without class weights) if tc[n] >= 0,
+//             else 0; written to wrow when wrow != null
+//   g[n]    = per-row weight of the reduction (see lce.h), built from w
+// counts[0] = n_valid, counts[1] = n_bad (also copied to the optional outs),
+// counts[2] = the bits of the double sum of w (the mean's denominator).
 hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index,
                         int reduction, float grad_scale, const float* upstream,
-                        int* tc, float* g, int64_t* counts, int64_t* n_valid_out,
-                        int64_t* n_bad_out, hipStream_t s);
+                        const float* class_weight, int* tc, float* g, float* wrow,
+                        int64_t* counts, int64_t* n_valid_out, int64_t* n_bad_out,
+                        hipStream_t s);
 
 // Row combine over the n_vt statistics blocks of a chunk: lse[n] (chunk-local),
-// loss_rows[n] = lse - zt (0 if tc < 0), argmax_out[n] if non-null.
+// loss_rows[n] = w[n] (lse - zt) (0 if tc < 0; w = wrow[n], 1 when wrow is
+// null), argmax_out[n] if non-null.
 hipError_t row_combine(const float* m_part, const float* s_part, const int* i_part,
                        int64_t ldp, int n_vt, const float* zt, const int* tc,
-                       int rows, float* lse, float* loss_rows, int* argmax_out,
-                       hipStream_t s);
+                       const float* wrow, int rows, float* lse, float* loss_rows,
+                       int* argmax_out, hipStream_t s);
 
 // In-place finalize: T[n][v] <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
 // - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V);
@@ -105,15 +110,16 @@ hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64
                             int V, float* acc, void* out, bool first, bool last,
                             hipStream_t s);
 
-// Final loss: mean (sum / n_valid, NaN when 0) or sum, in float64, fixed order.
+// Final loss: mean (sum / the row-weight sum in counts[2], NaN when 0) or
+// sum, in float64, fixed order.
 hipError_t loss_reduce(const float* loss_rows, int N, const int64_t* counts,
                        int reduction, float* loss, hipStream_t s);
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // Standalone CE: rows of fp32 logits overwritten with g_n (softmax - onehot);
-// loss_rows[n] = lse - z_t (0 if tc < 0).
+// loss_rows[n] = w[n] (lse - z_t) (0 if tc < 0; w = wrow[n], 1 when null).
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
-                           float* loss_rows, hipStream_t s);
+                           const float* wrow, float* loss_rows, hipStream_t s);
 
 }  // namespace lce

@@ -39,61 +39,76 @@ __device__ __forceinline__ float fast_exp(float x) {
 
 // ------------------------------------------------------------ target prep
 // One workgroup: the mean's denominator must be known before any row weight.
+// The weight sum is formed in float64 in a fixed order (per thread, then the
+// wave's butterfly, then the waves in index order), so it is deterministic.
 constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const int64_t* __restrict__ t, int N, int V, int64_t ign, int reduction,
-    float grad_scale, const float* __restrict__ upstream, int* __restrict__ tc,
-    float* __restrict__ g, int64_t* __restrict__ counts, int64_t* n_valid_out,
-    int64_t* n_bad_out) {
+    float grad_scale, const float* __restrict__ upstream, const float* __restrict__ cw,
+    int* __restrict__ tc, float* __restrict__ g, float* __restrict__ wrow,
+    int64_t* __restrict__ counts, int64_t* n_valid_out, int64_t* n_bad_out) {
   __shared__ long long s_valid[kPrepThreads / 64], s_bad[kPrepThreads / 64];
+  __shared__ double s_w[kPrepThreads / 64];
   __shared__ long long tot[2];
+  __shared__ double wtot;
   long long cv = 0, cb = 0;
+  double sw = 0.0;
   for (int n = threadIdx.x; n < N; n += kPrepThreads) {
     const int64_t x = t[n];
     const bool ignored = x == ign;
     const bool bad = !ignored && (x < 0 || x >= V);
-    cv += (!ignored && !bad) ? 1 : 0;
+    const bool valid = !ignored && !bad;
+    cv += valid ? 1 : 0;
     cb += bad ? 1 : 0;
+    if (valid) sw += cw ? static_cast<double>(cw[x]) : 1.0;
   }
   for (int o = 32; o > 0; o >>= 1) {
     cv += __shfl_xor(cv, o);
     cb += __shfl_xor(cb, o);
+    sw += __shfl_xor(sw, o);
   }
   if ((threadIdx.x & 63) == 0) {
     s_valid[threadIdx.x >> 6] = cv;
     s_bad[threadIdx.x >> 6] = cb;
+    s_w[threadIdx.x >> 6] = sw;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     long long a = 0, b = 0;
-    for (int w = 0; w < kPrepThreads / 64; ++w) {
-      a += s_valid[w];
-      b += s_bad[w];
+    double w = 0.0;
+    for (int k = 0; k < kPrepThreads / 64; ++k) {
+      a += s_valid[k];
+      b += s_bad[k];
+      w += s_w[k];
     }
     tot[0] = a;
     tot[1] = b;
+    wtot = w;
     counts[0] = a;
     counts[1] = b;
+    counts[2] = __double_as_longlong(w);
     if (n_valid_out) *n_valid_out = a;
     if (n_bad_out) *n_bad_out = b;
   }
   __syncthreads();
-  const long long nv = tot[0];
+  const double d = wtot;
   // reduction codes follow lce.h: 0 mean, 1 sum, 2 none
-  const bool mean_nan = reduction == 0 && nv == 0;
-  const float gmean = nv > 0 ? grad_scale / static_cast<float>(nv) : 0.0f;
+  const bool mean_nan = reduction == 0 && d == 0.0;
+  const double gmean = d != 0.0 ? static_cast<double>(grad_scale) / d : 0.0;
   for (int n = threadIdx.x; n < N; n += kPrepThreads) {
     const int64_t x = t[n];
     const bool valid = x != ign && x >= 0 && x < V;
     tc[n] = valid ? static_cast<int>(x) : -1;
-    float w;
-    if (mean_nan) w = NAN;
-    else if (!valid) w = 0.0f;
-    else if (reduction == 0) w = gmean;
-    else if (reduction == 1) w = grad_scale;
-    else w = upstream ? upstream[n] : 1.0f;
-    g[n] = w;
+    const float wn = valid ? (cw ? cw[x] : 1.0f) : 0.0f;
+    if (wrow) wrow[n] = wn;
+    float gn;
+    if (mean_nan) gn = NAN;
+    else if (!valid) gn = 0.0f;
+    else if (reduction == 0) gn = static_cast<float>(gmean * wn);
+    else if (reduction == 1) gn = grad_scale * wn;
+    else gn = (upstream ? upstream[n] : 1.0f) * wn;
+    g[n] = gn;
   }
 }
 
@@ -105,7 +120,8 @@ constexpr int kCombRows = 8, kCombParts = 32;
 __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
-    int rows, float* __restrict__ lse, float* __restrict__ loss_rows, int* __restrict__ amax) {
+    const float* __restrict__ wrow, int rows, float* __restrict__ lse,
+    float* __restrict__ loss_rows, int* __restrict__ amax) {
   __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
   __shared__ int sk[kCombParts][kCombRows];
   const int r = threadIdx.x % kCombRows, p = threadIdx.x / kCombRows;
@@ -140,7 +156,7 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
     }
     const float L = M + logf(S);
     lse[n] = L;
-    loss_rows[n] = tc[n] >= 0 ? L - zt[n] : 0.0f;
+    loss_rows[n] = tc[n] >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt[n]) : 0.0f;
     // K stays unset only if every block maximum is NaN; read block 0 then.
     if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
   }
@@ -298,8 +314,8 @@ __global__ __launch_bounds__(kLossThreads) void k_loss_reduce(const float* __res
   if (threadIdx.x == 0) {
     double L = part[0];
     if (reduction == 0) {
-      const long long nv = counts[0];
-      L = nv > 0 ? L / static_cast<double>(nv) : NAN;
+      const double d = __longlong_as_double(counts[2]);   // sum of the counted rows' weights
+      L = d != 0.0 ? L / d : NAN;
     }
     loss[0] = static_cast<float>(L);
   }
@@ -324,6 +340,7 @@ constexpr int kCeUnroll = 8;
 __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, int V,
                                                        const int* __restrict__ tc,
                                                        const float* __restrict__ g,
+                                                       const float* __restrict__ wrow,
                                                        float* __restrict__ loss_rows) {
   __shared__ float wm[kCeThreads / 64], wsum[kCeThreads / 64];
   __shared__ float bcast[2];
@@ -371,7 +388,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
       if (wm[w] > -INFINITY) S += wsum[w] * expf(wm[w] - M);
     const float L = M + logf(S);
     const float zt = t >= 0 ? z[static_cast<int64_t>(n) * V + t] : 0.0f;
-    loss_rows[n] = t >= 0 ? L - zt : 0.0f;
+    loss_rows[n] = t >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt) : 0.0f;
     bcast[0] = L;
   }
   __syncthreads();
@@ -410,6 +427,7 @@ template <int kRegVec>
 __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict__ z, int V,
                                                               const int* __restrict__ tc,
                                                               const float* __restrict__ g,
+                                                              const float* __restrict__ wrow,
                                                               float* __restrict__ loss_rows) {
   __shared__ __attribute__((aligned(16))) f32x4_t tail[kCeTailVec];
   __shared__ float wred[kOnThreads / 64];
@@ -497,7 +515,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   }
   const float S = block_sum(s);
   const float L = M + logf(S);
-  if (tid == 0) loss_rows[n] = t >= 0 ? L - zt : 0.0f;
+  if (tid == 0) loss_rows[n] = t >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt) : 0.0f;
 
   const float gn = g[n];
   const float scale = gn / S;
@@ -523,20 +541,20 @@ inline unsigned cdiv_u(int64_t a, int64_t b) { return static_cast<unsigned>((a +
 }  // namespace
 
 hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index, int reduction,
-                        float grad_scale, const float* upstream, int* tc, float* g,
-                        int64_t* counts, int64_t* n_valid_out, int64_t* n_bad_out,
-                        hipStream_t s) {
-  k_prep<<<1, kPrepThreads, 0, s>>>(t, N, V, ignore_index, reduction, grad_scale, upstream, tc,
-                                    g, counts, n_valid_out, n_bad_out);
+                        float grad_scale, const float* upstream, const float* class_weight,
+                        int* tc, float* g, float* wrow, int64_t* counts, int64_t* n_valid_out,
+                        int64_t* n_bad_out, hipStream_t s) {
+  k_prep<<<1, kPrepThreads, 0, s>>>(t, N, V, ignore_index, reduction, grad_scale, upstream,
+                                    class_weight, tc, g, wrow, counts, n_valid_out, n_bad_out);
   return hipGetLastError();
 }
 
 hipError_t row_combine(const float* m_part, const float* s_part, const int* i_part, int64_t ldp,
-                       int n_vt, const float* zt, const int* tc, int rows, float* lse,
-                       float* loss_rows, int* argmax_out, hipStream_t s) {
+                       int n_vt, const float* zt, const int* tc, const float* wrow, int rows,
+                       float* lse, float* loss_rows, int* argmax_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine<<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(m_part, s_part, i_part, ldp, n_vt, zt, tc, rows,
-                                                 lse, loss_rows, argmax_out);
+  k_row_combine<<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(
+      m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, rows, lse, loss_rows, argmax_out);
   return hipGetLastError();
 }
 
@@ -613,15 +631,15 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
-                           float* loss_rows, hipStream_t s) {
+                           const float* wrow, float* loss_rows, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   // Rows of 64K..128K classes stay on chip (one HBM read); others stream twice.
   const int V4 = V / 4;
   auto fits = [&](int reg) { return V4 <= kOnThreads * reg + kCeTailVec; };
-  if (V4 >= 16384 && fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
-  else if (V4 >= 16384 && fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
-  else if (V4 >= 16384 && fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, loss_rows);
-  else k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, loss_rows);
+  if (V4 >= 16384 && fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (V4 >= 16384 && fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (V4 >= 16384 && fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   return hipGetLastError();
 }
 

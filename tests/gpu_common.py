@@ -45,7 +45,7 @@ def to_dev(a, dt: str):
 def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0,
             acc_policy: str = "accurate", ignore_index: int = -100, grads: str = "xwb",
             argmax: bool = True, upstream=None, grad_scale: float = 1.0, bias: bool | None = None,
-            repeat: int = 1) -> dict | list:
+            repeat: int = 1, class_weight=None) -> dict | list:
     X, W, b, t = case["X"], case["W"], case["b"], case["t"]
     if bias is False:
         b = None
@@ -59,9 +59,11 @@ def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0
     td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
     ud = None if upstream is None else torch.from_numpy(
         np.ascontiguousarray(upstream, dtype=np.float32)).to("cuda")
+    cwd = None if class_weight is None else torch.from_numpy(
+        np.ascontiguousarray(class_weight, dtype=np.float32)).to("cuda")
     results = []
     for _ in range(repeat):
-        out = op(Xd, Wd, td, bd, grad_output=ud, grad_scale=grad_scale)
+        out = op(Xd, Wd, td, bd, grad_output=ud, grad_scale=grad_scale, class_weight=cwd)
         torch.cuda.synchronize()
         res = {}
         for k, v in out.items():
@@ -126,12 +128,14 @@ def check_all(gpu: dict, ref: dict, dt: str, reduction: str, z=None, grads="xwb"
 
 
 def run_ce(z: np.ndarray, t: np.ndarray, *, reduction: str = "mean", ignore_index: int = -100,
-           grad_scale: float = 1.0):
+           grad_scale: float = 1.0, class_weight=None):
     zd = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to("cuda")
     td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
     op = CrossEntropyInplace(z.shape[0], z.shape[1], reduction=reduction,
                              ignore_index=ignore_index)
-    loss, nv = op(zd, td, grad_scale)
+    cwd = None if class_weight is None else torch.from_numpy(
+        np.ascontiguousarray(class_weight, dtype=np.float32)).to("cuda")
+    loss, nv = op(zd, td, grad_scale, cwd)
     torch.cuda.synchronize()
     return (loss.cpu().numpy().astype(np.float64), int(nv.cpu()[0]),
             zd.cpu().numpy().astype(np.float64))
