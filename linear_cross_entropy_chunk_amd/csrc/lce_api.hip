@@ -43,6 +43,8 @@ struct lce_handle {
   int64_t n_groups;
   bool want_x, want_w, want_b, want_argmax, want_any;
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
+  bool w_inplace;     // grad_W reads dL where it lies in T (bf16 k-major operand)
+  int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
       o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, total;
@@ -129,6 +131,13 @@ void plan(lce_handle* h) {
   h->k_grp = h->grp * h->c_pad;
   h->n_groups = h->n_chunks ? cdiv64(h->n_chunks, h->grp) : 0;
   h->w_acc32 = h->want_w && h->bf16 && d.acc_policy == LCE_ACCURATE && h->n_groups > 1;
+  // bf16: the chunks of a group keep their dL in T (chunk j at row j c_pad of
+  // every panel) and grad_W reads it there as a k-major operand, so dL^T is
+  // not staged.  This needs the chunks back to back (c a multiple of 64, or
+  // one chunk per group) so that T's rows line up with the staged X^T
+  // columns.  Otherwise, and for fp32, the finalize stages dL^T.
+  h->w_inplace = h->want_w && h->bf16 && (h->c % 64 == 0 || h->grp == 1);
+  h->t_rows = h->w_inplace ? h->k_grp : h->c_pad;
 
   // split-K for grad_X = dL . W: aim at >= 512 workgroups, >= 1024 K per split.
   const int64_t tiles = cdiv64(h->c, lce::kTile) * cdiv64(d.D, lce::kTile);
@@ -145,8 +154,8 @@ void plan(lce_handle* h) {
     if (need) o = align_up(o + bytes);
     return need ? at : static_cast<size_t>(-1);
   };
-  h->o_T = take(c * Vp * es, h->want_any);
-  h->o_dLt = take(Vp * h->k_grp * es, h->want_w);
+  h->o_T = take(h->t_rows * Vp * es, h->want_any);
+  h->o_dLt = take(Vp * h->k_grp * es, h->want_w && !h->w_inplace);
   // bf16 grad_X reads W in place (k-major operand); fp32 uses a transposed copy
   h->o_Wt = take(D * Vp * es, h->want_x && !h->bf16);
   h->o_Xt = take(D * h->k_grp * es, h->want_w);
@@ -347,6 +356,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     const int rows_pad = static_cast<int>(round_up(rows, 64));
     const bool first = ck == 0, last = ck + 1 == h->n_chunks;
     const void* Xc = Xb + row0 * d.D * es;
+    const int64_t jj = ck % h->grp;               // position inside the grad_W group
+    const int64_t tps = h->t_rows * lce::kTile;   // T's panel stride (elements)
+    void* Tc = static_cast<char*>(T) + (h->w_inplace ? jj * cp : 0) * lce::kTile * es;
 
     lce::LogitsLse la{};
     la.X = Xc; la.ldx = D;
@@ -354,7 +366,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.bias = io->b;
     la.tc = tc + row0;
     la.rows = rows; la.V = V; la.D = D;
-    la.T = grads ? T : nullptr; la.ldt = Vp;
+    la.T = grads ? Tc : nullptr; la.tps = tps;
     la.m_part = mp; la.s_part = sp; la.i_part = h->want_argmax ? ip : nullptr; la.ldp = cp;
     la.zt = zt;
     LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(bf16, la, s));
@@ -365,9 +377,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                              h->want_argmax ? io->argmax + row0 : nullptr, s));
     if (!grads) continue;
 
-    const int64_t jj = ck % h->grp;               // position inside the grad_W group
-    char* dLt_j = static_cast<char*>(dLt) + jj * cp * es;
-    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, T, Vp, want_w ? dLt_j : nullptr,
+    char* dLt_j = dLt ? static_cast<char*>(dLt) + jj * cp * es : nullptr;
+    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, Tc, tps,
+                                  want_w && !h->w_inplace ? dLt_j : nullptr,
                                   h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
                                   V, static_cast<int>(Vp), want_b ? gbp : nullptr, s));
     if (want_x) {
@@ -381,7 +393,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       } else {
         gx.A = Wt; gx.lda = Vp;
       }
-      gx.B = T; gx.ldb = Vp;
+      gx.B = Tc; gx.ldb = lce::kTile; gx.b_pstride = tps;
       gx.M = D; gx.N = rows; gx.K = static_cast<int>(Vp);
       gx.splits = h->splits; gx.k_split = h->k_split;
       gx.split_stride = static_cast<int64_t>(rows) * D;
@@ -399,13 +411,20 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                                                         h->k_grp, rows_pad, s));
       if (jj + 1 == h->grp || last) {
         // grad_W[V][D] += dL^T . X over the group's rows, as (X^T)[D][K]
-        // against (dL^T)[V][K] with the transposed store.
+        // against dL^T with the transposed store: in place, dL is T's panels
+        // read k-major; staged, the finalize's dL^T[V][K].
         const int64_t gi = ck / h->grp;
         const bool gfirst = gi == 0, glast = last;
         lce::GemmNT gw{};
         gw.A = Xt; gw.lda = h->k_grp;
-        gw.B = dLt; gw.ldb = h->k_grp;
-        gw.M = D; gw.N = V; gw.K = static_cast<int>(jj * cp + rows_pad);
+        gw.K = static_cast<int>(jj * cp + rows_pad);
+        if (h->w_inplace) {
+          gw.B = T; gw.ldb = lce::kTile; gw.b_pstride = tps;
+          gw.b_kmajor = true; gw.b_krows = gw.K;
+        } else {
+          gw.B = dLt; gw.ldb = h->k_grp;
+        }
+        gw.M = D; gw.N = V;
         gw.splits = 1; gw.k_split = gw.K; gw.split_stride = 0;
         gw.ldc = D;
         gw.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along V

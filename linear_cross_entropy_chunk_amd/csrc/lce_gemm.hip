@@ -171,6 +171,10 @@ __device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
 // tile's existing rows); so do k-rows of a k-major operand past its valid
 // rows.  With kKTail, 16-byte chunks at or past k_end read as zero too
 // (their offsets are sent out of range; K-contiguous operands only).
+// With kBPan, B lies in the T panel layout (ldb = kTile, panel stride b_ps):
+// K-contiguous, a stage's 64 k sit in panel k0 / kTile and the copy's
+// descriptor starts at that panel's tile rows; k-major, the tile's kTile
+// columns are one panel and the descriptor starts at its k-row k0.
 //
 // Per stage s (two sub-steps of 4 chunks, 64 MFMAs per wave each), every wave:
 //   sub-step 0 and the first half of sub-step 1: MFMAs from registers; the
@@ -182,16 +186,17 @@ __device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
 //     stage s + 1; 8 copies of B of stage s + 2 into slot 2s mod 5.
 // A stage's B thus has three quarters of a stage to land and its A about
 // seven quarters.
-template <typename T, bool kKTail, bool kATr, bool kBTr>
+template <typename T, bool kKTail, bool kATr, bool kBTr, bool kBPan = false>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          int a_krows,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
-                                         int b_krows,
+                                         int b_krows, int64_t b_ps,
                                          int k_begin, int k_end, char* __restrict__ lds,
                                          Acc& acc) {
   static_assert(kI == 8 && kJ == 8 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
   static_assert(!(kATr || kBTr) || sizeof(T) == 2, "k-major operands are bf16 only");
   static_assert(!(kKTail && (kATr || kBTr)), "k tails apply to K-contiguous operands");
+  static_assert(!(kKTail && kBPan), "panels hold whole stages");
   constexpr int kEs = static_cast<int>(sizeof(T));
   constexpr int kBK = kRowBytes / kEs;            // K elements per stage
   constexpr int kVec = 16 / kEs;                  // elements per 16-byte chunk
@@ -231,25 +236,38 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
     va[j] = lane_off(kATr, lda, j);
     vb[j] = lane_off(kBTr, ldb, j);
   }
+  // a descriptor whose fields are visibly uniform, so that it lives in SGPRs
+  auto uniform_rsrc = [](const T* p, int64_t bytes) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+    const int range = __builtin_amdgcn_readfirstlane(
+        bytes > 0x7ffff000LL * 2 ? -1 : static_cast<int>(static_cast<uint32_t>(bytes)));
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, range, 0x00020000);
+  };
   auto copy = [&](int st, int slot, bool opb, int j) {
     const int k0 = k_begin + min(st, nk - 1) * kBK;   // stages past the end repeat the last
     const uint32_t dst = lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024);
     const bool tr = opb ? kBTr : kATr;
-    if (tr) {
+    if (kBPan && opb && !kBTr) {
+      // the tile's rows of panel k0 / kTile; rows past N read as zero
+      const T* base = B + (k0 / kTile) * b_ps + static_cast<int64_t>(n0) * kTile;
+      const int64_t bytes = static_cast<int64_t>(min(N - n0, kTile)) * kTile * kEs;
+      copy16_to_lds(uniform_rsrc(base, bytes), vb[j], dst,
+                    __builtin_amdgcn_readfirstlane((k0 % kTile) * kEs));
+    } else if (kBPan && opb) {
+      // k-major panel of the tile's columns: k-rows from k0 to b_krows
+      const T* base = B + (n0 / kTile) * b_ps + static_cast<int64_t>(k0) * kTile;
+      const int64_t bytes = static_cast<int64_t>(max(b_krows - k0, 0)) * kTile * kEs;
+      copy16_to_lds(uniform_rsrc(base, bytes), vb[j], dst);
+    } else if (tr) {
       const T* base = opb ? B + n0 : A + m0;
       const int64_t ld = opb ? ldb : lda;
       const int krows = opb ? b_krows : a_krows;
       const int64_t left = (static_cast<int64_t>(max(krows - k0, 0)) * ld - (opb ? n0 : m0)) * kEs;
-      // the descriptor must live in SGPRs: make its fields visibly uniform
-      const uint64_t addr = reinterpret_cast<uint64_t>(base + static_cast<int64_t>(k0) * ld);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
-      const int64_t bytes = max<int64_t>(left, 0);
-      const int range = __builtin_amdgcn_readfirstlane(
-          bytes > 0x7ffff000LL * 2 ? -1 : static_cast<int>(static_cast<uint32_t>(bytes)));
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, range, 0x00020000);
-      copy16_to_lds(rs, opb ? vb[j] : va[j], dst);
+      copy16_to_lds(uniform_rsrc(base + static_cast<int64_t>(k0) * ld, max<int64_t>(left, 0)),
+                    opb ? vb[j] : va[j], dst);
     } else {
       int o = opb ? vb[j] : va[j];
       if constexpr (kKTail) {
@@ -388,7 +406,7 @@ __device__ __forceinline__ void store4(T* p, f32x4_t v) {
   }
 }
 
-template <typename T, int kMode, bool kATr, bool kBTr>
+template <typename T, int kMode, bool kATr, bool kBTr, bool kBPan>
 __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   const int tiles_m = cdiv(g.M, kTile), tiles_n = cdiv(g.N, kTile);
@@ -400,9 +418,9 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   const int kb = split * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   Acc acc;
-  mainloop<T, false, kATr, kBTr>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M, g.a_krows,
-                                 static_cast<const T*>(g.B), g.ldb, tn * kTile, g.N, g.b_krows,
-                                 kb, ke, lds, acc);
+  mainloop<T, false, kATr, kBTr, kBPan>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
+                                        g.a_krows, static_cast<const T*>(g.B), g.ldb, tn * kTile,
+                                        g.N, g.b_krows, g.b_pstride, kb, ke, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -454,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   // M = classes (rows of W), N = chunk rows (rows of X), K = D.
   mainloop<T, kKTail, false, false>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V, 0,
                                     static_cast<const T*>(a.X), a.ldx, tn * kTile, a.rows, 0,
-                                    0, a.D, lds, acc);
+                                    0, 0, a.D, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -476,7 +494,9 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 
   // The epilogue walks the eight 16-column blocks j one at a time so that
   // only 32 accumulators per lane are live in VGPRs.
-  T* Tm = static_cast<T*>(a.T);
+  // the tile's panel of T; the lane's first class within it
+  T* Tm = static_cast<T*>(a.T) + static_cast<int64_t>(tm) * a.tps;
+  const int vpan = wm * kWaveM + 4 * q;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
@@ -571,9 +591,9 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
       }
       // 6. the exp tile T[n][v], 4 consecutive classes per store.
       if constexpr (kStoreT) {
-        T* row = Tm + static_cast<int64_t>(n) * a.ldt;
+        T* row = Tm + static_cast<int64_t>(n) * kTile;
 #pragma unroll
-        for (int i = 0; i < kI; ++i) store4(row + vlane + kBlk * i, acc[i][j]);
+        for (int i = 0; i < kI; ++i) store4(row + vpan + kBlk * i, acc[i][j]);
       }
     }
     // keep the blocks apart so only one block's values are live at a time
@@ -582,13 +602,15 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 }
 
 // Two entry points with the same body so profiles tell the products apart.
+// grad_X's B is always T (panel layout, classes along K); grad_W's B is T
+// when it is k-major, else the staged dL^T.
 template <typename T, int kMode, bool kATr, bool kBTr>
 __global__ __launch_bounds__(kThreads) void k_gemm_grad_x(GemmNT g) {
-  gemm_nt_tile<T, kMode, kATr, kBTr>(g);
+  gemm_nt_tile<T, kMode, kATr, kBTr, true>(g);
 }
 template <typename T, int kMode, bool kATr, bool kBTr>
 __global__ __launch_bounds__(kThreads) void k_gemm_grad_w(GemmNT g) {
-  gemm_nt_tile<T, kMode, kATr, kBTr>(g);
+  gemm_nt_tile<T, kMode, kATr, kBTr, kBTr>(g);
 }
 
 template <typename T, bool kATr, bool kBTr>
@@ -617,10 +639,16 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   // Every split range and K must be whole stages on this path.
   if (g.K % kBK != 0 || g.k_split % kBK != 0) return hipErrorInvalidValue;
+  // B in the panel layout exactly where the kernel expects it.
+  const bool pan = g.role == GemmRole::kGradX || g.b_kmajor;
+  if (pan != (g.b_pstride > 0) || (pan && g.ldb != kTile)) return hipErrorInvalidValue;
+  if (g.role == GemmRole::kGradX && g.b_kmajor) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
-    if (g.a_kmajor && g.b_kmajor) launch_gemm_l<T, true, true>(g, grid, block, s);
+    // both operands k-major doubles the transposing LDS reads per MFMA and
+    // measured slower than staging one of them; it is not built
+    if (g.a_kmajor && g.b_kmajor) return hipErrorInvalidValue;
     else if (g.a_kmajor) launch_gemm_l<T, true, false>(g, grid, block, s);
-    else if (g.b_kmajor) return hipErrorInvalidValue;
+    else if (g.b_kmajor) launch_gemm_l<T, false, true>(g, grid, block, s);
     else launch_gemm_l<T, false, false>(g, grid, block, s);
   } else {
     if (g.a_kmajor || g.b_kmajor) return hipErrorInvalidValue;

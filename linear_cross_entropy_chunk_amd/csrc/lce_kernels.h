@@ -15,6 +15,14 @@ constexpr int kStatCols = 128;
 // Rows per K4 finalize / transpose tile.
 constexpr int kSmallTile = 64;
 
+// Layout of the exp / dL buffer T of a chunk (or of a group of chunks): panels
+// of kTile classes, each panel [R][kTile] with the rows of every chunk of the
+// group back to back; element (n, v) lies at
+//   T + (v / kTile) * pstride + n * kTile + v % kTile,   pstride = R * kTile.
+// A logits tile (kTile classes x kTile rows) is then 128 KiB (bf16) of
+// consecutive memory, and the grad_W GEMM reads the classes of its tile over
+// all rows as one contiguous panel.
+
 enum class EpiMode : int {
   kStoreF32 = 0,     // C = acc                      (fp32 out, e.g. split-K parts)
   kAccumF32 = 1,     // C = C + acc                  (fp32 in/out)
@@ -26,7 +34,7 @@ enum class EpiMode : int {
 // ---- GEMM (lce_gemm.hip) -------------------------------------------------
 // P[m, n] = sum_k A(m, k) B(n, k).  A is stored either [M][lda] with K
 // contiguous, or k-major [K][lda] with M contiguous (a_kmajor, bf16 only);
-// B likewise with N.  Rows of a k-major operand at or past a_krows (b_krows)
+// B likewise with N (not both k-major).  Rows of a k-major operand at or past a_krows (b_krows)
 // read as zero.  The result is stored transposed, C[n * ldc + m] (M a
 // multiple of 4).  K is split into `splits` ranges of k_split elements (a
 // multiple of the stage depth); split s writes C + s * split_stride.
@@ -44,6 +52,9 @@ struct GemmNT {
   GemmRole role;
   bool a_kmajor, b_kmajor;        // operand layouts (see above)
   int a_krows, b_krows;           // valid k rows of a k-major operand
+  // B in the T panel layout (ldb = kTile): the grad_X kernel's B is always
+  // T (classes along K); the grad_W kernel's k-major B is T (classes along N).
+  int64_t b_pstride;
 };
 hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
 
@@ -52,15 +63,16 @@ hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
 // block k of kStatCols classes it writes the block max m_part[k][n], the block
 // sum of exp(z - m_part) s_part[k][n], the lowest class index attaining the
 // block max i_part[k][n] (if i_part != null), z[n, tc[n]] into zt[n]
-// (tc[n] < 0: none), and when T != null, T[n][v] = exp(z[n, v] - m_part[k][n])
-// rounded to the element type, for v < V_pad (0 beyond V).
+// (tc[n] < 0: none), and when T != null, T(n, v) = exp(z[n, v] - m_part[k][n])
+// rounded to the element type, for v < V_pad (0 beyond V), in the panel
+// layout with panel stride tps (T points at the chunk's row 0).
 struct LogitsLse {
   const void* X; int64_t ldx;     // chunk rows [rows][D]
   const void* W; int64_t ldw;     // [V][D]
   const void* bias;               // [V] or null
   const int* tc;                  // [rows]
   int rows, V, D;
-  void* T; int64_t ldt;           // [rows_pad][V_pad] or null
+  void* T; int64_t tps;           // panel layout, or null
   float* m_part; float* s_part; int* i_part; int64_t ldp;   // [V_pad / kStatCols][ldp]
   float* zt;                      // [rows]
 };
@@ -88,11 +100,11 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
                        const float* wrow, int rows, float* lse, float* loss_rows,
                        int* argmax_out, hipStream_t s);
 
-// In-place finalize: T[n][v] <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
-// - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V);
-// optionally writes dLt[v][n] (ld = ldlt) and per-64-row column partials
-// gb_part[n/64][v] (ld = V_pad).
-hipError_t finalize_dlogits(bool bf16, void* T, int64_t ldt, void* dLt, int64_t ldlt,
+// In-place finalize: T(n, v) <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
+// - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V), T
+// in the panel layout with panel stride tps; optionally writes dLt[v][n]
+// (ld = ldlt) and per-64-row column partials gb_part[n/64][v] (ld = V_pad).
+hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t ldlt,
                             const float* m_part, int64_t ldp, const float* lse,
                             const float* g, const int* tc, int rows, int rows_pad,
                             int V, int V_pad, float* gb_part, hipStream_t s);

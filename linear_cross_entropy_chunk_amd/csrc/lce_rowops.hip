@@ -164,10 +164,11 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
 
 // ------------------------------------------------------- in-place finalize
 // 64 rows x 64 classes per workgroup; the 64 classes sit in one statistics
-// block of kStatCols classes.  Writes dL over T, dL^T into dLt, and column partials.
+// block of kStatCols classes and in one panel of T.  Writes dL over T, dL^T
+// into dLt, and column partials.
 template <typename T>
 __global__ __launch_bounds__(256) void k_finalize(
-    T* __restrict__ Tm, int64_t ldt, T* __restrict__ dLt, int64_t ldlt,
+    T* __restrict__ Tm, int64_t tps, T* __restrict__ dLt, int64_t ldlt,
     const float* __restrict__ mp, int64_t ldp, const float* __restrict__ lse,
     const float* __restrict__ g, const int* __restrict__ tc, int rows, int V,
     int64_t ldgb, float* __restrict__ gbp) {
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(256) void k_finalize(
   const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   const int k = v0 / kStatCols;
   const int tid = threadIdx.x;
+  T* const pan = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile;
   if (tid < 64) {
     const int n = n0 + tid;
     const bool in = n < rows;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void k_finalize(
     const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
     const int n = n0 + rl;
     const int vb = v0 + cv * kVec;
-    T* p = Tm + static_cast<int64_t>(n) * ldt + vb;
+    T* p = pan + static_cast<int64_t>(n) * kTile + cv * kVec;
     i32x4_t raw = *reinterpret_cast<const i32x4_t*>(p);
     const T* x = reinterpret_cast<const T*>(&raw);
     i32x4_t outv;
@@ -558,18 +560,18 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
   return hipGetLastError();
 }
 
-hipError_t finalize_dlogits(bool bf16, void* T, int64_t ldt, void* dLt, int64_t ldlt,
+hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t ldlt,
                             const float* m_part, int64_t ldp, const float* lse, const float* g,
                             const int* tc, int rows, int rows_pad, int V, int V_pad,
                             float* gb_part, hipStream_t s) {
   if (rows_pad <= 0) return hipSuccess;
   const dim3 grid(V_pad / 64, rows_pad / 64);
   if (bf16)
-    k_finalize<uint16_t><<<grid, 256, 0, s>>>(static_cast<uint16_t*>(T), ldt,
+    k_finalize<uint16_t><<<grid, 256, 0, s>>>(static_cast<uint16_t*>(T), tps,
                                               static_cast<uint16_t*>(dLt), ldlt, m_part, ldp, lse,
                                               g, tc, rows, V, V_pad, gb_part);
   else
-    k_finalize<float><<<grid, 256, 0, s>>>(static_cast<float*>(T), ldt, static_cast<float*>(dLt),
+    k_finalize<float><<<grid, 256, 0, s>>>(static_cast<float*>(T), tps, static_cast<float*>(dLt),
                                            ldlt, m_part, ldp, lse, g, tc, rows, V, V_pad, gb_part);
   return hipGetLastError();
 }
