@@ -90,8 +90,10 @@ enum {
   LCE_ARGMAX = 8u
 };
 
-/* Special chunk_rows values. */
-#define LCE_CHUNK_ASPECT_RATIO 0   /* next_pow2(ceil(N / ceil(V / D))) rows */
+/* Special chunk_rows values (torch.nn.LinearCrossEntropyOptions page:
+ * chunking_method "aspect_ratio", "aspect_ratio:N", and no chunking). */
+#define LCE_CHUNK_ASPECT_RATIO 0   /* next_pow2(ceil(N / ceil(V / D))) rows,
+                                      divided by chunk_divisor (floor, >= 1) */
 #define LCE_CHUNK_ALL (-1)         /* one chunk of N rows */
 
 /* Problem description, fixed at lce_create.  Enum-typed fields are int32. */
@@ -107,6 +109,8 @@ typedef struct {
   int32_t reduction;     /* lce_reduction */
   int32_t acc_policy;    /* lce_acc_policy */
   uint32_t flags;        /* LCE_GRAD_* | LCE_ARGMAX */
+  int64_t chunk_divisor; /* "aspect_ratio:N" with LCE_CHUNK_ASPECT_RATIO: the
+                            N >= 1 (0 is read as 1); ignored otherwise */
 } lce_desc;
 
 /* Buffers of one call.  All pointers are device pointers. */
@@ -162,11 +166,12 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
 
 /* Enqueue the whole chunked forward+backward on `stream`.
  *
- * Per-row weight g_n (the negated neg_weight_target of the pages):
- *   MEAN: grad_scale / n_valid on counted rows (NaN on every row when
- *         n_valid == 0, so the loss and every gradient are NaN);
- *   SUM:  grad_scale on counted rows;
- *   NONE: grad_output[n] on counted rows (backward only).
+ * Per-row weight g_n (the negated neg_weight_target of the pages), with
+ * w_n = class_weight[t_n] (1 without class weights) on counted rows:
+ *   MEAN: grad_scale w_n / sum of the counted rows' w (NaN on every row when
+ *         that sum is 0, so the loss and every gradient are NaN);
+ *   SUM:  grad_scale w_n;
+ *   NONE: grad_output[n] w_n (backward only).
  * Ignored rows and rows with out-of-range targets have g_n = 0, loss 0 and a
  * zero grad_X row.  With N == 0, MEAN gives a NaN loss, SUM a zero loss, and
  * grad_W / grad_b are filled with zeros.
@@ -179,6 +184,24 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
 LCE_API lce_status lce_forward_backward(lce_handle* h, const lce_io* io,
                                 void* workspace, size_t ws_bytes,
                                 void* stream);
+
+/* out[r][c] = in[r][c] * scale[r * scale_stride] for r < rows, c < cols
+ * (dense row-major, row stride cols), in fp32 and rounded to `dtype` (LCE_F32
+ * or LCE_BF16) to nearest-even; in == out scales in place.  `scale` is a
+ * device pointer, so an upstream gradient never travels to the host:
+ * scale_stride 0 applies one scalar to everything, 1 one value per row.
+ * This is the backward of the ops whose gradients are formed in the forward:
+ * the scalar reductions of the PyTorch module source
+ * torch/nn/modules/linear_cross_entropy.py (stored gradients times the
+ * incoming scalar gradient, in place, or into new buffers when
+ * allow_retain_graph is set) and the in-place cross-entropy of Liger-Kernel
+ * issue #343 (its gradient times the incoming gradient).  in and out 16-byte
+ * aligned; with scale_stride != 0, cols a multiple of 8 (bf16) or 4 (fp32).
+ * Errors: INVALID_ARG (negative sizes or stride, NULL pointer with work to
+ * do), DTYPE, UNSUPPORTED (alignment), HIP. */
+LCE_API lce_status lce_scale(const void* in, void* out, int32_t dtype, int64_t rows,
+                             int64_t cols, const float* scale, int64_t scale_stride,
+                             void* stream);
 
 /* Release the handle (NULL is accepted). */
 LCE_API lce_status lce_destroy(lce_handle* h);

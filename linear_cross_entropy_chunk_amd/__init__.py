@@ -10,3 +10,5 @@ from ._binding import (EXPORTS, LIB_PATH, LceError, lce_ce_inplace,  # noqa: F40
                        lce_workspace_size)
 from .api import (CrossEntropyInplace, LinearCrossEntropy,  # noqa: F401
                   cross_entropy_inplace, linear_cross_entropy)
+from .functional import LinearCrossEntropyOptions  # noqa: F401
+from . import functional  # noqa: F401

@@ -20,7 +20,7 @@ LCE_CHUNK_ASPECT_RATIO, LCE_CHUNK_ALL = 0, -1
 # Every exported function of include/lce.h.
 EXPORTS = ("lce_create", "lce_workspace_size", "lce_chunk_info", "lce_forward_backward",
            "lce_destroy", "lce_ce_workspace_size", "lce_ce_inplace", "lce_timing_enable",
-           "lce_timing_read", "lce_status_string", "lce_last_error")
+           "lce_timing_read", "lce_status_string", "lce_last_error", "lce_scale")
 
 # kernel classes of the timing hook
 KERNEL_CLASSES = ("prep", "logits", "combine", "finalize", "gemm_x", "split_sum", "transpose",
@@ -32,7 +32,7 @@ class lce_desc(ctypes.Structure):
     _fields_ = [("N", c_int64), ("D", c_int64), ("V", c_int64), ("ignore_index", c_int64),
                 ("chunk_rows", c_int64), ("dtype", c_int32), ("acc_dtype", c_int32),
                 ("has_bias", c_int32), ("reduction", c_int32), ("acc_policy", c_int32),
-                ("flags", c_uint32)]
+                ("flags", c_uint32), ("chunk_divisor", c_int64)]
 
 
 class lce_io(ctypes.Structure):
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.lce_ce_inplace.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
                                      c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                      c_void_p]
+        L.lce_scale.argtypes = [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int64,
+                                c_void_p]
         L.lce_timing_enable.argtypes = [c_void_p, c_uint32]
         L.lce_timing_read.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int64)]
         L.lce_status_string.argtypes = [c_int32]
@@ -154,6 +156,13 @@ def lce_ce_inplace(logits: int, targets: int, class_weight: int | None, N: int, 
                                 reduction, grad_scale, c_void_p(loss), c_void_p(n_valid or None),
                                 c_void_p(workspace), ws_bytes, c_void_p(stream)),
            "lce_ce_inplace")
+
+
+def lce_scale(src: int, dst: int, dtype: int, rows: int, cols: int, scale: int,
+              scale_stride: int, stream: int) -> None:
+    _check(lib().lce_scale(c_void_p(src or None), c_void_p(dst or None), dtype, rows, cols,
+                           c_void_p(scale or None), scale_stride, c_void_p(stream)),
+           "lce_scale")
 
 
 def lce_timing_enable(handle, kernel_mask: int) -> None:

@@ -49,7 +49,8 @@ class LinearCrossEntropy:
     def __init__(self, N: int, D: int, V: int, dtype: torch.dtype, *, bias: bool = False,
                  reduction: str = "mean", ignore_index: int = -100, chunk_rows: int = 0,
                  acc_policy: str = "accurate", grad_x: bool = True, grad_w: bool = True,
-                 grad_b: bool | None = None, argmax: bool = False, device="cuda"):
+                 grad_b: bool | None = None, argmax: bool = False, device="cuda",
+                 chunk_divisor: int = 1):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
         grad_b = bias if grad_b is None else grad_b
@@ -64,7 +65,8 @@ class LinearCrossEntropy:
         self.desc = B.lce_desc(N=N, D=D, V=V, ignore_index=ignore_index, chunk_rows=chunk_rows,
                                dtype=_DTYPES[dtype], acc_dtype=B.LCE_F32, has_bias=int(bias),
                                reduction=_REDUCTIONS[reduction],
-                               acc_policy=_POLICIES[acc_policy], flags=flags)
+                               acc_policy=_POLICIES[acc_policy], flags=flags,
+                               chunk_divisor=chunk_divisor)
         self.handle = B.lce_create(self.desc)
         self.ws_bytes = B.lce_workspace_size(self.handle)
         self.chunk_rows, self.n_chunks = B.lce_chunk_info(self.handle)

@@ -95,13 +95,15 @@ int64_t next_pow2(int64_t x) {
 }
 
 // Rows per chunk.  aspect_ratio: the logits buffer (rows, V) holds as many
-// elements as the input (N, D): next_pow2(ceil(N / ceil(V / D))).
+// elements as the input (N, D): next_pow2(ceil(N / ceil(V / D))); the
+// "aspect_ratio:N" form divides that by N (rounded down, at least 1 row).
 int64_t resolve_chunk_rows(const lce_desc& d) {
   if (d.N == 0) return 0;
   int64_t c;
   if (d.chunk_rows > 0) c = d.chunk_rows;
   else if (d.chunk_rows == LCE_CHUNK_ALL) c = d.N;
-  else c = next_pow2(cdiv64(d.N, cdiv64(d.V, d.D)));
+  else c = std::max<int64_t>(1, next_pow2(cdiv64(d.N, cdiv64(d.V, d.D))) /
+                                    std::max<int64_t>(1, d.chunk_divisor));
   return std::min(c, d.N);
 }
 
@@ -205,7 +207,8 @@ const char* lce_last_error(void) { return g_last_error; }
 lce_status lce_create(const lce_desc* d, lce_handle** out) {
   if (!d || !out) return LCE_ERR_INVALID_ARG;
   *out = nullptr;
-  if (d->N < 0 || d->D < 1 || d->V < 1 || d->chunk_rows < LCE_CHUNK_ALL)
+  if (d->N < 0 || d->D < 1 || d->V < 1 || d->chunk_rows < LCE_CHUNK_ALL ||
+      d->chunk_divisor < 0)
     return LCE_ERR_INVALID_ARG;
   if (d->dtype != LCE_F32 && d->dtype != LCE_BF16) return LCE_ERR_DTYPE;
   if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
@@ -452,6 +455,21 @@ lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes) {
   if (!bytes || N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
   const int64_t n = std::max<int64_t>(N, 1);
   *bytes = align_up(n * 4) * 4 + align_up(24);
+  return LCE_OK;
+}
+
+lce_status lce_scale(const void* in, void* out, int32_t dtype, int64_t rows, int64_t cols,
+                     const float* scale, int64_t scale_stride, void* stream) {
+  if (rows < 0 || cols < 0 || scale_stride < 0) return LCE_ERR_INVALID_ARG;
+  if (dtype != LCE_F32 && dtype != LCE_BF16) return LCE_ERR_DTYPE;
+  if (rows == 0 || cols == 0) return LCE_OK;
+  if (!in || !out || !scale) return LCE_ERR_INVALID_ARG;
+  const int64_t vec = dtype == LCE_BF16 ? 8 : 4;
+  if (!aligned16(in) || !aligned16(out) || (scale_stride != 0 && cols % vec != 0))
+    return LCE_ERR_UNSUPPORTED;
+  if (rows > INT64_MAX / cols) return LCE_ERR_INVALID_ARG;
+  LCE_HIP(lce::scale(dtype == LCE_BF16, in, out, rows * cols, scale_stride == 0 ? 0 : cols,
+                     scale, scale_stride, static_cast<hipStream_t>(stream)));
   return LCE_OK;
 }
 

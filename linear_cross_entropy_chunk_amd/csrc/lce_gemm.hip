@@ -266,7 +266,7 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
       const int64_t ld = opb ? ldb : lda;
       const int krows = opb ? b_krows : a_krows;
       const int64_t left = (static_cast<int64_t>(max(krows - k0, 0)) * ld - (opb ? n0 : m0)) * kEs;
-      copy16_to_lds(uniform_rsrc(base + static_cast<int64_t>(k0) * ld, max<int64_t>(left, 0)),
+      copy16_to_lds(uniform_rsrc(base + static_cast<int64_t>(k0) * ld, left > 0 ? left : 0),
                     opb ? vb[j] : va[j], dst);
     } else {
       int o = opb ? vb[j] : va[j];

@@ -129,6 +129,13 @@ hipError_t loss_reduce(const float* loss_rows, int N, const int64_t* counts,
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// out[i] = in[i] * scale[(i / cols) * stride] for i < n (cols == 0: scale[0]
+// everywhere), computed in fp32 and rounded to the element type; in == out
+// allowed.  in and out 16-byte aligned; cols, when not 0, a multiple of the
+// 16-byte vector width.
+hipError_t scale(bool bf16, const void* in, void* out, int64_t n, int64_t cols,
+                 const float* scale, int64_t stride, hipStream_t s);
+
 // Standalone CE: rows of fp32 logits overwritten with g_n (softmax - onehot);
 // loss_rows[n] = w[n] (lse - z_t) (0 if tc < 0; w = wrow[n], 1 when null).
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,

@@ -330,6 +330,30 @@ __global__ void k_fill_zero(i32x4_t* __restrict__ p, int64_t n16, char* __restri
   if (i < tail_bytes) tail[i] = 0;
 }
 
+// ---------------------------------------------------- scaling
+// One 16-byte vector per thread, inside one row when there are rows; the last
+// vector of a length that is not a multiple of the vector width goes element
+// by element.
+template <typename T>
+__global__ __launch_bounds__(256) void k_scale(const T* in, T* out, int64_t n, int64_t cols,
+                                               const float* __restrict__ scale, int64_t stride) {
+  constexpr int kVec = 16 / sizeof(T);
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kVec;
+  if (i >= n) return;
+  const float f = scale[cols ? (i / cols) * stride : 0];
+  if (i + kVec <= n) {
+    i32x4_t raw = *reinterpret_cast<const i32x4_t*>(in + i);
+    const T* x = reinterpret_cast<const T*>(&raw);
+    i32x4_t outv;
+    T* y = reinterpret_cast<T*>(&outv);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) y[e] = from_f32<T>(to_f32(x[e]) * f);
+    *reinterpret_cast<i32x4_t*>(out + i) = outv;
+  } else {
+    for (int64_t k = i; k < n; ++k) out[k] = from_f32<T>(to_f32(in[k]) * f);
+  }
+}
+
 // ---------------------------------------------------- standalone CE
 // One workgroup per row.  Pass 1 streams the row with 16-byte loads keeping
 // an online (max, sum of exp); pass 2 streams it again and overwrites it with
@@ -573,6 +597,21 @@ hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t 
   else
     k_finalize<float><<<grid, 256, 0, s>>>(static_cast<float*>(T), tps, static_cast<float*>(dLt),
                                            ldlt, m_part, ldp, lse, g, tc, rows, V, V_pad, gb_part);
+  return hipGetLastError();
+}
+
+hipError_t scale(bool bf16, const void* in, void* out, int64_t n, int64_t cols,
+                 const float* f, int64_t stride, hipStream_t s) {
+  const int64_t vecs = (n + (bf16 ? 7 : 3)) / (bf16 ? 8 : 4);
+  const int64_t blocks = (vecs + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (bf16)
+    k_scale<uint16_t><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), n, cols, f, stride);
+  else
+    k_scale<float><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        static_cast<const float*>(in), static_cast<float*>(out), n, cols, f, stride);
   return hipGetLastError();
 }
 
