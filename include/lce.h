@@ -82,12 +82,19 @@ typedef enum { LCE_MEAN = 0, LCE_SUM = 1, LCE_NONE = 2 } lce_reduction;
 typedef enum { LCE_ACCURATE = 0, LCE_COMPACT = 1 } lce_acc_policy;
 
 /* Output flags (the pages' compute_input_grad / compute_linear_weight_grad /
- * compute_linear_bias_grad, plus the per-row argmax of the logits). */
+ * compute_linear_bias_grad, plus the per-row argmax of the logits).
+ * LCE_ACCUMULATE adds the gradients to what grad_X / grad_W / grad_b hold
+ * (beta = 1) instead of overwriting them, each element rounded once,
+ * out = round(out + new): the gradient goes straight into its destination
+ * with no separate accumulation pass (Liger-Kernel issue #343, on saving the
+ * gradient into the input's .grad directly).  With N == 0 the buffers are
+ * left as they are. */
 enum {
   LCE_GRAD_X = 1u,
   LCE_GRAD_W = 2u,
   LCE_GRAD_B = 4u,
-  LCE_ARGMAX = 8u
+  LCE_ARGMAX = 8u,
+  LCE_ACCUMULATE = 16u
 };
 
 /* Special chunk_rows values (torch.nn.LinearCrossEntropyOptions page:
@@ -108,7 +115,7 @@ typedef struct {
   int32_t has_bias;      /* 0 or 1 */
   int32_t reduction;     /* lce_reduction */
   int32_t acc_policy;    /* lce_acc_policy */
-  uint32_t flags;        /* LCE_GRAD_* | LCE_ARGMAX */
+  uint32_t flags;        /* LCE_GRAD_* | LCE_ARGMAX | LCE_ACCUMULATE */
   int64_t chunk_divisor; /* "aspect_ratio:N" with LCE_CHUNK_ASPECT_RATIO: the
                             N >= 1 (0 is read as 1); ignored otherwise */
 } lce_desc;

@@ -14,7 +14,7 @@ LCE_OK, LCE_ERR_INVALID_ARG, LCE_ERR_DTYPE, LCE_ERR_UNSUPPORTED, LCE_ERR_WORKSPA
 LCE_F32, LCE_BF16 = 0, 1
 LCE_MEAN, LCE_SUM, LCE_NONE = 0, 1, 2
 LCE_ACCURATE, LCE_COMPACT = 0, 1
-LCE_GRAD_X, LCE_GRAD_W, LCE_GRAD_B, LCE_ARGMAX = 1, 2, 4, 8
+LCE_GRAD_X, LCE_GRAD_W, LCE_GRAD_B, LCE_ARGMAX, LCE_ACCUMULATE = 1, 2, 4, 8, 16
 LCE_CHUNK_ASPECT_RATIO, LCE_CHUNK_ALL = 0, -1
 
 # Every exported function of include/lce.h.

@@ -50,12 +50,14 @@ class LinearCrossEntropy:
                  reduction: str = "mean", ignore_index: int = -100, chunk_rows: int = 0,
                  acc_policy: str = "accurate", grad_x: bool = True, grad_w: bool = True,
                  grad_b: bool | None = None, argmax: bool = False, device="cuda",
-                 chunk_divisor: int = 1):
+                 chunk_divisor: int = 1, accumulate: bool = False):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
         grad_b = bias if grad_b is None else grad_b
         flags = ((B.LCE_GRAD_X if grad_x else 0) | (B.LCE_GRAD_W if grad_w else 0) |
-                 (B.LCE_GRAD_B if grad_b else 0) | (B.LCE_ARGMAX if argmax else 0))
+                 (B.LCE_GRAD_B if grad_b else 0) | (B.LCE_ARGMAX if argmax else 0) |
+                 (B.LCE_ACCUMULATE if accumulate else 0))
+        self.accumulate = accumulate
         self.shape = (N, D, V)
         self.dtype = dtype
         self.bias = bias
@@ -122,6 +124,25 @@ class LinearCrossEntropy:
                                         or tuple(grad_output.shape) != (N,)):
             raise RuntimeError("grad_output must be a float32 tensor of shape (N,)")
 
+    def check_outputs(self, out: dict) -> None:
+        """Caller-supplied outputs: the requested gradients with their shapes."""
+        N, D, V = self.shape
+        want = (("grad_X", B.LCE_GRAD_X, (N, D)), ("grad_W", B.LCE_GRAD_W, (V, D)),
+                ("grad_b", B.LCE_GRAD_B, (V,)))
+        for name, flag, shape in want:
+            if not self.flags & flag:
+                continue
+            g = out.get(name)
+            if (g is None or tuple(g.shape) != shape or g.dtype != self.dtype
+                    or not g.is_contiguous() or g.device != self.device):
+                raise RuntimeError(f"out[{name!r}] must be a contiguous {self.dtype} tensor of "
+                                   f"shape {shape} on {self.device}")
+        for name, n, dt in (("loss", N if self.reduction == "none" else 1, torch.float32),
+                            ("n_valid", 1, torch.int64), ("n_bad", 1, torch.int64)):
+            x = out.get(name)
+            if x is not None and (x.numel() != n or x.dtype != dt or x.device != self.device):
+                raise RuntimeError(f"out[{name!r}] must hold {n} {dt} on {self.device}")
+
     def make_io(self, X, W, t, b=None, *, out: dict, grad_output=None,
                 grad_scale: float = 1.0, class_weight=None) -> B.lce_io:
         return B.lce_io(X=_ptr(X), W=_ptr(W), b=_ptr(b), targets=_ptr(t),
@@ -140,7 +161,15 @@ class LinearCrossEntropy:
         self.check_inputs(X, W, t, b, grad_output, class_weight)
         grads = self.reduction != "none" or grad_output is not None
         if out is None:
+            if self.accumulate and grads:
+                raise ValueError("accumulate adds into existing gradients: pass them in out=")
             out = self.make_outputs(grads)
+        else:
+            full = self.make_outputs(grads=False)   # loss, counts, argmax the caller left out
+            full.update(out)
+            out = full
+            if grads:
+                self.check_outputs(out)
         io = self.make_io(X, W, t, b, out=out, grad_output=grad_output, grad_scale=grad_scale,
                           class_weight=class_weight)
         self.run_io(io)

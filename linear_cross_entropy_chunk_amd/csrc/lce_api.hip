@@ -42,6 +42,7 @@ struct lce_handle {
   int64_t k_grp;      // columns of the dL^T / X^T staging buffers (grp * c_pad)
   int64_t n_groups;
   bool want_x, want_w, want_b, want_argmax, want_any;
+  bool accum;         // add the gradients into the caller's buffers
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
   bool w_inplace;     // grad_W reads dL where it lies in T (bf16 k-major operand)
   int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
@@ -120,6 +121,7 @@ void plan(lce_handle* h) {
   h->want_w = d.flags & LCE_GRAD_W;
   h->want_b = d.flags & LCE_GRAD_B;
   h->want_argmax = d.flags & LCE_ARGMAX;
+  h->accum = d.flags & LCE_ACCUMULATE;
   h->want_any = h->want_x || h->want_w || h->want_b;
 
   // grad_W groups.  The dL^T of `grp` consecutive chunks is staged and one
@@ -214,7 +216,8 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
   if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
   if (d->acc_policy != LCE_ACCURATE && d->acc_policy != LCE_COMPACT) return LCE_ERR_INVALID_ARG;
   if (d->has_bias != 0 && d->has_bias != 1) return LCE_ERR_INVALID_ARG;
-  if (d->flags & ~static_cast<uint32_t>(LCE_GRAD_X | LCE_GRAD_W | LCE_GRAD_B | LCE_ARGMAX))
+  if (d->flags &
+      ~static_cast<uint32_t>(LCE_GRAD_X | LCE_GRAD_W | LCE_GRAD_B | LCE_ARGMAX | LCE_ACCUMULATE))
     return LCE_ERR_INVALID_ARG;
   if ((d->flags & LCE_GRAD_B) && !d->has_bias) return LCE_ERR_INVALID_ARG;
   // Mixed precision is bf16 (or fp32) inputs with an fp32 accumulator only.
@@ -343,8 +346,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                             io->n_bad, s));
 
   if (N == 0) {
-    if (want_w) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_W, static_cast<size_t>(d.V) * d.D * es, s));
-    if (want_b) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_b, static_cast<size_t>(d.V) * es, s));
+    if (want_w && !h->accum) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_W, static_cast<size_t>(d.V) * d.D * es, s));
+    if (want_b && !h->accum) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_b, static_cast<size_t>(d.V) * es, s));
     if (!none) LCE_LAUNCH(h, LCE_K_LOSS, lce::loss_reduce(lrows, 0, cnt, d.reduction, io->loss, s));
     return LCE_OK;
   }
@@ -406,7 +409,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       gx.role = lce::GemmRole::kGradX;
       LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(bf16, gx, s));
       LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(bf16, gxp, h->splits, gx.split_stride, rows, D,
-                              static_cast<char*>(io->grad_X) + row0 * d.D * es, s));
+                              static_cast<char*>(io->grad_X) + row0 * d.D * es, h->accum, s));
     }
     if (want_w) {
       LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, Xc, D, rows, D,
@@ -435,17 +438,20 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         if (h->w_acc32) {
           if (gfirst) { gw.C = gw32; gw.mode = lce::EpiMode::kStoreF32; }
           else if (!glast) { gw.C = gw32; gw.mode = lce::EpiMode::kAccumF32; }
-          else { gw.C = io->grad_W; gw.Cin = gw32; gw.mode = lce::EpiMode::kFinalOut; }
+          else {
+            gw.C = io->grad_W; gw.Cin = gw32;
+            gw.mode = h->accum ? lce::EpiMode::kFinalAccum : lce::EpiMode::kFinalOut;
+          }
         } else {
           gw.C = io->grad_W;
-          gw.mode = gfirst ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
+          gw.mode = gfirst && !h->accum ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
         }
         LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(bf16, gw, s));
       }
     }
     if (want_b)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(bf16, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
-                                    last, s));
+                                    last, h->accum, s));
   }
   if (!none) LCE_LAUNCH(h, LCE_K_LOSS, lce::loss_reduce(lrows, N, cnt, d.reduction, io->loss, s));
   return LCE_OK;

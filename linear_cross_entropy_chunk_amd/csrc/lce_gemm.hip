@@ -446,6 +446,9 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
         store4(static_cast<T*>(g.C) + off, load4(static_cast<const float*>(g.Cin) + off) + v);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
         store4(static_cast<T*>(g.C) + off, v);
+      } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalAccum)) {
+        T* c = static_cast<T*>(g.C) + off;
+        store4(c, load4(c) + (load4(static_cast<const float*>(g.Cin) + off) + v));
       } else {
         T* c = static_cast<T*>(g.C) + off;
         store4(c, load4(c) + v);
@@ -627,6 +630,9 @@ void launch_gemm_l(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
     LCE_GEMM_CASE(kFinalOut)
     LCE_GEMM_CASE(kStoreOut)
     LCE_GEMM_CASE(kAccumOut)
+    case EpiMode::kFinalAccum:   // grad_W only (checked by the caller)
+      k_gemm_grad_w<T, static_cast<int>(EpiMode::kFinalAccum), kATr, kBTr><<<grid, block, 0, s>>>(g);
+      break;
   }
 #undef LCE_GEMM_CASE
 }
@@ -642,7 +648,8 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   // B in the panel layout exactly where the kernel expects it.
   const bool pan = g.role == GemmRole::kGradX || g.b_kmajor;
   if (pan != (g.b_pstride > 0) || (pan && g.ldb != kTile)) return hipErrorInvalidValue;
-  if (g.role == GemmRole::kGradX && g.b_kmajor) return hipErrorInvalidValue;
+  if (g.role == GemmRole::kGradX && (g.b_kmajor || g.mode == EpiMode::kFinalAccum))
+    return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     // both operands k-major doubles the transposing LDS reads per MFMA and
     // measured slower than staging one of them; it is not built

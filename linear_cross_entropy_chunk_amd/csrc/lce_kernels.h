@@ -28,7 +28,8 @@ enum class EpiMode : int {
   kAccumF32 = 1,     // C = C + acc                  (fp32 in/out)
   kFinalOut = 2,     // out = cvt(C_f32 + acc)       (fp32 in, dtype out)
   kStoreOut = 3,     // out = cvt(acc)               (dtype out)
-  kAccumOut = 4      // out = cvt(out + acc)         (dtype in/out)
+  kAccumOut = 4,     // out = cvt(out + acc)         (dtype in/out)
+  kFinalAccum = 5    // out = cvt(out + C_f32 + acc) (fp32 in, dtype in/out; grad_W only)
 };
 
 // ---- GEMM (lce_gemm.hip) -------------------------------------------------
@@ -113,13 +114,15 @@ hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t 
 hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int cols,
                          void* out, int64_t ldo, int rows_pad, hipStream_t s);
 
-// out[r][c] = cvt(sum_s parts[s][r][c]) for r < rows, c < cols (ld = cols).
+// out[r][c] = cvt(sum_s parts[s][r][c] (+ out[r][c] if accum)) for r < rows,
+// c < cols (ld = cols).
 hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride,
-                      int rows, int cols, void* out, hipStream_t s);
+                      int rows, int cols, void* out, bool accum, hipStream_t s);
 
-// acc[v] = (first ? 0 : acc[v]) + sum_b parts[b][v]; if last: out[v] = cvt(acc).
+// acc[v] = (first ? 0 : acc[v]) + sum_b parts[b][v]; if last:
+// out[v] = cvt(acc (+ out[v] if accum)).
 hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp,
-                            int V, float* acc, void* out, bool first, bool last,
+                            int V, float* acc, void* out, bool first, bool last, bool accum,
                             hipStream_t s);
 
 // Final loss: mean (sum / the row-weight sum in counts[2], NaN when 0) or

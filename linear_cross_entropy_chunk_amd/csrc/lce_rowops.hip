@@ -268,15 +268,23 @@ __global__ __launch_bounds__(256) void k_transpose_pad(const T* __restrict__ in,
 template <typename T>
 __global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ parts, int splits,
                                                    int64_t stride, int64_t count4,
-                                                   T* __restrict__ out) {
+                                                   T* __restrict__ out, int accum) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= count4) return;
   f32x4_t acc = reinterpret_cast<const f32x4_t*>(parts)[i];
   for (int s = 1; s < splits; ++s) acc += reinterpret_cast<const f32x4_t*>(parts + s * stride)[i];
   if constexpr (sizeof(T) == 4) {
+    if (accum) acc += reinterpret_cast<const f32x4_t*>(out)[i];
     reinterpret_cast<f32x4_t*>(out)[i] = acc;
   } else {
     uint16_t* o = reinterpret_cast<uint16_t*>(out) + 4 * i;
+    if (accum) {
+      const uint2 old = *reinterpret_cast<const uint2*>(o);
+      acc[0] += to_f32(static_cast<uint16_t>(old.x & 0xffffu));
+      acc[1] += to_f32(static_cast<uint16_t>(old.x >> 16));
+      acc[2] += to_f32(static_cast<uint16_t>(old.y & 0xffffu));
+      acc[3] += to_f32(static_cast<uint16_t>(old.y >> 16));
+    }
     uint2 pk;
     pk.x = static_cast<uint32_t>(from_f32<uint16_t>(acc[0])) |
            (static_cast<uint32_t>(from_f32<uint16_t>(acc[1])) << 16);
@@ -290,12 +298,13 @@ __global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ pa
 template <typename T>
 __global__ __launch_bounds__(256) void k_bias_reduce(const float* __restrict__ parts, int nparts,
                                                     int64_t ldp, int V, float* __restrict__ acc,
-                                                    T* __restrict__ out, int first, int last) {
+                                                    T* __restrict__ out, int first, int last,
+                                                    int accum) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float a = first ? 0.0f : acc[v];
   for (int b = 0; b < nparts; ++b) a += parts[static_cast<int64_t>(b) * ldp + v];
-  if (last) out[v] = from_f32<T>(a);
+  if (last) out[v] = from_f32<T>(accum ? to_f32(out[v]) + a : a);
   else acc[v] = a;
 }
 
@@ -630,28 +639,30 @@ hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int c
 }
 
 hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride, int rows,
-                      int cols, void* out, hipStream_t s) {
+                      int cols, void* out, bool accum, hipStream_t s) {
   const int64_t count4 = static_cast<int64_t>(rows) * cols / 4;
   if (count4 <= 0) return hipSuccess;
   if (bf16_out)
     k_sum_splits<uint16_t><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
-                                                               static_cast<uint16_t*>(out));
+                                                               static_cast<uint16_t*>(out), accum);
   else
     k_sum_splits<float><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
-                                                            static_cast<float*>(out));
+                                                            static_cast<float*>(out), accum);
   return hipGetLastError();
 }
 
 hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp, int V,
-                            float* acc, void* out, bool first, bool last, hipStream_t s) {
+                            float* acc, void* out, bool first, bool last, bool accum,
+                            hipStream_t s) {
   if (V <= 0) return hipSuccess;
   if (bf16_out)
     k_bias_reduce<uint16_t><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
                                                            static_cast<uint16_t*>(out), first,
-                                                           last);
+                                                           last, accum);
   else
     k_bias_reduce<float><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
-                                                        static_cast<float*>(out), first, last);
+                                                        static_cast<float*>(out), first, last,
+                                                        accum);
   return hipGetLastError();
 }
 

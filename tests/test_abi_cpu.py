@@ -86,7 +86,8 @@ def _desc(**kw):
     ({"reduction": 3}, B.LCE_ERR_INVALID_ARG),
     ({"acc_policy": 2}, B.LCE_ERR_INVALID_ARG),
     ({"has_bias": 0}, B.LCE_ERR_INVALID_ARG),            # grad_b requested without bias
-    ({"flags": 16}, B.LCE_ERR_INVALID_ARG),
+    ({"flags": 32}, B.LCE_ERR_INVALID_ARG),
+    ({"flags": B.LCE_GRAD_X | B.LCE_ACCUMULATE}, B.LCE_OK),
     ({"D": 62}, B.LCE_ERR_UNSUPPORTED),                  # fp32 rows not 16-byte aligned
     ({"dtype": B.LCE_BF16, "D": 60}, B.LCE_ERR_UNSUPPORTED),
     ({"dtype": B.LCE_BF16, "D": 64}, B.LCE_OK),
