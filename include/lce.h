@@ -34,8 +34,9 @@
  *     except the logits buffer of lce_ce_inplace, which by contract is
  *     overwritten with the gradient.
  *   - All matrices are dense row-major with the row length as stride.
- *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t).
- *   - Rows of X and W must be 16-byte aligned: D % 8 == 0 for bf16,
+ *   - bf16 tensors are raw bfloat16 bit patterns, fp16 tensors IEEE binary16
+ *     (both uint16_t in memory).
+ *   - Rows of X and W must be 16-byte aligned: D % 8 == 0 for bf16 / fp16,
  *     D % 4 == 0 for fp32 (LCE_ERR_UNSUPPORTED otherwise); base pointers
  *     16-byte aligned.
  */
@@ -63,21 +64,24 @@ typedef struct lce_handle lce_handle;  /* opaque, host memory only */
 typedef enum {
   LCE_OK = 0,
   LCE_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
-  LCE_ERR_DTYPE = 2,        /* dtype not in {LCE_F32, LCE_BF16} */
+  LCE_ERR_DTYPE = 2,        /* dtype not in {LCE_F32, LCE_BF16, LCE_F16} */
   LCE_ERR_UNSUPPORTED = 3,  /* acc_dtype != LCE_F32, unaligned rows, ... */
   LCE_ERR_WORKSPACE = 4,    /* workspace NULL, misaligned or too small */
   LCE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
 } lce_status;
 
-typedef enum { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype;
+/* Element types.  bf16 and fp16 accumulate in fp32 (the pages' mixed
+ * precision with acc_dtype float32); fp16 keeps the logits gradient scaled by
+ * a power of two inside the library so that it stays in fp16's range. */
+typedef enum { LCE_F32 = 0, LCE_BF16 = 1, LCE_F16 = 2 } lce_dtype;
 
 /* Loss reduction (the pages' reduction argument). */
 typedef enum { LCE_MEAN = 0, LCE_SUM = 1, LCE_NONE = 2 } lce_reduction;
 
-/* How grad_W is accumulated across chunks when the input dtype is bf16
- * (the pages' acc_policy).  ACCURATE keeps an fp32 V x D accumulator in the
- * workspace across all chunks and rounds to bf16 once at the end; COMPACT
- * adds each chunk's fp32 tile straight into the bf16 grad_W (one rounding
+/* How grad_W is accumulated across chunks when the input dtype is bf16 or
+ * fp16 (the pages' acc_policy).  ACCURATE keeps an fp32 V x D accumulator in
+ * the workspace across all chunks and rounds once at the end; COMPACT adds
+ * each chunk's fp32 tile straight into the 16-bit grad_W (one rounding
  * per chunk) and needs no V x D accumulator.  Identical for fp32 input. */
 typedef enum { LCE_ACCURATE = 0, LCE_COMPACT = 1 } lce_acc_policy;
 
@@ -159,7 +163,7 @@ typedef struct {
 /* Validate `d`, resolve the chunk size and build a handle.  Host only.
  * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, bad
  * reduction / acc_policy / has_bias, unknown flag bits, NULL pointers),
- * DTYPE, UNSUPPORTED (acc_dtype != LCE_F32; D not a multiple of 8 for bf16
+ * DTYPE, UNSUPPORTED (acc_dtype != LCE_F32; D not a multiple of 8 for bf16 / fp16
  * or 4 for fp32; N, V or D above 2^31 - 1).  LCE_GRAD_B without a bias is
  * INVALID_ARG. */
 LCE_API lce_status lce_create(const lce_desc* d, lce_handle** out);
@@ -193,8 +197,8 @@ LCE_API lce_status lce_forward_backward(lce_handle* h, const lce_io* io,
                                 void* stream);
 
 /* out[r][c] = in[r][c] * scale[r * scale_stride] for r < rows, c < cols
- * (dense row-major, row stride cols), in fp32 and rounded to `dtype` (LCE_F32
- * or LCE_BF16) to nearest-even; in == out scales in place.  `scale` is a
+ * (dense row-major, row stride cols), in fp32 and rounded to `dtype` (LCE_F32,
+ * LCE_BF16 or LCE_F16) to nearest-even; in == out scales in place.  `scale` is a
  * device pointer, so an upstream gradient never travels to the host:
  * scale_stride 0 applies one scalar to everything, 1 one value per row.
  * This is the backward of the ops whose gradients are formed in the forward:
@@ -203,7 +207,7 @@ LCE_API lce_status lce_forward_backward(lce_handle* h, const lce_io* io,
  * incoming scalar gradient, in place, or into new buffers when
  * allow_retain_graph is set) and the in-place cross-entropy of Liger-Kernel
  * issue #343 (its gradient times the incoming gradient).  in and out 16-byte
- * aligned; with scale_stride != 0, cols a multiple of 8 (bf16) or 4 (fp32).
+ * aligned; with scale_stride != 0, cols a multiple of 8 (16-bit) or 4 (fp32).
  * Errors: INVALID_ARG (negative sizes or stride, NULL pointer with work to
  * do), DTYPE, UNSUPPORTED (alignment), HIP. */
 LCE_API lce_status lce_scale(const void* in, void* out, int32_t dtype, int64_t rows,

@@ -11,10 +11,10 @@ parallel threads, and any block can be redrawn on its own.
 Stream keys: 0 X, 1 W, 2 b, 3 targets, 4 ignore-row permutation,
 5 upstream per-row gradient, 6 standalone-CE logits, 7 per-class weights.
 
-bf16 tensors are returned as float32 arrays whose values are exactly
-representable in bf16 (rounded to nearest-even from the float32 draw), so a
-``torch.tensor(...).to(torch.bfloat16)`` upload is exact and an upcast to
-float64 on the CPU is exact as well.
+bf16 and fp16 tensors are returned as float32 arrays whose values are
+exactly representable in that type (rounded to nearest-even from the float32
+draw), so a ``torch.tensor(...).to(torch.bfloat16)`` (or float16) upload is
+exact and an upcast to float64 on the CPU is exact as well.
 """
 from __future__ import annotations
 
@@ -90,14 +90,30 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     return rounded.view(np.float32)
 
 
+def round_to_f16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest IEEE binary16 value (ties to even),
+    returned as float32.  Inputs here are finite and far inside fp16's range."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def _round(vals: np.ndarray, rounding) -> np.ndarray:
+    """rounding: True or "bf16", "f16", or False / None / "f32" (none)."""
+    if rounding is True or rounding == "bf16":
+        return round_to_bf16(vals)
+    if rounding == "f16":
+        return round_to_f16(vals)
+    return vals
+
+
 def _rows_per_block(row_len: int) -> int:
     return max(1, BLOCK_ELEMS // max(1, row_len))
 
 
 def normal_rows(rows: int, cols: int, std: float, seed: int, key: int,
-                bf16: bool, row_start: int = 0, row_stop: int | None = None
+                bf16, row_start: int = 0, row_stop: int | None = None
                 ) -> np.ndarray:
-    """Rows [row_start, row_stop) of a (rows, cols) float32 N(0, std^2) draw.
+    """Rows [row_start, row_stop) of a (rows, cols) float32 N(0, std^2) draw,
+    rounded per ``bf16`` (True or "bf16", "f16", or False for none).
 
     The draw is defined block by block, so a row range gives the same values
     as the corresponding slice of the full tensor."""
@@ -115,8 +131,7 @@ def normal_rows(rows: int, cols: int, std: float, seed: int, key: int,
         vals = rng.standard_normal((b1 - b0) * cols, dtype=np.float32)
         vals = vals.reshape(b1 - b0, cols)
         vals *= np.float32(std)
-        if bf16:
-            vals = round_to_bf16(vals)
+        vals = _round(vals, bf16)
         s0, s1 = max(b0, row_start), min(b1, row_stop)
         out[s0 - row_start:s1 - row_start] = vals[s0 - b0:s1 - b0]
 
@@ -179,10 +194,11 @@ def class_weights(V: int, seed: int, zero_frac: float = 0.0) -> np.ndarray:
 def lce_inputs(cfg: LceConfig, rows: slice | None = None) -> dict:
     """All inputs of a fused workload as numpy arrays.
 
-    X, W, b are float32 arrays (bf16-exact when cfg.dtype == 'bf16'); b is None
-    without bias; t is int64; u (the per-row upstream gradient) is None unless
-    cfg.upstream.  With ``rows`` only those rows of X, t and u are returned."""
-    bf16 = cfg.dtype == "bf16"
+    X, W, b are float32 arrays (exact in cfg.dtype when it is 'bf16' or 'f16');
+    b is None without bias; t is int64; u (the per-row upstream gradient) is
+    None unless cfg.upstream.  With ``rows`` only those rows of X, t and u are
+    returned."""
+    bf16 = cfg.dtype
     r0 = 0 if rows is None else (rows.start or 0)
     r1 = cfg.N if rows is None else (cfg.N if rows.stop is None else rows.stop)
     X = normal_rows(cfg.N, cfg.D, 1.0, cfg.seed, KEY_X, bf16, r0, r1)
@@ -208,8 +224,9 @@ def small_case(N: int, D: int, V: int, *, dtype: str = "f32", bias: bool = True,
                ignore_frac: float = 0.1, seed: int = 0, x_std: float = 1.0,
                w_std: float | None = None, dist: str = "uniform",
                ignore_index: int = IGNORE_INDEX) -> dict:
-    """A small ad-hoc case with the same recipe as the named workloads."""
-    bf16 = dtype == "bf16"
+    """A small ad-hoc case with the same recipe as the named workloads; dtype
+    'f32', 'bf16' or 'f16' fixes the rounding of X, W and b."""
+    bf16 = dtype
     w_std = 1.0 / np.sqrt(max(D, 1)) if w_std is None else w_std
     X = normal_rows(N, D, x_std, seed, KEY_X, bf16) if N else np.zeros((0, D), np.float32)
     W = normal_rows(V, D, w_std, seed, KEY_W, bf16)

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblce.so")
 
 # enums of lce.h
 LCE_OK, LCE_ERR_INVALID_ARG, LCE_ERR_DTYPE, LCE_ERR_UNSUPPORTED, LCE_ERR_WORKSPACE, LCE_ERR_HIP = range(6)
-LCE_F32, LCE_BF16 = 0, 1
+LCE_F32, LCE_BF16, LCE_F16 = 0, 1, 2
 LCE_MEAN, LCE_SUM, LCE_NONE = 0, 1, 2
 LCE_ACCURATE, LCE_COMPACT = 0, 1
 LCE_GRAD_X, LCE_GRAD_W, LCE_GRAD_B, LCE_ARGMAX, LCE_ACCUMULATE = 1, 2, 4, 8, 16

@@ -13,7 +13,7 @@ import torch
 
 from . import _binding as B
 
-_DTYPES = {torch.float32: B.LCE_F32, torch.bfloat16: B.LCE_BF16}
+_DTYPES = {torch.float32: B.LCE_F32, torch.bfloat16: B.LCE_BF16, torch.float16: B.LCE_F16}
 _REDUCTIONS = {"mean": B.LCE_MEAN, "sum": B.LCE_SUM, "none": B.LCE_NONE}
 _POLICIES = {"accurate": B.LCE_ACCURATE, "compact": B.LCE_COMPACT}
 

@@ -29,7 +29,8 @@ struct TimingPool {
 
 struct lce_handle {
   lce_desc d;
-  bool bf16;
+  lce::Elem elem;     // element type of the inputs, gradients and T
+  bool half;          // a 2-byte element type (bf16 or fp16): MFMA on 16-bit operands
   int esize;
   int64_t c;          // rows per chunk
   int64_t n_chunks;
@@ -44,7 +45,7 @@ struct lce_handle {
   bool want_x, want_w, want_b, want_argmax, want_any;
   bool accum;         // add the gradients into the caller's buffers
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
-  bool w_inplace;     // grad_W reads dL where it lies in T (bf16 k-major operand)
+  bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
   int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
@@ -110,8 +111,10 @@ int64_t resolve_chunk_rows(const lce_desc& d) {
 
 void plan(lce_handle* h) {
   const lce_desc& d = h->d;
-  h->bf16 = d.dtype == LCE_BF16;
-  h->esize = h->bf16 ? 2 : 4;
+  h->elem = d.dtype == LCE_BF16 ? lce::Elem::kBF16
+            : d.dtype == LCE_F16 ? lce::Elem::kF16 : lce::Elem::kF32;
+  h->half = h->elem != lce::Elem::kF32;
+  h->esize = lce::elem_size(h->elem);
   h->c = resolve_chunk_rows(d);
   h->n_chunks = h->c ? cdiv64(d.N, h->c) : 0;
   h->c_pad = round_up(std::max<int64_t>(h->c, 1), 64);
@@ -134,13 +137,13 @@ void plan(lce_handle* h) {
   h->grp = std::max<int64_t>(1, std::min<int64_t>(h->grp, std::max<int64_t>(h->n_chunks, 1)));
   h->k_grp = h->grp * h->c_pad;
   h->n_groups = h->n_chunks ? cdiv64(h->n_chunks, h->grp) : 0;
-  h->w_acc32 = h->want_w && h->bf16 && d.acc_policy == LCE_ACCURATE && h->n_groups > 1;
-  // bf16: the chunks of a group keep their dL in T (chunk j at row j c_pad of
+  h->w_acc32 = h->want_w && h->half && d.acc_policy == LCE_ACCURATE && h->n_groups > 1;
+  // 2-byte types: the chunks of a group keep their dL in T (chunk j at row j c_pad of
   // every panel) and grad_W reads it there as a k-major operand, so dL^T is
   // not staged.  This needs the chunks back to back (c a multiple of 64, or
   // one chunk per group) so that T's rows line up with the staged X^T
   // columns.  Otherwise, and for fp32, the finalize stages dL^T.
-  h->w_inplace = h->want_w && h->bf16 && (h->c % 64 == 0 || h->grp == 1);
+  h->w_inplace = h->want_w && h->half && (h->c % 64 == 0 || h->grp == 1);
   h->t_rows = h->w_inplace ? h->k_grp : h->c_pad;
 
   // split-K for grad_X = dL . W: aim at >= 512 workgroups, >= 1024 K per split.
@@ -160,8 +163,8 @@ void plan(lce_handle* h) {
   };
   h->o_T = take(h->t_rows * Vp * es, h->want_any);
   h->o_dLt = take(Vp * h->k_grp * es, h->want_w && !h->w_inplace);
-  // bf16 grad_X reads W in place (k-major operand); fp32 uses a transposed copy
-  h->o_Wt = take(D * Vp * es, h->want_x && !h->bf16);
+  // 2-byte grad_X reads W in place (k-major operand); fp32 uses a transposed copy
+  h->o_Wt = take(D * Vp * es, h->want_x && !h->half);
   h->o_Xt = take(D * h->k_grp * es, h->want_w);
   h->o_mp = take(h->n_vt * c * 4, true);
   h->o_sp = take(h->n_vt * c * 4, true);
@@ -176,7 +179,8 @@ void plan(lce_handle* h) {
   h->o_gb32 = take(Vp * 4, h->want_b);
   h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_wrow = take(std::max<int64_t>(N, 1) * 4, true);
-  h->o_cnt = take(3 * 8, true);       // n_valid, n_bad, row-weight sum (double)
+  // n_valid, n_bad, row-weight sum (double), then the fp16 dL scale 2^k and 2^-k
+  h->o_cnt = take(3 * 8 + 2 * 4, true);
   h->total = o;
 }
 
@@ -212,7 +216,7 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
   if (d->N < 0 || d->D < 1 || d->V < 1 || d->chunk_rows < LCE_CHUNK_ALL ||
       d->chunk_divisor < 0)
     return LCE_ERR_INVALID_ARG;
-  if (d->dtype != LCE_F32 && d->dtype != LCE_BF16) return LCE_ERR_DTYPE;
+  if (d->dtype != LCE_F32 && d->dtype != LCE_BF16 && d->dtype != LCE_F16) return LCE_ERR_DTYPE;
   if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
   if (d->acc_policy != LCE_ACCURATE && d->acc_policy != LCE_COMPACT) return LCE_ERR_INVALID_ARG;
   if (d->has_bias != 0 && d->has_bias != 1) return LCE_ERR_INVALID_ARG;
@@ -220,9 +224,9 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
       ~static_cast<uint32_t>(LCE_GRAD_X | LCE_GRAD_W | LCE_GRAD_B | LCE_ARGMAX | LCE_ACCUMULATE))
     return LCE_ERR_INVALID_ARG;
   if ((d->flags & LCE_GRAD_B) && !d->has_bias) return LCE_ERR_INVALID_ARG;
-  // Mixed precision is bf16 (or fp32) inputs with an fp32 accumulator only.
+  // Mixed precision is bf16 / fp16 (or fp32) inputs with an fp32 accumulator only.
   if (d->acc_dtype != LCE_F32) return LCE_ERR_UNSUPPORTED;
-  const int64_t vec = d->dtype == LCE_BF16 ? 8 : 4;
+  const int64_t vec = d->dtype == LCE_F32 ? 4 : 8;
   if (d->D % vec != 0) return LCE_ERR_UNSUPPORTED;
   const int64_t kMax = 2147483647LL - 1024;
   if (d->N > kMax || d->V > kMax || d->D > kMax) return LCE_ERR_UNSUPPORTED;
@@ -318,7 +322,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     return LCE_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = h->bf16;
+  const lce::Elem el = h->elem;
+  const bool half = h->half;
   const int es = h->esize;
   const int N = static_cast<int>(d.N), D = static_cast<int>(d.D), V = static_cast<int>(d.V);
   const int64_t cp = h->c_pad, Vp = h->V_pad;
@@ -340,10 +345,15 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   float* lrows = at<float>(workspace, h->o_lrows);
   float* wrow = at<float>(workspace, h->o_wrow);
   int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
+  // fp16 keeps dL times a power of two 2^k (from the largest row weight) so
+  // that it stays inside fp16's range; the gradients' element-type stores
+  // multiply by 2^-k.  Exact scalings: no rounding is added.
+  float* dl_scale = h->elem == lce::Elem::kF16 ? reinterpret_cast<float*>(cnt + 3) : nullptr;
+  const float* dl_unscale = dl_scale ? dl_scale + 1 : nullptr;
 
   LCE_LAUNCH(h, LCE_K_PREP, lce::prep_targets(io->targets, N, V, d.ignore_index, d.reduction, io->grad_scale,
                             io->grad_output, io->class_weight, tc, g, wrow, cnt, io->n_valid,
-                            io->n_bad, s));
+                            io->n_bad, dl_scale, s));
 
   if (N == 0) {
     if (want_w && !h->accum) LCE_LAUNCH(h, LCE_K_LOSS, lce::fill_zero(io->grad_W, static_cast<size_t>(d.V) * d.D * es, s));
@@ -352,8 +362,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     return LCE_OK;
   }
 
-  if (want_x && !bf16)
-    LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
+  if (want_x && !half)
+    LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
 
   const char* Xb = static_cast<const char*>(io->X);
   for (int64_t ck = 0; ck < h->n_chunks; ++ck) {
@@ -375,7 +385,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.T = grads ? Tc : nullptr; la.tps = tps;
     la.m_part = mp; la.s_part = sp; la.i_part = h->want_argmax ? ip : nullptr; la.ldp = cp;
     la.zt = zt;
-    LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(bf16, la, s));
+    LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
 
     float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
     LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
@@ -384,17 +394,17 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     if (!grads) continue;
 
     char* dLt_j = dLt ? static_cast<char*>(dLt) + jj * cp * es : nullptr;
-    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(bf16, Tc, tps,
+    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(el, Tc, tps,
                                   want_w && !h->w_inplace ? dLt_j : nullptr,
                                   h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
-                                  V, static_cast<int>(Vp), want_b ? gbp : nullptr, s));
+                                  V, static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale, s));
     if (want_x) {
       // grad_X[rows] = dL . W, with M = D against dL[rows][V] (K = V): the
-      // transposed store writes grad_X rows with contiguous vectors.  bf16
+      // transposed store writes grad_X rows with contiguous vectors.  2-byte types
       // reads W[V][D] itself as a k-major operand (rows past V read as 0);
       // fp32 reads the transposed copy W^T[D][V_pad].
       lce::GemmNT gx{};
-      if (bf16) {
+      if (half) {
         gx.A = io->W; gx.lda = D; gx.a_kmajor = true; gx.a_krows = V;
       } else {
         gx.A = Wt; gx.lda = Vp;
@@ -407,12 +417,13 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       gx.mode = lce::EpiMode::kStoreF32;
       gx.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along rows
       gx.role = lce::GemmRole::kGradX;
-      LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(bf16, gx, s));
-      LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(bf16, gxp, h->splits, gx.split_stride, rows, D,
-                              static_cast<char*>(io->grad_X) + row0 * d.D * es, h->accum, s));
+      LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
+      LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(el, gxp, h->splits, gx.split_stride, rows, D,
+                              static_cast<char*>(io->grad_X) + row0 * d.D * es, h->accum,
+                              dl_unscale, s));
     }
     if (want_w) {
-      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(bf16, Xc, D, rows, D,
+      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xc, D, rows, D,
                                                         static_cast<char*>(Xt) + jj * cp * es,
                                                         h->k_grp, rows_pad, s));
       if (jj + 1 == h->grp || last) {
@@ -446,11 +457,12 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
           gw.C = io->grad_W;
           gw.mode = gfirst && !h->accum ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
         }
-        LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(bf16, gw, s));
+        gw.out_scale = dl_unscale;
+        LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gw, s));
       }
     }
     if (want_b)
-      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(bf16, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
+      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
                                     last, h->accum, s));
   }
   if (!none) LCE_LAUNCH(h, LCE_K_LOSS, lce::loss_reduce(lrows, N, cnt, d.reduction, io->loss, s));
@@ -467,14 +479,16 @@ lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes) {
 lce_status lce_scale(const void* in, void* out, int32_t dtype, int64_t rows, int64_t cols,
                      const float* scale, int64_t scale_stride, void* stream) {
   if (rows < 0 || cols < 0 || scale_stride < 0) return LCE_ERR_INVALID_ARG;
-  if (dtype != LCE_F32 && dtype != LCE_BF16) return LCE_ERR_DTYPE;
+  if (dtype != LCE_F32 && dtype != LCE_BF16 && dtype != LCE_F16) return LCE_ERR_DTYPE;
   if (rows == 0 || cols == 0) return LCE_OK;
   if (!in || !out || !scale) return LCE_ERR_INVALID_ARG;
-  const int64_t vec = dtype == LCE_BF16 ? 8 : 4;
+  const int64_t vec = dtype == LCE_F32 ? 4 : 8;
   if (!aligned16(in) || !aligned16(out) || (scale_stride != 0 && cols % vec != 0))
     return LCE_ERR_UNSUPPORTED;
   if (rows > INT64_MAX / cols) return LCE_ERR_INVALID_ARG;
-  LCE_HIP(lce::scale(dtype == LCE_BF16, in, out, rows * cols, scale_stride == 0 ? 0 : cols,
+  const lce::Elem el = dtype == LCE_BF16 ? lce::Elem::kBF16
+                      : dtype == LCE_F16 ? lce::Elem::kF16 : lce::Elem::kF32;
+  LCE_HIP(lce::scale(el, in, out, rows * cols, scale_stride == 0 ? 0 : cols,
                      scale, scale_stride, static_cast<hipStream_t>(stream)));
   return LCE_OK;
 }
@@ -505,7 +519,7 @@ lce_status lce_ce_inplace(float* logits, const int64_t* targets, const float* cl
   // the weight the 'sum' reduction gives.
   LCE_HIP(lce::prep_targets(targets, static_cast<int>(N), static_cast<int>(V), ignore_index,
                             none ? LCE_SUM : reduction, grad_scale, nullptr, class_weight, tc, g,
-                            wrow, cnt, n_valid, nullptr, s));
+                            wrow, cnt, n_valid, nullptr, nullptr, s));
   LCE_HIP(lce::ce_inplace_rows(logits, static_cast<int>(N), static_cast<int>(V), tc, g,
                                class_weight ? wrow : nullptr, none ? loss : lrows, s));
   if (!none) LCE_HIP(lce::loss_reduce(lrows, static_cast<int>(N), cnt, reduction, loss, s));

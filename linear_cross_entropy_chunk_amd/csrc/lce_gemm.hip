@@ -40,6 +40,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -70,6 +72,7 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 __device__ __forceinline__ float to_f32(float f) { return f; }
+__device__ __forceinline__ float to_f32(_Float16 h) { return static_cast<float>(h); }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -97,8 +100,8 @@ __device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_
 
 // One pair of 16-byte fragments.  Lane l holds row l & 15 of its 16-row
 // block at the logical chunk 4 h + (l >> 4) of sub-step h.
-//   bf16: the chunk is k = 8 (l >> 4) .. + 7 of the sub-step, exactly the
-//         operand of v_mfma_f32_16x16x32_bf16.
+//   bf16 / fp16: the chunk is k = 8 (l >> 4) .. + 7 of the sub-step, exactly
+//         the operand of v_mfma_f32_16x16x32_bf16 / _f16.
 //   fp32: the chunk holds 4 consecutive k; MFMA p takes component p, so lane
 //         group q supplies k = 4 q + p and the four MFMAs cover the 16 k of
 //         the sub-step once, with A and B paired on the same k.
@@ -109,6 +112,12 @@ template <>
 __device__ __forceinline__ void mfma_step<uint16_t>(f32x4_t& acc, i32x4_t a, i32x4_t b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mfma_step<_Float16>(f32x4_t& acc, i32x4_t a, i32x4_t b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                               __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
 }
 
 template <>
@@ -194,7 +203,7 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
                                          int k_begin, int k_end, char* __restrict__ lds,
                                          Acc& acc) {
   static_assert(kI == 8 && kJ == 8 && kWaves == 4 && kCopies == 8, "four waves of 128 x 128");
-  static_assert(!(kATr || kBTr) || sizeof(T) == 2, "k-major operands are bf16 only");
+  static_assert(!(kATr || kBTr) || sizeof(T) == 2, "k-major operands are 2-byte types only");
   static_assert(!(kKTail && (kATr || kBTr)), "k tails apply to K-contiguous operands");
   static_assert(!(kKTail && kBPan), "panels hold whole stages");
   constexpr int kEs = static_cast<int>(sizeof(T));
@@ -378,13 +387,17 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 // ---------------------------------------------------------------- plain GEMM
 // The output is stored transposed, C[n * ldc + m]: lane l holds 4
 // consecutive m (registers 0..3) of column n, so every store (and every load
-// of the accumulate modes) is one 16-byte (fp32) or 8-byte (bf16) vector, and
+// of the accumulate modes) is one 16-byte (fp32) or 8-byte (bf16, fp16) vector, and
 // the four lane groups of a column cover 16 consecutive m.  M must be a
 // multiple of 4.
 template <typename T>
 __device__ __forceinline__ f32x4_t load4(const T* p) {
   if constexpr (sizeof(T) == 4) {
     return *reinterpret_cast<const f32x4_t*>(p);
+  } else if constexpr (std::is_same_v<T, _Float16>) {
+    const f16x4_t v = *reinterpret_cast<const f16x4_t*>(p);
+    return f32x4_t{static_cast<float>(v[0]), static_cast<float>(v[1]),
+                   static_cast<float>(v[2]), static_cast<float>(v[3])};
   } else {
     const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
     return f32x4_t{static_cast<float>(v[0]), static_cast<float>(v[1]),
@@ -396,6 +409,13 @@ template <typename T>
 __device__ __forceinline__ void store4(T* p, f32x4_t v) {
   if constexpr (sizeof(T) == 4) {
     *reinterpret_cast<f32x4_t*>(p) = v;
+  } else if constexpr (std::is_same_v<T, _Float16>) {
+    f16x4_t o;
+    o[0] = static_cast<_Float16>(v[0]);
+    o[1] = static_cast<_Float16>(v[1]);
+    o[2] = static_cast<_Float16>(v[2]);
+    o[3] = static_cast<_Float16>(v[3]);
+    *reinterpret_cast<f16x4_t*>(p) = o;
   } else {
     bf16x4_t o;
     o[0] = static_cast<__bf16>(v[0]);
@@ -427,6 +447,7 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   const int mb = tm * kTile + wm * kWaveM + 4 * (lane >> 4);
   const int nb = tn * kTile + wn * kWaveN + (lane & 15);
   const int64_t ldc = g.ldc;
+  const float osc = g.out_scale ? g.out_scale[0] : 1.0f;   // product scale, element-type stores
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const int n = nb + kBlk * j;
@@ -443,15 +464,16 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
         float* c = static_cast<float*>(g.C) + off;
         store4(c, load4(c) + v);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
-        store4(static_cast<T*>(g.C) + off, load4(static_cast<const float*>(g.Cin) + off) + v);
+        store4(static_cast<T*>(g.C) + off,
+               (load4(static_cast<const float*>(g.Cin) + off) + v) * osc);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
-        store4(static_cast<T*>(g.C) + off, v);
+        store4(static_cast<T*>(g.C) + off, v * osc);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalAccum)) {
         T* c = static_cast<T*>(g.C) + off;
-        store4(c, load4(c) + (load4(static_cast<const float*>(g.Cin) + off) + v));
+        store4(c, load4(c) + (load4(static_cast<const float*>(g.Cin) + off) + v) * osc);
       } else {
         T* c = static_cast<T*>(g.C) + off;
-        store4(c, load4(c) + v);
+        store4(c, load4(c) + v * osc);
       }
     }
   }
@@ -686,12 +708,16 @@ hipError_t launch_logits(const LogitsLse& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s) {
-  return bf16 ? launch_gemm<uint16_t>(g, s) : launch_gemm<float>(g, s);
+hipError_t gemm_nt(Elem e, const GemmNT& g, hipStream_t s) {
+  if (e == Elem::kBF16) return launch_gemm<uint16_t>(g, s);
+  if (e == Elem::kF16) return launch_gemm<_Float16>(g, s);
+  return launch_gemm<float>(g, s);
 }
 
-hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s) {
-  return bf16 ? launch_logits<uint16_t>(a, s) : launch_logits<float>(a, s);
+hipError_t logits_lse(Elem e, const LogitsLse& a, hipStream_t s) {
+  if (e == Elem::kBF16) return launch_logits<uint16_t>(a, s);
+  if (e == Elem::kF16) return launch_logits<_Float16>(a, s);
+  return launch_logits<float>(a, s);
 }
 
 }  // namespace lce

@@ -7,6 +7,11 @@
 
 namespace lce {
 
+// Element type of X, W, b, the gradients and the exp / dL buffer T.  bf16 and
+// fp16 accumulate in fp32.
+enum class Elem : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+inline int elem_size(Elem e) { return e == Elem::kF32 ? 4 : 2; }
+
 // Square output tile of every GEMM launch (rows x cols of C per workgroup).
 constexpr int kTile = 256;
 // Classes per softmax-statistics partial of the logits epilogue (one wave's
@@ -56,8 +61,12 @@ struct GemmNT {
   // B in the T panel layout (ldb = kTile): the grad_X kernel's B is always
   // T (classes along K); the grad_W kernel's k-major B is T (classes along N).
   int64_t b_pstride;
+  // Device scalar that multiplies the product wherever it is written in the
+  // element type (modes kStoreOut, kAccumOut, kFinalOut, kFinalAccum; the
+  // fp32 modes store it unscaled); null means 1.
+  const float* out_scale;
 };
-hipError_t gemm_nt(bool bf16, const GemmNT& g, hipStream_t s);
+hipError_t gemm_nt(Elem e, const GemmNT& g, hipStream_t s);
 
 // Logits GEMM with the fused softmax-statistics epilogue.  Computes, for the
 // chunk's rows n < rows and classes v < V, z[n, v] = X[n] . W[v] + b[v]; per
@@ -77,7 +86,7 @@ struct LogitsLse {
   float* m_part; float* s_part; int* i_part; int64_t ldp;   // [V_pad / kStatCols][ldp]
   float* zt;                      // [rows]
 };
-hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s);
+hipError_t logits_lse(Elem e, const LogitsLse& a, hipStream_t s);
 
 // ---- row-wise kernels (lce_rowops.hip) -------------------------------------
 // Target preparation: counts rows, forms corrected targets and row weights.
@@ -87,11 +96,14 @@ hipError_t logits_lse(bool bf16, const LogitsLse& a, hipStream_t s);
 //   g[n]    = per-row weight of the reduction (see lce.h), built from w
 // counts[0] = n_valid, counts[1] = n_bad (also copied to the optional outs),
 // counts[2] = the bits of the double sum of w (the mean's denominator).
+// dl_scale (if not null): [0] = 2^k with 2^k max_n |g[n]| in [0.5, 1) (1 when
+// every g is 0 or not finite), the factor that keeps dL inside fp16's range;
+// [1] = 2^-k.
 hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index,
                         int reduction, float grad_scale, const float* upstream,
                         const float* class_weight, int* tc, float* g, float* wrow,
                         int64_t* counts, int64_t* n_valid_out, int64_t* n_bad_out,
-                        hipStream_t s);
+                        float* dl_scale, hipStream_t s);
 
 // Row combine over the n_vt statistics blocks of a chunk: lse[n] (chunk-local),
 // loss_rows[n] = w[n] (lse - zt) (0 if tc < 0; w = wrow[n], 1 when wrow is
@@ -105,23 +117,27 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
 // - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V), T
 // in the panel layout with panel stride tps; optionally writes dLt[v][n]
 // (ld = ldlt) and per-64-row column partials gb_part[n/64][v] (ld = V_pad).
-hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t ldlt,
+// dL is stored times dl_scale[0] when dl_scale is not null (the partials are
+// not scaled).
+hipError_t finalize_dlogits(Elem e, void* T, int64_t tps, void* dLt, int64_t ldlt,
                             const float* m_part, int64_t ldp, const float* lse,
                             const float* g, const int* tc, int rows, int rows_pad,
-                            int V, int V_pad, float* gb_part, hipStream_t s);
+                            int V, int V_pad, float* gb_part, const float* dl_scale,
+                            hipStream_t s);
 
 // out[c][r] = r < rows ? in[r][c] : 0 for r < rows_pad, c < cols.
-hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int cols,
+hipError_t transpose_pad(Elem e, const void* in, int64_t ldi, int rows, int cols,
                          void* out, int64_t ldo, int rows_pad, hipStream_t s);
 
-// out[r][c] = cvt(sum_s parts[s][r][c] (+ out[r][c] if accum)) for r < rows,
-// c < cols (ld = cols).
-hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride,
-                      int rows, int cols, void* out, bool accum, hipStream_t s);
+// out[r][c] = cvt(f * sum_s parts[s][r][c] (+ out[r][c] if accum)) for
+// r < rows, c < cols (ld = cols), f = scale[0] (1 when scale is null).
+hipError_t sum_splits(Elem e, const float* parts, int splits, int64_t stride,
+                      int rows, int cols, void* out, bool accum, const float* scale,
+                      hipStream_t s);
 
 // acc[v] = (first ? 0 : acc[v]) + sum_b parts[b][v]; if last:
 // out[v] = cvt(acc (+ out[v] if accum)).
-hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp,
+hipError_t bias_grad_reduce(Elem e, const float* parts, int nparts, int64_t ldp,
                             int V, float* acc, void* out, bool first, bool last, bool accum,
                             hipStream_t s);
 
@@ -136,7 +152,7 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 // everywhere), computed in fp32 and rounded to the element type; in == out
 // allowed.  in and out 16-byte aligned; cols, when not 0, a multiple of the
 // 16-byte vector width.
-hipError_t scale(bool bf16, const void* in, void* out, int64_t n, int64_t cols,
+hipError_t scale(Elem e, const void* in, void* out, int64_t n, int64_t cols,
                  const float* scale, int64_t stride, hipStream_t s);
 
 // Standalone CE: rows of fp32 logits overwritten with g_n (softmax - onehot);

@@ -27,7 +27,11 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 __device__ __forceinline__ float to_f32(float f) { return f; }
+__device__ __forceinline__ float to_f32(_Float16 h) { return static_cast<float>(h); }
 template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float f) {
+  return static_cast<_Float16>(f);
+}
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -47,9 +51,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     const int64_t* __restrict__ t, int N, int V, int64_t ign, int reduction,
     float grad_scale, const float* __restrict__ upstream, const float* __restrict__ cw,
     int* __restrict__ tc, float* __restrict__ g, float* __restrict__ wrow,
-    int64_t* __restrict__ counts, int64_t* n_valid_out, int64_t* n_bad_out) {
+    int64_t* __restrict__ counts, int64_t* n_valid_out, int64_t* n_bad_out,
+    float* __restrict__ dl_scale) {
   __shared__ long long s_valid[kPrepThreads / 64], s_bad[kPrepThreads / 64];
   __shared__ double s_w[kPrepThreads / 64];
+  __shared__ float s_gmax[kPrepThreads / 64];
   __shared__ long long tot[2];
   __shared__ double wtot;
   long long cv = 0, cb = 0;
@@ -96,6 +102,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
   // reduction codes follow lce.h: 0 mean, 1 sum, 2 none
   const bool mean_nan = reduction == 0 && d == 0.0;
   const double gmean = d != 0.0 ? static_cast<double>(grad_scale) / d : 0.0;
+  float gmax = 0.0f;                     // largest finite |g|
   for (int n = threadIdx.x; n < N; n += kPrepThreads) {
     const int64_t x = t[n];
     const bool valid = x != ign && x >= 0 && x < V;
@@ -109,6 +116,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     else if (reduction == 1) gn = grad_scale * wn;
     else gn = (upstream ? upstream[n] : 1.0f) * wn;
     g[n] = gn;
+    if (isfinite(gn)) gmax = fmaxf(gmax, fabsf(gn));
+  }
+  if (dl_scale == nullptr) return;
+  for (int o = 32; o > 0; o >>= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, o));
+  if ((threadIdx.x & 63) == 0) s_gmax[threadIdx.x >> 6] = gmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    for (int k = 0; k < kPrepThreads / 64; ++k) m = fmaxf(m, s_gmax[k]);
+    int e = 0;
+    if (m > 0.0f) frexpf(m, &e);           // m = f 2^e, f in [0.5, 1)
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    dl_scale[0] = m > 0.0f ? ldexpf(1.0f, -e) : 1.0f;
+    dl_scale[1] = m > 0.0f ? ldexpf(1.0f, e) : 1.0f;    // its inverse, exactly
   }
 }
 
@@ -171,7 +192,7 @@ __global__ __launch_bounds__(256) void k_finalize(
     T* __restrict__ Tm, int64_t tps, T* __restrict__ dLt, int64_t ldlt,
     const float* __restrict__ mp, int64_t ldp, const float* __restrict__ lse,
     const float* __restrict__ g, const int* __restrict__ tc, int rows, int V,
-    int64_t ldgb, float* __restrict__ gbp) {
+    int64_t ldgb, float* __restrict__ gbp, const float* __restrict__ dl_scale) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kVecPerRow = 64 / kVec;
   __shared__ float tile[64][65];
@@ -181,6 +202,7 @@ __global__ __launch_bounds__(256) void k_finalize(
   const int k = v0 / kStatCols;
   const int tid = threadIdx.x;
   T* const pan = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile;
+  const float ds = dl_scale ? dl_scale[0] : 1.0f;     // stored dL = ds * dL
   if (tid < 64) {
     const int n = n0 + tid;
     const bool in = n < rows;
@@ -206,7 +228,7 @@ __global__ __launch_bounds__(256) void k_finalize(
       float d = 0.0f;
       if (nin && v < V) d = sc[rl] * to_f32(x[e]) - (v == tt[rl] ? gg[rl] : 0.0f);
       tile[rl][cv * kVec + e] = d;
-      y[e] = from_f32<T>(d);
+      y[e] = from_f32<T>(d * ds);
     }
     *reinterpret_cast<i32x4_t*>(p) = outv;
   }
@@ -221,7 +243,7 @@ __global__ __launch_bounds__(256) void k_finalize(
     for (int e = 0; e < kVec; ++e) {
       const float d = tile[nv * kVec + e][vl];
       part += d;
-      y[e] = from_f32<T>(d);
+      y[e] = from_f32<T>(d * ds);
     }
     if (dLt) *reinterpret_cast<i32x4_t*>(dLt + static_cast<int64_t>(v0 + vl) * ldlt + n0 + nv * kVec) = outv;
     if (gbp) {
@@ -268,29 +290,29 @@ __global__ __launch_bounds__(256) void k_transpose_pad(const T* __restrict__ in,
 template <typename T>
 __global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ parts, int splits,
                                                    int64_t stride, int64_t count4,
-                                                   T* __restrict__ out, int accum) {
+                                                   T* __restrict__ out, int accum,
+                                                   const float* __restrict__ scale) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= count4) return;
   f32x4_t acc = reinterpret_cast<const f32x4_t*>(parts)[i];
   for (int s = 1; s < splits; ++s) acc += reinterpret_cast<const f32x4_t*>(parts + s * stride)[i];
+  if (scale) acc *= scale[0];
   if constexpr (sizeof(T) == 4) {
     if (accum) acc += reinterpret_cast<const f32x4_t*>(out)[i];
     reinterpret_cast<f32x4_t*>(out)[i] = acc;
   } else {
-    uint16_t* o = reinterpret_cast<uint16_t*>(out) + 4 * i;
+    uint2* o = reinterpret_cast<uint2*>(out + 4 * i);
     if (accum) {
-      const uint2 old = *reinterpret_cast<const uint2*>(o);
-      acc[0] += to_f32(static_cast<uint16_t>(old.x & 0xffffu));
-      acc[1] += to_f32(static_cast<uint16_t>(old.x >> 16));
-      acc[2] += to_f32(static_cast<uint16_t>(old.y & 0xffffu));
-      acc[3] += to_f32(static_cast<uint16_t>(old.y >> 16));
+      uint2 old = *o;
+      const T* x = reinterpret_cast<const T*>(&old);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += to_f32(x[e]);
     }
     uint2 pk;
-    pk.x = static_cast<uint32_t>(from_f32<uint16_t>(acc[0])) |
-           (static_cast<uint32_t>(from_f32<uint16_t>(acc[1])) << 16);
-    pk.y = static_cast<uint32_t>(from_f32<uint16_t>(acc[2])) |
-           (static_cast<uint32_t>(from_f32<uint16_t>(acc[3])) << 16);
-    *reinterpret_cast<uint2*>(o) = pk;
+    T* y = reinterpret_cast<T*>(&pk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = from_f32<T>(acc[e]);
+    *o = pk;
   }
 }
 
@@ -578,9 +600,10 @@ inline unsigned cdiv_u(int64_t a, int64_t b) { return static_cast<unsigned>((a +
 hipError_t prep_targets(const int64_t* t, int N, int V, int64_t ignore_index, int reduction,
                         float grad_scale, const float* upstream, const float* class_weight,
                         int* tc, float* g, float* wrow, int64_t* counts, int64_t* n_valid_out,
-                        int64_t* n_bad_out, hipStream_t s) {
+                        int64_t* n_bad_out, float* dl_scale, hipStream_t s) {
   k_prep<<<1, kPrepThreads, 0, s>>>(t, N, V, ignore_index, reduction, grad_scale, upstream,
-                                    class_weight, tc, g, wrow, counts, n_valid_out, n_bad_out);
+                                    class_weight, tc, g, wrow, counts, n_valid_out, n_bad_out,
+                                    dl_scale);
   return hipGetLastError();
 }
 
@@ -593,42 +616,45 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
   return hipGetLastError();
 }
 
-hipError_t finalize_dlogits(bool bf16, void* T, int64_t tps, void* dLt, int64_t ldlt,
+// Instantiate a 2-byte or 4-byte kernel for the element type.
+#define LCE_BY_ELEM(e, KERNEL_CALL)                        \
+  do {                                                     \
+    if ((e) == Elem::kBF16) { using T = uint16_t; KERNEL_CALL; } \
+    else if ((e) == Elem::kF16) { using T = _Float16; KERNEL_CALL; } \
+    else { using T = float; KERNEL_CALL; }                 \
+  } while (0)
+
+hipError_t finalize_dlogits(Elem e, void* Tb, int64_t tps, void* dLt, int64_t ldlt,
                             const float* m_part, int64_t ldp, const float* lse, const float* g,
                             const int* tc, int rows, int rows_pad, int V, int V_pad,
-                            float* gb_part, hipStream_t s) {
+                            float* gb_part, const float* dl_scale, hipStream_t s) {
   if (rows_pad <= 0) return hipSuccess;
   const dim3 grid(V_pad / 64, rows_pad / 64);
-  if (bf16)
-    k_finalize<uint16_t><<<grid, 256, 0, s>>>(static_cast<uint16_t*>(T), tps,
-                                              static_cast<uint16_t*>(dLt), ldlt, m_part, ldp, lse,
-                                              g, tc, rows, V, V_pad, gb_part);
-  else
-    k_finalize<float><<<grid, 256, 0, s>>>(static_cast<float*>(T), tps, static_cast<float*>(dLt),
-                                           ldlt, m_part, ldp, lse, g, tc, rows, V, V_pad, gb_part);
+  LCE_BY_ELEM(e, (k_finalize<T><<<grid, 256, 0, s>>>(static_cast<T*>(Tb), tps,
+                                                    static_cast<T*>(dLt), ldlt, m_part, ldp,
+                                                    lse, g, tc, rows, V, V_pad, gb_part,
+                                                    dl_scale)));
   return hipGetLastError();
 }
 
-hipError_t scale(bool bf16, const void* in, void* out, int64_t n, int64_t cols,
+hipError_t scale(Elem e, const void* in, void* out, int64_t n, int64_t cols,
                  const float* f, int64_t stride, hipStream_t s) {
-  const int64_t vecs = (n + (bf16 ? 7 : 3)) / (bf16 ? 8 : 4);
+  const int vec = 16 / elem_size(e);
+  const int64_t vecs = (n + vec - 1) / vec;
   const int64_t blocks = (vecs + 255) / 256;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (bf16)
-    k_scale<uint16_t><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
-        static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), n, cols, f, stride);
-  else
-    k_scale<float><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
-        static_cast<const float*>(in), static_cast<float*>(out), n, cols, f, stride);
+  LCE_BY_ELEM(e, (k_scale<T><<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+                     static_cast<const T*>(in), static_cast<T*>(out), n, cols, f, stride)));
   return hipGetLastError();
 }
 
-hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int cols, void* out,
+hipError_t transpose_pad(Elem e, const void* in, int64_t ldi, int rows, int cols, void* out,
                          int64_t ldo, int rows_pad, hipStream_t s) {
   if (rows_pad <= 0 || cols <= 0) return hipSuccess;
   const dim3 grid(cdiv_u(cols, 64), cdiv_u(rows_pad, 64));
-  if (bf16)
+  // a bit copy: both 2-byte types go through the uint16_t instance
+  if (elem_size(e) == 2)
     k_transpose_pad<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in), ldi, rows,
                                                    cols, static_cast<uint16_t*>(out), ldo,
                                                    rows_pad);
@@ -638,31 +664,21 @@ hipError_t transpose_pad(bool bf16, const void* in, int64_t ldi, int rows, int c
   return hipGetLastError();
 }
 
-hipError_t sum_splits(bool bf16_out, const float* parts, int splits, int64_t stride, int rows,
-                      int cols, void* out, bool accum, hipStream_t s) {
+hipError_t sum_splits(Elem e, const float* parts, int splits, int64_t stride, int rows,
+                      int cols, void* out, bool accum, const float* scale, hipStream_t s) {
   const int64_t count4 = static_cast<int64_t>(rows) * cols / 4;
   if (count4 <= 0) return hipSuccess;
-  if (bf16_out)
-    k_sum_splits<uint16_t><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
-                                                               static_cast<uint16_t*>(out), accum);
-  else
-    k_sum_splits<float><<<cdiv_u(count4, 256), 256, 0, s>>>(parts, splits, stride, count4,
-                                                            static_cast<float*>(out), accum);
+  LCE_BY_ELEM(e, (k_sum_splits<T><<<cdiv_u(count4, 256), 256, 0, s>>>(
+                     parts, splits, stride, count4, static_cast<T*>(out), accum, scale)));
   return hipGetLastError();
 }
 
-hipError_t bias_grad_reduce(bool bf16_out, const float* parts, int nparts, int64_t ldp, int V,
+hipError_t bias_grad_reduce(Elem e, const float* parts, int nparts, int64_t ldp, int V,
                             float* acc, void* out, bool first, bool last, bool accum,
                             hipStream_t s) {
   if (V <= 0) return hipSuccess;
-  if (bf16_out)
-    k_bias_reduce<uint16_t><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
-                                                           static_cast<uint16_t*>(out), first,
-                                                           last, accum);
-  else
-    k_bias_reduce<float><<<cdiv_u(V, 256), 256, 0, s>>>(parts, nparts, ldp, V, acc,
-                                                        static_cast<float*>(out), first, last,
-                                                        accum);
+  LCE_BY_ELEM(e, (k_bias_reduce<T><<<cdiv_u(V, 256), 256, 0, s>>>(
+                     parts, nparts, ldp, V, acc, static_cast<T*>(out), first, last, accum)));
   return hipGetLastError();
 }
 

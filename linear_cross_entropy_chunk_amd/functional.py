@@ -32,7 +32,7 @@ from torch.autograd.function import once_differentiable
 from . import _binding as B
 from .api import CrossEntropyInplace, LinearCrossEntropy, _stream
 
-_LCE_DTYPE = {torch.float32: B.LCE_F32, torch.bfloat16: B.LCE_BF16}
+_LCE_DTYPE = {torch.float32: B.LCE_F32, torch.bfloat16: B.LCE_BF16, torch.float16: B.LCE_F16}
 
 
 @dataclasses.dataclass(frozen=True)

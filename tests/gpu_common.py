@@ -2,10 +2,15 @@
 path through the C ABI, and compare with the fp64 oracle to the stated
 tolerances.
 
-Tolerances (one per input dtype; bf16 inputs accumulate in fp32):
-  loss            |dL| / |L|                      f32 1e-5   bf16 5e-3
-  per-row loss    max |d loss_n| / max |loss_n|   f32 1e-5   bf16 5e-3
-  each gradient   max |dG| / max |G_ref|          f32 1e-4   bf16 2e-2
+Tolerances (one per input dtype; bf16 and fp16 inputs accumulate in fp32):
+  loss            |dL| / |L|                      f32 1e-5   bf16 5e-3   f16 1e-4
+  per-row loss    max |d loss_n| / max |loss_n|   f32 1e-5   bf16 5e-3   f16 1e-4
+  each gradient   max |dG| / max |G_ref|          f32 1e-4   bf16 2e-2   f16 5e-3
+fp16 (not among the stated bars) is derived from its unit roundoff 2^-11:
+the loss comes from fp32 logits of exact inputs (rounding error ~1e-6, 1e-4
+leaves a wide margin); a gradient carries one fp16 rounding of dL and one of
+the output, together at most ~2 x 2^-11 ~ 1e-3 of max|G| when the target
+term dominates a row, so 5e-3 is about five times that bound.
   n_valid, n_bad  bit-exact
   argmax          bit-exact where the oracle's top-2 gap exceeds
                   1e-4 * max(1, |row max|); elsewhere the GPU's class must
@@ -22,8 +27,9 @@ import torch
 import oracle
 from linear_cross_entropy_chunk_amd import CrossEntropyInplace, LinearCrossEntropy
 
-TOL = {"f32": {"loss": 1e-5, "grad": 1e-4}, "bf16": {"loss": 5e-3, "grad": 2e-2}}
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": {"loss": 1e-5, "grad": 1e-4}, "bf16": {"loss": 5e-3, "grad": 2e-2},
+       "f16": {"loss": 1e-4, "grad": 5e-3}}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 ARGMAX_MARGIN = 1e-4
 
 

@@ -20,18 +20,18 @@ def _dev(a, dt):
 
 def _prefill(shape, scale, dt, seed):
     a = (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
-    return li.round_to_bf16(a) if dt == "bf16" else a
+    return li.round_to_bf16(a) if dt == "bf16" else (li.round_to_f16(a) if dt == "f16" else a)
 
 
 def _check(got, pre, ref, dt, name):
     got = got.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - (pre.astype(np.float64) + ref)).max() / max(np.abs(ref).max(), 1e-30)
-    # bf16: one rounding of a sum about twice the gradient's size
+    # 16-bit types: one rounding of a sum about twice the gradient's size
     bound = TOL[dt]["grad"] * (1.0 if dt == "f32" else 2.0)
     assert err <= bound, f"{name} accumulate error {err:.3e}"
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("policy,chunk", [("accurate", 64), ("compact", 64), ("accurate", 0),
                                           ("accurate", -1)])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
@@ -56,7 +56,7 @@ def test_accumulate_adds_into_existing_gradients(dt, policy, chunk, reduction):
         _check(out[k], pre[k], ref[k], dt, k)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_accumulate_twice_is_twice_the_gradient(dt):
     require_gpu()
     N, D, V = 200, 64, 500

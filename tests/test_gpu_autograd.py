@@ -33,7 +33,7 @@ def _case(dt, seed=31, N=300, D=64, V=777):
     return case, cw
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("reduction", ["mean", "sum"])
 def test_scalar_backward_matches_oracle(dt, reduction):
     require_gpu()

@@ -1,5 +1,5 @@
 """GPU parity of per-class cross-entropy weights against the fp64 oracle: the
-fused path (fp32 and bf16, every reduction, ignored and out-of-range rows,
+fused path (fp32, bf16 and fp16, every reduction, ignored and out-of-range rows,
 classes of weight 0, ragged chunks) and the standalone in-place CE (streamed
 and on-chip rows).  With weights the mean divides by the sum of the counted
 rows' weights; a zero weight sum makes the mean loss and every gradient NaN.
@@ -26,7 +26,7 @@ def _z(case):
     return oracle.logits(case["X"], case["W"], case["b"])
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
 def test_fused_class_weights(dt, reduction):
     """N=333 rows in chunks of 70 (a ragged last chunk), V=777 (a ragged last
@@ -63,7 +63,7 @@ def test_mid_bf16_class_weights():
     log(f"mid-bf16 class weights errors {errs}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_unit_weights_are_bit_identical(dt):
     require_gpu()
     case = li.small_case(200, 64, 500, dtype=dt, seed=22, ignore_frac=0.1)
@@ -75,7 +75,7 @@ def test_unit_weights_are_bit_identical(dt):
             np.testing.assert_array_equal(a[k], b[k], err_msg=f"{reduction} {k}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_zero_total_weight(dt):
     """Every counted row's class weighs 0: the mean loss and every gradient
     are NaN (0/0 on the pages); the sum is 0 with zero gradients."""
@@ -93,7 +93,7 @@ def test_zero_total_weight(dt):
         assert np.all(gs[k] == 0.0), k
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_class_weights_with_ignore_index_in_range_and_bad_targets(dt):
     """ignore_index=7 is a class id; targets 300 and -5 are out of range: both
     kinds of row weigh 0 whatever class_weight holds."""

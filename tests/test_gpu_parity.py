@@ -1,6 +1,6 @@
 """GPU parity of the chunked fused path against the fp64 oracle, element by
 element, at sizes the oracle finishes in seconds: the tiny fp32 and mid bf16
-workloads, every chunk size from 1 row to all rows, ragged vocabularies,
+workloads, fp16 inputs, every chunk size from 1 row to all rows, ragged vocabularies,
 every reduction, the degenerate cases (all rows ignored, no rows, targets out
 of range, ignore_index inside the class range), output subsets, determinism
 and both grad_W accumulation policies."""
@@ -51,7 +51,7 @@ def test_mid_bf16_workload():
     log(f"mid-bf16 errors {errs}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("chunk_rows", [1, 3, 64, 300, -1, 0])
 def test_any_chunk_size_gives_the_unchunked_result(dt, chunk_rows):
     require_gpu()
@@ -61,7 +61,7 @@ def test_any_chunk_size_gives_the_unchunked_result(dt, chunk_rows):
     check_all(gpu, _ref(case), dt, "mean", z=_z(case))
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("V", [1, 2, 7, 255, 257, 1000, 2049])
 def test_ragged_vocab(dt, V):
     require_gpu()
@@ -71,7 +71,7 @@ def test_ragged_vocab(dt, V):
     check_all(gpu, _ref(case), dt, "mean", z=_z(case))
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
 def test_reductions(dt, reduction):
     require_gpu()
@@ -90,7 +90,7 @@ def test_reductions(dt, reduction):
         check_all(gpu, _ref(case, reduction, grad_scale=0.75), dt, reduction, z=_z(case))
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_ignore_index_inside_class_range(dt):
     require_gpu()
     case = li.small_case(200, 64, 50, dtype=dt, seed=9, ignore_frac=0.0)
@@ -102,7 +102,7 @@ def test_ignore_index_inside_class_range(dt):
     assert ign.any() and np.all(gpu["grad_X"][ign] == 0.0)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_all_rows_ignored(dt):
     require_gpu()
     case = li.small_case(100, 32, 300, dtype=dt, seed=11, ignore_frac=1.0)
@@ -117,7 +117,7 @@ def test_all_rows_ignored(dt):
         assert np.all(gs[k] == 0.0), k
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_empty_batch(dt):
     require_gpu()
     case = li.small_case(0, 32, 300, dtype=dt, seed=12)
@@ -129,7 +129,7 @@ def test_empty_batch(dt):
     assert gs["loss"][0] == 0.0
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_out_of_range_targets_are_counted(dt):
     require_gpu()
     case = li.small_case(150, 32, 100, dtype=dt, seed=13, ignore_frac=0.1)
@@ -154,7 +154,7 @@ def test_output_subsets(grads):
         assert (key in gpu) == (flag in grads)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_runs_are_bit_identical(dt):
     require_gpu()
     case = li.small_case(700, 128, 3000, dtype=dt, seed=15)
@@ -197,3 +197,23 @@ def test_row_sums_of_grads_vanish():
     gpu = run_gpu(case, "f32", reduction="sum", chunk_rows=128)
     assert abs(gpu["grad_b"].sum()) <= 1e-4 * np.abs(gpu["grad_b"]).sum()
     assert np.all(np.abs(gpu["grad_W"].sum(0)) <= 1e-4 * np.abs(gpu["grad_W"]).sum(0))
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_f16_small_gradients_keep_their_scale(reduction):
+    """fp16 with N=2048, V=32000: g P ~ 1e-8 lies below fp16's smallest
+    subnormal, so dL is kept scaled by a power of two.  W carries a common
+    offset of 0.25, which makes sum_v P_v W_v, the part of grad_X built from
+    those small entries, as large as the target term: losing them would be an
+    error of order one."""
+    require_gpu()
+    case = li.small_case(2048, 256, 32000, dtype="f16", seed=51, ignore_frac=0.05)
+    case["W"] = li.round_to_f16(case["W"] + np.float32(0.25))
+    up = case["u"] if reduction == "none" else None
+    log(f"f16 scale {reduction}")
+    gpu = run_gpu(case, "f16", reduction=reduction, chunk_rows=512, upstream=up)
+    ref = oracle.linear_cross_entropy(case["X"], case["W"], case["b"], case["t"],
+                                      reduction=reduction, upstream=up)
+    errs = check_all(gpu, ref, "f16", reduction, z=_z(case))
+    log(f"f16 scale errors {errs}")
+

@@ -24,6 +24,20 @@ def test_bf16_rounding_is_exact_and_nearest_even():
     assert abs(r[3] - x[3]) <= abs(x[3]) * 2.0 ** -8
 
 
+def test_f16_rounding_is_exact_and_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -11, 1.0 + 3.0 * 2.0 ** -11, -3.1415926, 1e-3], np.float32)
+    r = li.round_to_f16(x)
+    # every value survives a round trip through binary16 unchanged
+    np.testing.assert_array_equal(r.astype(np.float16).astype(np.float32), r)
+    # 1 + 2^-11 is halfway between 1 and 1 + 2^-10: ties go to the even one (1.0)
+    assert r[1] == 1.0
+    # 1 + 3 * 2^-11 is halfway between 1 + 2^-10 and 1 + 2^-9: even is 1 + 2^-9
+    assert r[2] == np.float32(1.0 + 2.0 ** -9)
+    assert abs(r[3] - x[3]) <= abs(x[3]) * 2.0 ** -11
+    w = li.normal_rows(50, 40, 0.3, 7, li.KEY_W, "f16")
+    np.testing.assert_array_equal(w.astype(np.float16).astype(np.float32), w)
+
+
 def test_ignored_counts_are_exact():
     for cfg, n_ign in ((li.TINY_F32, 26), (li.MID_BF16, 205),
                        (li.LARGE_VOCAB_BF16, 410), (li.NONE_BF16, 0)):
