@@ -57,8 +57,13 @@ def _resolve(opts: LinearCrossEntropyOptions, N: int, D: int, V: int, dtype) -> 
     """Options -> C descriptor fields (chunk_rows, chunk_divisor, acc_policy)."""
     if opts.acc_policy not in ("auto", "accurate", "compact"):
         raise ValueError(f"unknown acc_policy {opts.acc_policy!r}")
-    if opts.acc_dtype not in (None, torch.float32):
-        raise NotImplementedError("only float32 accumulation is supported")
+    acc = opts.acc_dtype
+    if acc is not None and acc != torch.float32:
+        # [LCE]: acc_dtype must equal the input dtype unless a 16-bit input
+        # accumulates in float32; the 16-bit non-mixed layouts are not built
+        if acc != dtype:
+            raise RuntimeError(f"acc_dtype {acc} does not fit input dtype {dtype}")
+        raise NotImplementedError(f"accumulation in {acc} is not supported; use float32")
     policy = "compact" if opts.acc_policy == "auto" else opts.acc_policy
     bcs = opts.batch_chunk_size
     if bcs is not None and (not isinstance(bcs, int) or bcs < 1):

@@ -68,8 +68,13 @@ def test_options_resolution():
         _resolve(LinearCrossEntropyOptions(chunking_method="balanced"), N, D, V, f32)
     with pytest.raises(ValueError):
         _resolve(LinearCrossEntropyOptions(acc_policy="fast"), N, D, V, f32)
-    with pytest.raises(NotImplementedError):
+    # acc_dtype: a mismatch with the input dtype is an error, 16-bit non-mixed
+    # accumulation is not built, float32 is the only accumulator
+    with pytest.raises(RuntimeError):
         _resolve(LinearCrossEntropyOptions(acc_dtype=torch.bfloat16), N, D, V, f32)
+    with pytest.raises(NotImplementedError):
+        _resolve(LinearCrossEntropyOptions(acc_dtype=torch.bfloat16), N, D, V, torch.bfloat16)
+    _resolve(LinearCrossEntropyOptions(acc_dtype=torch.float32), N, D, V, torch.float16)
 
 
 def test_argument_errors_before_any_device_work():
