@@ -217,3 +217,17 @@ def test_f16_small_gradients_keep_their_scale(reduction):
     errs = check_all(gpu, ref, "f16", reduction, z=_z(case))
     log(f"f16 scale errors {errs}")
 
+
+
+@pytest.mark.parametrize("dt,D", [("f32", 516), ("bf16", 520), ("f16", 520)])
+def test_medium_ragged_in_every_dimension(dt, D):
+    """N=1100 in chunks of 300 (a ragged last chunk), D not a multiple of the
+    64-element stage (a K tail in the logits GEMM), V=3001 (a ragged last
+    tile and statistics block), bias, 10% ignored rows: many tiles along every
+    dimension of all three GEMMs."""
+    require_gpu()
+    case = li.small_case(1100, D, 3001, dtype=dt, seed=61, ignore_frac=0.1)
+    log(f"medium ragged dt={dt} D={D}")
+    gpu = run_gpu(case, dt, chunk_rows=300)
+    errs = check_all(gpu, _ref(case), dt, "mean", z=_z(case))
+    log(f"medium ragged errors {errs}")
