@@ -186,15 +186,18 @@ __device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
 // columns are one panel and the descriptor starts at its k-row k0.
 //
 // Per stage s (two sub-steps of 4 chunks, 64 MFMAs per wave each), every wave:
-//   sub-step 0 and the first half of sub-step 1: MFMAs from registers; the
-//     16 LDS reads of sub-step 1 (during sub-step 0); 8 copies of A of stage
-//     s + 2 into slot 2s + 4 mod 5 (the slot B of stage s - 1 left);
+//   sub-step 0 and the first quarter of sub-step 1: MFMAs from registers;
+//     the 16 LDS reads of sub-step 1 (during sub-step 0, one per 4 MFMAs);
+//     8 copies of A of stage s + 2 into slot 2s + 4 mod 5 (the slot B of
+//     stage s - 1 left), one per 8 MFMAs and never in a read's slot;
 //   wait for its copies of stage s + 1 (all but the 8 just issued) and for
 //   its LDS reads; barrier: stage s + 1 is whole and stage s is fully read;
-//   second half of sub-step 1: MFMAs; the 16 LDS reads of sub-step 0 of
-//     stage s + 1; 8 copies of B of stage s + 2 into slot 2s mod 5.
-// A stage's B thus has three quarters of a stage to land and its A about
-// seven quarters.
+//   the rest of sub-step 1: MFMAs; the 16 LDS reads of sub-step 0 of stage
+//     s + 1 (one per 3 MFMAs); 8 copies of B of stage s + 2 into slot 2s mod
+//     5 (one per 6 MFMAs, again in slots of their own).
+// A stage's B thus has most of a stage to land and its A about seven
+// quarters.  An MFMA slot carries at most one read or one copy: a slot with
+// both stretches the gap between two MFMAs past the 16 cycles one takes.
 template <typename T, bool kKTail, bool kATr, bool kBTr, bool kBPan = false>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          int a_krows,
@@ -344,7 +347,7 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 
   // One stage; r5 = s mod 5 is a compile-time constant so every slot index is.
   // The order of MFMAs, LDS reads and copies is pinned with scheduling
-  // barriers: every slot of the MFMA stream carries at most one read and one
+  // barriers: every slot of the MFMA stream carries at most one read or one
   // copy.
   auto stage = [&](auto rc, int kt) {
     constexpr int r5 = decltype(rc)::value;
@@ -355,9 +358,9 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
     constexpr int ca = (2 * r5 + 4) % kSlots, cb = (2 * r5 + 5) % kSlots;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 96; ++t) {          // sub-step 0, first half of sub-step 1
+    for (int t = 0; t < 80; ++t) {          // sub-step 0, first quarter of sub-step 1
       mfma(t >> 6, t & 63);
-      if (t < 64 && t % 8 == 0) copy(s + 2, ca, false, t / 8);
+      if (t < 64 && t % 8 == 2) copy(s + 2, ca, false, t / 8);
       if (t < 64 && t % 4 == 0) read(sa, sb, 1, 1, t / 4);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -365,10 +368,10 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 32; u < 64; ++u) {         // second half of sub-step 1
+    for (int u = 16; u < 64; ++u) {         // rest of sub-step 1
       mfma(1, u);
-      if (u % 4 == 0) copy(s + 2, cb, true, (u - 32) / 4);
-      if (u % 2 == 0) read(na, nb, 0, 0, (u - 32) / 2);
+      if ((u - 16) % 6 == 1) copy(s + 2, cb, true, (u - 17) / 6);
+      if ((u - 16) % 3 == 0) read(na, nb, 0, 0, (u - 16) / 3);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -638,13 +641,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_grad_w(GemmNT g) {
   gemm_nt_tile<T, kMode, kATr, kBTr, kBTr>(g);
 }
 
-template <typename T, bool kATr, bool kBTr>
-void launch_gemm_l(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
-  const bool wgrad = g.role == GemmRole::kGradW;
-#define LCE_GEMM_CASE(mode)                                                                    \
-  case EpiMode::mode:                                                                          \
-    if (wgrad) k_gemm_grad_w<T, static_cast<int>(EpiMode::mode), kATr, kBTr><<<grid, block, 0, s>>>(g); \
-    else k_gemm_grad_x<T, static_cast<int>(EpiMode::mode), kATr, kBTr><<<grid, block, 0, s>>>(g);       \
+// grad_W: every epilogue mode, B either the staged dL^T or T's panels (k-major).
+template <typename T, bool kBTr>
+void launch_grad_w(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
+#define LCE_GEMM_CASE(mode)                                                                  \
+  case EpiMode::mode:                                                                        \
+    k_gemm_grad_w<T, static_cast<int>(EpiMode::mode), false, kBTr><<<grid, block, 0, s>>>(g); \
     break;
   switch (g.mode) {
     LCE_GEMM_CASE(kStoreF32)
@@ -652,13 +654,16 @@ void launch_gemm_l(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
     LCE_GEMM_CASE(kFinalOut)
     LCE_GEMM_CASE(kStoreOut)
     LCE_GEMM_CASE(kAccumOut)
-    case EpiMode::kFinalAccum:   // grad_W only (checked by the caller)
-      k_gemm_grad_w<T, static_cast<int>(EpiMode::kFinalAccum), kATr, kBTr><<<grid, block, 0, s>>>(g);
-      break;
+    LCE_GEMM_CASE(kFinalAccum)
   }
 #undef LCE_GEMM_CASE
 }
 
+// The layouts and modes the path uses, and no others:
+//   grad_X: fp32 split partials (kStoreF32); A = W^T staged (fp32) or W read
+//           k-major in place (16-bit types); B = T's panels, K-contiguous.
+//   grad_W: any mode; A = X^T staged; B = the staged dL^T, or (16-bit types)
+//           T's panels read k-major.
 template <typename T>
 hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   const int tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile) * g.splits;
@@ -670,19 +675,30 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   // B in the panel layout exactly where the kernel expects it.
   const bool pan = g.role == GemmRole::kGradX || g.b_kmajor;
   if (pan != (g.b_pstride > 0) || (pan && g.ldb != kTile)) return hipErrorInvalidValue;
-  if (g.role == GemmRole::kGradX && (g.b_kmajor || g.mode == EpiMode::kFinalAccum))
-    return hipErrorInvalidValue;
-  if constexpr (sizeof(T) == 2) {
-    // both operands k-major doubles the transposing LDS reads per MFMA and
-    // measured slower than staging one of them; it is not built
-    if (g.a_kmajor && g.b_kmajor) return hipErrorInvalidValue;
-    else if (g.a_kmajor) launch_gemm_l<T, true, false>(g, grid, block, s);
-    else if (g.b_kmajor) launch_gemm_l<T, false, true>(g, grid, block, s);
-    else launch_gemm_l<T, false, false>(g, grid, block, s);
-  } else {
-    if (g.a_kmajor || g.b_kmajor) return hipErrorInvalidValue;
-    launch_gemm_l<T, false, false>(g, grid, block, s);
+  constexpr bool k16 = sizeof(T) == 2;
+  if (g.role == GemmRole::kGradX) {
+    if (g.b_kmajor || g.mode != EpiMode::kStoreF32 || (g.a_kmajor && !k16))
+      return hipErrorInvalidValue;
+    if constexpr (k16) {
+      if (g.a_kmajor) {
+        k_gemm_grad_x<T, static_cast<int>(EpiMode::kStoreF32), true, false>
+            <<<grid, block, 0, s>>>(g);
+        return hipGetLastError();
+      }
+    }
+    k_gemm_grad_x<T, static_cast<int>(EpiMode::kStoreF32), false, false><<<grid, block, 0, s>>>(g);
+    return hipGetLastError();
   }
+  // grad_W.  Both operands k-major doubles the transposing LDS reads per MFMA
+  // and measured slower than staging one of them; it is not built.
+  if (g.a_kmajor || (g.b_kmajor && !k16)) return hipErrorInvalidValue;
+  if constexpr (k16) {
+    if (g.b_kmajor) {
+      launch_grad_w<T, true>(g, grid, block, s);
+      return hipGetLastError();
+    }
+  }
+  launch_grad_w<T, false>(g, grid, block, s);
   return hipGetLastError();
 }
 
