@@ -258,36 +258,47 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
     return __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, range, 0x00020000);
   };
-  auto copy = [&](int st, int slot, bool opb, int j) {
+  // Where the copies of one operand of one stage read: a descriptor and a
+  // scalar offset, fixed for the stage.  They are formed in an MFMA slot of
+  // their own ahead of the stage's first copy, so that no copy slot carries
+  // the address arithmetic (a 64-bit product and clamps for the k-major and
+  // panel operands).
+  struct Src {
+    __amdgpu_buffer_rsrc_t rs;
+    int soff;
+    int k0;
+  };
+  auto src_of = [&](int st, bool opb) -> Src {
     const int k0 = k_begin + min(st, nk - 1) * kBK;   // stages past the end repeat the last
-    const uint32_t dst = lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024);
     const bool tr = opb ? kBTr : kATr;
     if (kBPan && opb && !kBTr) {
       // the tile's rows of panel k0 / kTile; rows past N read as zero
       const T* base = B + (k0 / kTile) * b_ps + static_cast<int64_t>(n0) * kTile;
       const int64_t bytes = static_cast<int64_t>(min(N - n0, kTile)) * kTile * kEs;
-      copy16_to_lds(uniform_rsrc(base, bytes), vb[j], dst,
-                    __builtin_amdgcn_readfirstlane((k0 % kTile) * kEs));
+      return Src{uniform_rsrc(base, bytes), __builtin_amdgcn_readfirstlane((k0 % kTile) * kEs),
+                 k0};
     } else if (kBPan && opb) {
       // k-major panel of the tile's columns: k-rows from k0 to b_krows
       const T* base = B + (n0 / kTile) * b_ps + static_cast<int64_t>(k0) * kTile;
       const int64_t bytes = static_cast<int64_t>(max(b_krows - k0, 0)) * kTile * kEs;
-      copy16_to_lds(uniform_rsrc(base, bytes), vb[j], dst);
+      return Src{uniform_rsrc(base, bytes), 0, k0};
     } else if (tr) {
       const T* base = opb ? B + n0 : A + m0;
       const int64_t ld = opb ? ldb : lda;
       const int krows = opb ? b_krows : a_krows;
       const int64_t left = (static_cast<int64_t>(max(krows - k0, 0)) * ld - (opb ? n0 : m0)) * kEs;
-      copy16_to_lds(uniform_rsrc(base + static_cast<int64_t>(k0) * ld, left > 0 ? left : 0),
-                    opb ? vb[j] : va[j], dst);
-    } else {
-      int o = opb ? vb[j] : va[j];
-      if constexpr (kKTail) {
-        const int row = 8 * (kCopies * wave + j) + (lane >> 3);
-        o = (k0 + ((lane & 7) ^ swz(row)) * kVec) < k_end ? o : kOutOfRange;
-      }
-      copy16_to_lds(opb ? rb : ra, o, dst, __builtin_amdgcn_readfirstlane(k0 * kEs));
+      return Src{uniform_rsrc(base + static_cast<int64_t>(k0) * ld, left > 0 ? left : 0), 0, k0};
     }
+    return Src{opb ? rb : ra, __builtin_amdgcn_readfirstlane(k0 * kEs), k0};
+  };
+  auto copy = [&](const Src& src, int slot, bool opb, int j) {
+    const uint32_t dst = lds_addr(lds + slot * kSlotBytes + (kCopies * wave + j) * 1024);
+    int o = opb ? vb[j] : va[j];
+    if constexpr (kKTail) {                   // K-contiguous operands only
+      const int row = 8 * (kCopies * wave + j) + (lane >> 3);
+      o = (src.k0 + ((lane & 7) ^ swz(row)) * kVec) < k_end ? o : kOutOfRange;
+    }
+    copy16_to_lds(src.rs, o, dst, src.soff);
   };
 
   // Fragment reads of a K-contiguous operand: lane l reads row (l & 15) of
@@ -336,10 +347,16 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
   };
 
   // Prologue: stages 0 and 1 whole (slots 0-3), stage 0 landed.
+  {
+    const Src a0 = src_of(0, false), b0 = src_of(0, true);
 #pragma unroll
-  for (int j = 0; j < kCopies; ++j) { copy(0, 0, false, j); copy(0, 1, true, j); }
+    for (int j = 0; j < kCopies; ++j) { copy(a0, 0, false, j); copy(b0, 1, true, j); }
+    const Src a1 = src_of(1, false), b1 = src_of(1, true);
 #pragma unroll
-  for (int j = 0; j < kCopies; ++j) { copy(1, 2, false, j); copy(1, 3, true, j); }
+    for (int j = 0; j < kCopies; ++j) { copy(a1, 2, false, j); copy(b1, 3, true, j); }
+  }
+  // the sources of stage s + 2's copies, formed a few slots ahead of them
+  Src src_a = src_of(2, false), src_b = src_of(2, true);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
   __syncthreads();
 #pragma unroll
@@ -360,8 +377,9 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 #pragma unroll
     for (int t = 0; t < 80; ++t) {          // sub-step 0, first quarter of sub-step 1
       mfma(t >> 6, t & 63);
-      if (t < 64 && t % 8 == 2) copy(s + 2, ca, false, t / 8);
+      if (t < 64 && t % 8 == 2) copy(src_a, ca, false, t / 8);
       if (t < 64 && t % 4 == 0) read(sa, sb, 1, 1, t / 4);
+      if (t == 5) src_b = src_of(s + 2, true);             // an empty slot
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies) & ~0x0f00);   // vmcnt(8) lgkmcnt(0)
@@ -370,8 +388,9 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
 #pragma unroll
     for (int u = 16; u < 64; ++u) {         // rest of sub-step 1
       mfma(1, u);
-      if ((u - 16) % 6 == 1) copy(s + 2, cb, true, (u - 17) / 6);
+      if ((u - 16) % 6 == 1) copy(src_b, cb, true, (u - 17) / 6);
       if ((u - 16) % 3 == 0) read(na, nb, 0, 0, (u - 16) / 3);
+      if (u == 20) src_a = src_of(s + 3, false);           // an empty slot: next stage's A
       __builtin_amdgcn_sched_barrier(0);
     }
   };
