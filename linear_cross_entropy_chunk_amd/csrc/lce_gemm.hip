@@ -593,24 +593,35 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     //    classes: in-lane, then over the four lane groups of the column.
     float mx = -INFINITY;
     int mi = 0x7fffffff;
+    if constexpr (kArgmax) {
 #pragma unroll
-    for (int i = 0; i < kI; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float z = acc[i][j][r];
-        if (z > mx) {
-          mx = z;
-          if constexpr (kArgmax) mi = vlane + kBlk * i + r;
+        for (int r = 0; r < 4; ++r) {
+          const float z = acc[i][j][r];
+          if (z > mx) {
+            mx = z;
+            mi = vlane + kBlk * i + r;
+          }
+        }
+#pragma unroll
+      for (int sh = 16; sh <= 32; sh <<= 1) {
+        const float om = __shfl_xor(mx, sh);
+        const int oi = __shfl_xor(mi, sh);
+        if (om > mx || (om == mx && oi < mi)) {
+          mx = om;
+          mi = oi;
         }
       }
+    } else {
+      // max alone: fmaxf (NaN-skipping, as the comparison above) maps to
+      // three-input maxima instead of a compare and a select per element
 #pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-      const float om = __shfl_xor(mx, sh);
-      const int oi = __shfl_xor(mi, sh);
-      if (om > mx || (om == mx && oi < mi)) {
-        mx = om;
-        mi = oi;
-      }
+      for (int i = 0; i < kI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
     }
 
     // 4. e = exp(z - block max) in place, column sums.  A block wholly past
@@ -621,7 +632,8 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // (z - max) first: the maximum maps to exactly 1.
+        // (z - max) first: the maximum maps to exactly 1 (a one-class row has
+        // loss exactly 0), which a fused z log2(e) - max log2(e) would not give
         const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - ref) * kLog2e);
         acc[i][j][r] = e;
         sum += e;
