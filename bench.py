@@ -17,6 +17,7 @@ fp64 CPU oracle timed on a bounded row sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -27,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused LCE fwd+bwd tokens/sec and TFLOP/s (6NVD) at N=8192,D=4096,V=128256 bf16"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_16BIT_TFLOPS = 2500.0     # MI355X dense bf16 / fp16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -95,8 +96,13 @@ def bench_lce(args) -> dict:
     from linear_cross_entropy_chunk_amd import _binding as B
 
     cfg = li.LCE_CONFIGS[args.workload]
+    label = cfg.name
+    if args.dtype is not None and args.dtype != cfg.dtype:
+        # the same workload with its inputs rounded to another input type
+        cfg = dataclasses.replace(cfg, dtype=args.dtype)
+        label = f"{cfg.name} with {cfg.dtype} inputs"
     chunk = cfg.chunk_rows if args.chunk_rows is None else args.chunk_rows
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cfg.dtype]
     log(f"generating {cfg.name}: N={cfg.N} D={cfg.D} V={cfg.V}")
     inputs = li.lce_inputs(cfg)
     dev = torch.device("cuda", 0)
@@ -136,9 +142,6 @@ def bench_lce(args) -> dict:
     log(f"{ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
 
     N, D, V = cfg.N, cfg.D, cfg.V
-    # Algorithmic work per launch of each GEMM class: 2 * rows * V * D flops
-    # (a chunk of `c` rows per launch; grad_X runs split-K as one launch).
-    flops_per_launch = 2.0 * op.chunk_rows * V * D
     per_kernel = {}
     for name, (ms, n) in timing.items():
         if n:
@@ -149,10 +152,14 @@ def bench_lce(args) -> dict:
     dom = max((n for n in ("logits", "gemm_x", "gemm_w") if n in per_kernel),
               key=lambda n: per_kernel[n]["ms_total"])
     avg_s = per_kernel[dom]["avg_ms"] / 1e3
-    # The last chunk may be ragged; its share of the flops is exact when the
-    # chunk size divides N (as in the named workloads).
+    # Each GEMM class does 2*N*V*D flops per step: logits and grad_X one chunk
+    # of rows per launch (2*c*V*D), grad_W one group of chunks per launch
+    # (2*c*group*V*D).  Per launch that is the step's flops over the launches
+    # per step (an average when the last chunk is ragged).
+    launches_per_step = per_kernel[dom]["launches"] / args.steps
+    flops_per_launch = 2.0 * N * V * D / launches_per_step
     achieved = flops_per_launch / avg_s / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_16BIT_TFLOPS
     tokens_s = N / (ms_step / 1e3)
     tflops = 6.0 * N * V * D / (ms_step / 1e3) / 1e12
     result = {
@@ -160,15 +167,15 @@ def bench_lce(args) -> dict:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded numpy, the workload's distributions)",
-        "config": {"workload": f"{cfg.name} N={N} D={D} V={V} chunk_rows={op.chunk_rows} "
+        "config": {"workload": f"{label} N={N} D={D} V={V} chunk_rows={op.chunk_rows} "
                                f"reduction={cfg.reduction} acc_fp32 {args.acc_policy}",
                    "N": N, "D": D, "V": V, "chunk_rows": op.chunk_rows,
                    "acc_policy": args.acc_policy, "parallelism": "single GPU"},
         "tflops": tflops,
-        "frac_of_bf16_peak": tflops / peak,
+        "frac_of_peak": tflops / peak,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": load_traffic(dom, cfg.name),
+                     "traffic": load_traffic(dom, cfg.name) if label == cfg.name else None,
                      "avg_launch_ms": per_kernel[dom]["avg_ms"],
                      "flops_per_launch": flops_per_launch},
         "kernels": {k: round(v["ms_total"] / args.steps, 4) for k, v in per_kernel.items()},
@@ -176,7 +183,7 @@ def bench_lce(args) -> dict:
     if not args.no_cpu_baseline:
         rows = args.cpu_rows
         log(f"cpu baseline: oracle on {rows} rows")
-        result["cpu_baseline"] = cpu_baseline_lce(inputs, rows, cfg.name)
+        result["cpu_baseline"] = cpu_baseline_lce(inputs, rows, label)
         log(f"cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
     return result
 
@@ -324,6 +331,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large-vocab-bf16",
                     choices=["tiny-f32", "mid-bf16", "large-vocab-bf16", "none-bf16", "ce-f32"])
+    ap.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"],
+                    help="round the workload's inputs to this type instead of its own")
     ap.add_argument("--acc-policy", default="accurate", choices=["accurate", "compact"])
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--cpu-rows", type=int, default=4096)

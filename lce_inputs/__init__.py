@@ -39,7 +39,7 @@ class LceConfig:
     N: int
     D: int
     V: int
-    dtype: str                  # "f32" or "bf16"
+    dtype: str                  # "f32", "bf16" or "f16"
     has_bias: bool
     targets: str                # "uniform" or "zipf1.1"
     ignore_frac: float          # exact count = round(frac * N) rows
