@@ -4,12 +4,14 @@ outputs: per-row loss, argmax and grad_X on sampled rows (each depends on its
 row only), grad_W / grad_b on sampled classes (sums over every row, so the
 oracle walks all rows in blocks), and the mean loss over all rows; plus
 properties that hold at any size (every dL row sums to zero)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import lce_inputs as li
-from gpu_common import TOL, check_argmax, log, oracle, rel_err, require_gpu
+from gpu_common import TOL, TORCH_DT, check_argmax, log, oracle, rel_err, require_gpu
 from linear_cross_entropy_chunk_amd import CrossEntropyInplace, LinearCrossEntropy
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +40,7 @@ def _sample_cols(V, t, k=24, seed=1):
 
 
 def _run_fused(cfg, inputs, upstream=None, reduction=None):
-    dt = torch.bfloat16
+    dt = TORCH_DT[cfg.dtype]
     dev = torch.device("cuda", 0)
     X = torch.from_numpy(inputs["X"]).to(dev).to(dt)
     W = torch.from_numpy(inputs["W"]).to(dev).to(dt)
@@ -87,12 +89,14 @@ def _check_rows(gpu, inputs, rows, g, W64, tol, key_loss="loss_rows"):
 
 
 @pytest.mark.timeout(900)
-def test_large_vocab_full_size():
-    """N=8192, D=4096, V=128256 bf16, Zipf targets, 410 ignored, mean,
-    2048-row chunks, fp32 grad_W accumulation (the benchmark's launch)."""
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_large_vocab_full_size(dt):
+    """N=8192, D=4096, V=128256, Zipf targets, 410 ignored, mean, 2048-row
+    chunks, fp32 grad_W accumulation: the benchmark's launch with bf16 inputs,
+    and the same workload with its inputs rounded to fp16 or kept in fp32."""
     require_gpu()
-    cfg = li.LARGE_VOCAB_BF16
-    log(f"{cfg.name}: generating inputs")
+    cfg = dataclasses.replace(li.LARGE_VOCAB_BF16, dtype=dt)
+    log(f"{cfg.name} with {dt} inputs: generating inputs")
     inputs = li.lce_inputs(cfg)
     gpu = _run_fused(cfg, inputs)
     assert gpu["chunk_rows"] == 2048
@@ -101,7 +105,7 @@ def test_large_vocab_full_size():
     assert int(gpu["n_valid"][0]) == nv == cfg.N - 410 and int(gpu["n_bad"][0]) == nb == 0
     g = oracle.row_weights(valid, "mean")
     W64 = inputs["W"].astype(np.float64)
-    tol = TOL["bf16"]
+    tol = TOL[dt]
     rows = _sample_rows(cfg.N, inputs["t"])
     _, e_gx, near = _check_rows(gpu, inputs, rows, g, W64, tol)
     ign = inputs["t"] == -100
@@ -137,7 +141,7 @@ def test_none_reduction_full_size():
     assert int(bwd["n_valid"][0]) == nv == cfg.N
     g = oracle.row_weights(valid, "none", upstream=inputs["u"])
     W64 = inputs["W"].astype(np.float64)
-    tol = TOL["bf16"]
+    tol = TOL[dt]
     rows = _sample_rows(cfg.N, inputs["t"])
     r, e_gx, near = _check_rows(bwd, inputs, rows, g, W64, tol)
     e_lr = rel_err(fwd["loss"][rows], r["loss_rows"])
