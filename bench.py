@@ -140,6 +140,24 @@ def bench_lce(args) -> dict:
     B.lce_timing_enable(op.handle, 0)
     loss = float(out["loss"].cpu()[0]) if cfg.reduction != "none" else float("nan")
     log(f"{ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
+    eager_ms = ms_step
+    if args.graph:
+        # One call captured into a HIP graph and replayed: the same kernels
+        # without the host's per-launch cost (the per-kernel figures and the
+        # roofline come from the eager steps above).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            op.run_io(io)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / args.steps
+        log(f"graph replay: {ms_step:.3f} ms/step (eager {eager_ms:.3f})")
 
     N, D, V = cfg.N, cfg.D, cfg.V
     per_kernel = {}
@@ -180,6 +198,9 @@ def bench_lce(args) -> dict:
                      "flops_per_launch": flops_per_launch},
         "kernels": {k: round(v["ms_total"] / args.steps, 4) for k, v in per_kernel.items()},
     }
+    if args.graph:
+        result["graph"] = True
+        result["eager_ms_per_step"] = eager_ms
     if not args.no_cpu_baseline:
         rows = args.cpu_rows
         log(f"cpu baseline: oracle on {rows} rows")
@@ -333,6 +354,8 @@ def main() -> int:
                     choices=["tiny-f32", "mid-bf16", "large-vocab-bf16", "none-bf16", "ce-f32"])
     ap.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"],
                     help="round the workload's inputs to this type instead of its own")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one call captured into a HIP graph")
     ap.add_argument("--acc-policy", default="accurate", choices=["accurate", "compact"])
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--cpu-rows", type=int, default=4096)
