@@ -1,0 +1,86 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the HBM-traffic summary
+built from two rocprofv3 counter CSVs scaled by the calibration copy, and the
+rule that traffic taken on other kernel sources is not reported."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _write_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+@pytest.fixture
+def traffic_file(tmp_path, monkeypatch):
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    return path
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path, traffic_file):
+    gib_kib = (1 << 30) / 1024
+    # the copy moves 1 GiB each way; FETCH_SIZE reads half of it, WRITE_SIZE all
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _write_csv(fetch, "FETCH_SIZE", [
+        ("copyBuffer(...)", gib_kib / 2),
+        ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1000.0),
+        ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1200.0),
+        ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1100.0),
+        ("void lce::k_gemm_grad_w<...>(...)", 50.0),
+        ("some_other_kernel", 9e9),
+    ])
+    _write_csv(write, "WRITE_SIZE", [
+        ("copyBuffer(...)", gib_kib),
+        ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 300.0),
+        ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 300.0),
+        ("void lce::k_gemm_grad_w<...>(...)", 7.0),
+    ])
+    out = bench.summarize_counters(str(fetch), str(write), "w1", "cmd")
+    assert set(out) == {"logits", "gemm_w"}
+    lg = out["logits"]
+    assert lg["copy_scale_fetch"] == pytest.approx(2.0)
+    assert lg["copy_scale_write"] == pytest.approx(1.0)
+    assert lg["read_bytes"] == pytest.approx(1100.0 * 2.0 * 1024)     # the median dispatch
+    assert lg["write_bytes"] == pytest.approx(300.0 * 1024)
+    assert lg["bytes_per_launch"] == pytest.approx(lg["read_bytes"] + lg["write_bytes"])
+    assert json.loads(traffic_file.read_text())["w1"]["gemm_w"]["command"] == "cmd"
+    assert bench.load_traffic("logits", "w1") == pytest.approx(lg["bytes_per_launch"])
+    assert bench.load_traffic("gemm_x", "w1") is None
+    assert bench.load_traffic("logits", "other") is None
+
+
+def test_traffic_of_other_kernel_sources_is_not_reported(tmp_path, traffic_file, monkeypatch):
+    traffic_file.write_text(json.dumps(
+        {"w1": {"logits": {"bytes_per_launch": 5.0, "source_sha": bench.kernel_source_sha()}}}))
+    assert bench.load_traffic("logits", "w1") == 5.0
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
+    assert bench.load_traffic("logits", "w1") is None
+
+
+def test_no_copy_calibration_means_no_traffic(tmp_path, traffic_file):
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _write_csv(fetch, "FETCH_SIZE", [("k_logits_lse", 10.0)])
+    _write_csv(write, "WRITE_SIZE", [("k_logits_lse", 10.0)])
+    assert bench.summarize_counters(str(fetch), str(write), "w1", "cmd") == {}
