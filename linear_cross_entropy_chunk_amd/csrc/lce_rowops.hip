@@ -136,8 +136,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 // ------------------------------------------------------------ row combine
 // kCombRows rows x kCombParts parts per workgroup; part p folds statistics
 // blocks p, p + kCombParts, ... of its row (an online max / rescaled sum),
-// then part 0 merges the parts in a fixed order.
-constexpr int kCombRows = 8, kCombParts = 32;
+// then part 0 merges the parts in a fixed order.  The loads of kCombBatch
+// consecutive blocks of a part are issued before any is folded, so a thread
+// waits on memory once per batch rather than once per block (the fold order,
+// and so the result, is the same).
+constexpr int kCombRows = 8, kCombParts = 32, kCombBatch = 4;
 __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
@@ -150,15 +153,24 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
   float m = -INFINITY, s = 0.0f;
   int kb = 0x7fffffff;
   if (n < rows) {
-    for (int k = p; k < n_vt; k += kCombParts) {
-      const float mk = mp[k * ldp + n];
-      const float sk_ = sp[k * ldp + n];
-      if (mk > m) {
-        s = s * expf(m - mk) + sk_;
-        m = mk;
-        kb = k;
-      } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
-        s += sk_ * expf(mk - m);
+    for (int k0 = p; k0 < n_vt; k0 += kCombBatch * kCombParts) {
+      float mb[kCombBatch], sb[kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const int k = k0 + u * kCombParts;
+        mb[u] = k < n_vt ? mp[k * ldp + n] : -INFINITY;
+        sb[u] = k < n_vt ? sp[k * ldp + n] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const float mk = mb[u];
+        if (mk > m) {
+          s = s * expf(m - mk) + sb[u];
+          m = mk;
+          kb = k0 + u * kCombParts;
+        } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
+          s += sb[u] * expf(mk - m);
+        }
       }
     }
   }
