@@ -210,11 +210,24 @@ __global__ __launch_bounds__(256) void k_finalize(
   __shared__ float tile[64][65];
   __shared__ float sc[64], gg[64];
   __shared__ int tt[64];
+  constexpr int kPer = 64 * kVecPerRow / 256;          // vectors per thread
   const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   const int k = v0 / kStatCols;
   const int tid = threadIdx.x;
   T* const pan = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile;
   const float ds = dl_scale ? dl_scale[0] : 1.0f;     // stored dL = ds * dL
+  // The thread's vectors of T are loaded first, so that their latency
+  // overlaps the row scales' loads below.  T has room for all 64 rows of
+  // the workgroup (the chunk's rows rounded up to 64); rows past the chunk
+  // are rewritten as 0.
+  i32x4_t raw[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = tid + 256 * u;
+    const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
+    raw[u] = *reinterpret_cast<const i32x4_t*>(pan + static_cast<int64_t>(n0 + rl) * kTile +
+                                               cv * kVec);
+  }
   if (tid < 64) {
     const int n = n0 + tid;
     const bool in = n < rows;
@@ -224,13 +237,14 @@ __global__ __launch_bounds__(256) void k_finalize(
     tt[tid] = in ? tc[n] : -1;
   }
   __syncthreads();
-  for (int idx = tid; idx < 64 * kVecPerRow; idx += 256) {
+  const bool stage = dLt != nullptr || gbp != nullptr;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = tid + 256 * u;
     const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
     const int n = n0 + rl;
     const int vb = v0 + cv * kVec;
-    T* p = pan + static_cast<int64_t>(n) * kTile + cv * kVec;
-    i32x4_t raw = *reinterpret_cast<const i32x4_t*>(p);
-    const T* x = reinterpret_cast<const T*>(&raw);
+    const T* x = reinterpret_cast<const T*>(&raw[u]);
     i32x4_t outv;
     T* y = reinterpret_cast<T*>(&outv);
     const bool nin = n < rows;
@@ -239,10 +253,10 @@ __global__ __launch_bounds__(256) void k_finalize(
       const int v = vb + e;
       float d = 0.0f;
       if (nin && v < V) d = sc[rl] * to_f32(x[e]) - (v == tt[rl] ? gg[rl] : 0.0f);
-      tile[rl][cv * kVec + e] = d;
+      if (stage) tile[rl][cv * kVec + e] = d;
       y[e] = from_f32<T>(d * ds);
     }
-    *reinterpret_cast<i32x4_t*>(p) = outv;
+    *reinterpret_cast<i32x4_t*>(pan + static_cast<int64_t>(n) * kTile + cv * kVec) = outv;
   }
   if (dLt == nullptr && gbp == nullptr) return;
   __syncthreads();
