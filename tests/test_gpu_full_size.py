@@ -105,7 +105,7 @@ def test_large_vocab_full_size(dt):
     assert int(gpu["n_valid"][0]) == nv == cfg.N - 410 and int(gpu["n_bad"][0]) == nb == 0
     g = oracle.row_weights(valid, "mean")
     W64 = inputs["W"].astype(np.float64)
-    tol = TOL[dt]
+    tol = TOL[cfg.dtype]
     rows = _sample_rows(cfg.N, inputs["t"])
     _, e_gx, near = _check_rows(gpu, inputs, rows, g, W64, tol)
     ign = inputs["t"] == -100
@@ -141,7 +141,7 @@ def test_none_reduction_full_size():
     assert int(bwd["n_valid"][0]) == nv == cfg.N
     g = oracle.row_weights(valid, "none", upstream=inputs["u"])
     W64 = inputs["W"].astype(np.float64)
-    tol = TOL[dt]
+    tol = TOL[cfg.dtype]
     rows = _sample_rows(cfg.N, inputs["t"])
     r, e_gx, near = _check_rows(bwd, inputs, rows, g, W64, tol)
     e_lr = rel_err(fwd["loss"][rows], r["loss_rows"])
