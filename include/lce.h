@@ -39,6 +39,10 @@
  *   - Rows of X and W must be 16-byte aligned: D % 8 == 0 for bf16 / fp16,
  *     D % 4 == 0 for fp32 (LCE_ERR_UNSUPPORTED otherwise); base pointers
  *     16-byte aligned.
+ *   - Size limits of lce_create (LCE_ERR_UNSUPPORTED otherwise): N, V and D
+ *     below 2^31 - 1024; D <= 2^20 and rows per chunk <= 2^20; fp32 inputs
+ *     that request grad_X also need V <= 2^21 - 256.  (The GEMMs address a
+ *     256-row operand tile with 32-bit offsets.)
  */
 #ifndef LCE_H
 #define LCE_H

@@ -232,10 +232,20 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
   if (d->D % vec != 0) return LCE_ERR_UNSUPPORTED;
   const int64_t kMax = 2147483647LL - 1024;
   if (d->N > kMax || d->V > kMax || d->D > kMax) return LCE_ERR_UNSUPPORTED;
+  // The GEMMs address the rows of a 256-row operand tile with 32-bit byte
+  // offsets, so each operand's row length (D; the chunk and group rows for
+  // the staged X^T / dL^T; V_pad for fp32's W^T) times 256 rows must stay
+  // below 2 GiB.  These limits keep every one at or below 1 GiB.
+  constexpr int64_t kMaxRowLen = int64_t{1} << 20;
+  if (d->D > kMaxRowLen) return LCE_ERR_UNSUPPORTED;
   lce_handle* h = new (std::nothrow) lce_handle();
   if (!h) return LCE_ERR_INVALID_ARG;
   h->d = *d;
   plan(h);
+  if (h->c > kMaxRowLen || (!h->half && h->want_x && h->V_pad >= 2 * kMaxRowLen)) {
+    delete h;
+    return LCE_ERR_UNSUPPORTED;
+  }
   *out = h;
   return LCE_OK;
 }

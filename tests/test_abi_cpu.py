@@ -93,6 +93,16 @@ def _desc(**kw):
     ({"dtype": B.LCE_BF16, "D": 64}, B.LCE_OK),
     ({"N": 0}, B.LCE_OK),
     ({"N": 1 << 32}, B.LCE_ERR_UNSUPPORTED),
+    # 32-bit offsets inside a 256-row operand tile: row lengths up to 2^20
+    ({"dtype": B.LCE_BF16, "D": 1 << 20}, B.LCE_OK),
+    ({"dtype": B.LCE_BF16, "D": (1 << 20) + 8}, B.LCE_ERR_UNSUPPORTED),
+    ({"N": 1 << 21, "chunk_rows": 1 << 20}, B.LCE_OK),
+    ({"N": 1 << 21, "chunk_rows": (1 << 20) + 1}, B.LCE_ERR_UNSUPPORTED),
+    ({"N": 1 << 21, "chunk_rows": B.LCE_CHUNK_ALL}, B.LCE_ERR_UNSUPPORTED),
+    ({"V": (1 << 21) - 256}, B.LCE_OK),                 # fp32 W^T for grad_X
+    ({"V": (1 << 21) - 255}, B.LCE_ERR_UNSUPPORTED),
+    ({"V": (1 << 21) - 255, "flags": B.LCE_GRAD_W | B.LCE_GRAD_B}, B.LCE_OK),
+    ({"V": 1 << 22, "dtype": B.LCE_BF16}, B.LCE_OK),    # 16-bit grad_X reads W in place
 ])
 def test_create_validation(lib, kw, status):
     assert B.lce_create_status(_desc(**kw)) == status
