@@ -697,9 +697,11 @@ void launch_grad_w(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
 //           T's panels read k-major.
 template <typename T>
 hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
-  const int tiles = ((g.M + kTile - 1) / kTile) * ((g.N + kTile - 1) / kTile) * g.splits;
+  const int64_t tiles = static_cast<int64_t>((g.M + kTile - 1) / kTile) *
+                        ((g.N + kTile - 1) / kTile) * g.splits;
   if (tiles <= 0) return hipSuccess;
-  const dim3 grid(tiles), block(kThreads);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;     // workgroup ids are int
+  const dim3 grid(static_cast<uint32_t>(tiles)), block(kThreads);
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   // Every split range and K must be whole stages on this path.
   if (g.K % kBK != 0 || g.k_split % kBK != 0) return hipErrorInvalidValue;
@@ -744,9 +746,11 @@ void launch_logits_k(const LogitsLse& a, dim3 grid, dim3 block, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_logits(const LogitsLse& a, hipStream_t s) {
-  const int tiles = ((a.V + kTile - 1) / kTile) * ((a.rows + kTile - 1) / kTile);
+  const int64_t tiles = static_cast<int64_t>((a.V + kTile - 1) / kTile) *
+                        ((a.rows + kTile - 1) / kTile);
   if (tiles <= 0) return hipSuccess;
-  const dim3 grid(tiles), block(kThreads);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;     // workgroup ids are int
+  const dim3 grid(static_cast<uint32_t>(tiles)), block(kThreads);
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   if (a.D % kBK == 0) launch_logits_k<T, false>(a, grid, block, s);
   else launch_logits_k<T, true>(a, grid, block, s);
