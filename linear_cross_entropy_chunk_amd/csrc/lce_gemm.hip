@@ -554,6 +554,9 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     for (int jj = j + 1; jj < kJ; ++jj)
 #pragma unroll
       for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
+    // A block wholly past the chunk's rows (a short or ragged last chunk)
+    // has nothing to store, and neither have the blocks after it.
+    if (tn * kTile + wn * kWaveN + kBlk * j >= a.rows) break;   // uniform
     const int n = nbase + kBlk * j;         // chunk row
     const bool nin = n < a.rows;
 
