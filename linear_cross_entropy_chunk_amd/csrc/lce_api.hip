@@ -146,11 +146,13 @@ void plan(lce_handle* h) {
   h->w_inplace = h->want_w && h->half && (h->c % 64 == 0 || h->grp == 1);
   h->t_rows = h->w_inplace ? h->k_grp : h->c_pad;
 
-  // split-K for grad_X = dL . W: aim at >= 512 workgroups, >= 64 K per split
-  // (one stage; a small problem would otherwise leave a few workgroups
-  // walking all of K through mostly empty 256 x 256 tiles).
+  // split-K for grad_X = dL . W: aim at one workgroup per CU (256; two
+  // rounds of 512 measured slower: more partials to sum, twice the tile
+  // starts), >= 64 K per split (one stage; a small problem would otherwise
+  // leave a few workgroups walking all of K through mostly empty 256 x 256
+  // tiles).
   const int64_t tiles = cdiv64(h->c, lce::kTile) * cdiv64(d.D, lce::kTile);
-  int64_t splits = std::max<int64_t>(1, cdiv64(512, std::max<int64_t>(tiles, 1)));
+  int64_t splits = std::max<int64_t>(1, cdiv64(256, std::max<int64_t>(tiles, 1)));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, h->V_pad / 64));
   int64_t ks = round_up(cdiv64(h->V_pad, splits), 64);
   h->splits = static_cast<int>(cdiv64(h->V_pad, ks));
