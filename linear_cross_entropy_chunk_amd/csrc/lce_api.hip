@@ -46,6 +46,8 @@ struct lce_handle {
   bool accum;         // add the gradients into the caller's buffers
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
   bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
+  bool gx_group;      // one grad_X GEMM per grad_W group (its rows all in T)
+  int64_t gx_rows;    // most rows of one grad_X GEMM
   int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
@@ -151,7 +153,11 @@ void plan(lce_handle* h) {
   // starts), >= 64 K per split (one stage; a small problem would otherwise
   // leave a few workgroups walking all of K through mostly empty 256 x 256
   // tiles).
-  const int64_t tiles = cdiv64(h->c, lce::kTile) * cdiv64(d.D, lce::kTile);
+  // With the group's dL in T, grad_X runs once per group over all its rows
+  // (fewer, larger launches; one split needs no partials and no split sum).
+  h->gx_group = h->want_x && h->w_inplace;
+  h->gx_rows = h->gx_group ? std::min<int64_t>(h->grp * h->c, d.N) : h->c;
+  const int64_t tiles = cdiv64(h->gx_rows, lce::kTile) * cdiv64(d.D, lce::kTile);
   int64_t splits = std::max<int64_t>(1, cdiv64(256, std::max<int64_t>(tiles, 1)));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, h->V_pad / 64));
   int64_t ks = round_up(cdiv64(h->V_pad, splits), 64);
@@ -177,7 +183,8 @@ void plan(lce_handle* h) {
   h->o_lse = take(c * 4, true);
   h->o_g = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_tc = take(std::max<int64_t>(N, 1) * 4, true);
-  h->o_gxp = take(static_cast<size_t>(h->splits) * c * D * 4, h->want_x);
+  h->o_gxp = take(static_cast<size_t>(h->splits) * round_up(h->gx_rows, 64) * D * 4,
+                  h->want_x && !(h->gx_group && h->splits == 1));
   h->o_gw32 = take(V * D * 4, h->w_acc32);
   h->o_gbp = take((c / 64) * Vp * 4, h->want_b);
   h->o_gb32 = take(Vp * 4, h->want_b);
@@ -379,6 +386,43 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   if (want_x && !half)
     LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
 
+  // grad_X[xrow0 .. + nrows) = dL . W for dL rows held in T from Tb on, with
+  // M = D against dL[rows][V] (K = V): the transposed store writes grad_X
+  // rows with contiguous vectors.  2-byte types read W[V][D] itself as a
+  // k-major operand (rows past V read as 0); fp32 reads the transposed copy
+  // W^T[D][V_pad].  With one split (2-byte types) the GEMM writes grad_X
+  // itself; otherwise fp32 split partials are summed into it.
+  auto grad_x = [&](void* Tb, int64_t xrow0, int nrows) -> lce_status {
+    const int64_t tps = h->t_rows * lce::kTile;
+    lce::GemmNT gx{};
+    if (half) {
+      gx.A = io->W; gx.lda = D; gx.a_kmajor = true; gx.a_krows = V;
+    } else {
+      gx.A = Wt; gx.lda = Vp;
+    }
+    gx.B = Tb; gx.ldb = lce::kTile; gx.b_pstride = tps;
+    gx.M = D; gx.N = nrows; gx.K = static_cast<int>(Vp);
+    gx.splits = h->splits; gx.k_split = h->k_split;
+    gx.split_stride = static_cast<int64_t>(nrows) * D;
+    gx.ldc = D; gx.Cin = nullptr;
+    gx.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along rows
+    gx.role = lce::GemmRole::kGradX;
+    char* out = static_cast<char*>(io->grad_X) + xrow0 * d.D * es;
+    if (half && h->splits == 1) {
+      gx.C = out;
+      gx.mode = h->accum ? lce::EpiMode::kAccumOut : lce::EpiMode::kStoreOut;
+      gx.out_scale = dl_unscale;
+      LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
+      return LCE_OK;
+    }
+    gx.C = gxp;
+    gx.mode = lce::EpiMode::kStoreF32;
+    LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
+    LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(el, gxp, h->splits, gx.split_stride, nrows, D,
+                                                   out, h->accum, dl_unscale, s));
+    return LCE_OK;
+  };
+
   const char* Xb = static_cast<const char*>(io->X);
   for (int64_t ck = 0; ck < h->n_chunks; ++ck) {
     const int64_t row0 = ck * h->c;
@@ -412,35 +456,21 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                                   want_w && !h->w_inplace ? dLt_j : nullptr,
                                   h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
                                   V, static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale, s));
-    if (want_x) {
-      // grad_X[rows] = dL . W, with M = D against dL[rows][V] (K = V): the
-      // transposed store writes grad_X rows with contiguous vectors.  2-byte types
-      // reads W[V][D] itself as a k-major operand (rows past V read as 0);
-      // fp32 reads the transposed copy W^T[D][V_pad].
-      lce::GemmNT gx{};
-      if (half) {
-        gx.A = io->W; gx.lda = D; gx.a_kmajor = true; gx.a_krows = V;
-      } else {
-        gx.A = Wt; gx.lda = Vp;
-      }
-      gx.B = Tc; gx.ldb = lce::kTile; gx.b_pstride = tps;
-      gx.M = D; gx.N = rows; gx.K = static_cast<int>(Vp);
-      gx.splits = h->splits; gx.k_split = h->k_split;
-      gx.split_stride = static_cast<int64_t>(rows) * D;
-      gx.C = gxp; gx.ldc = D; gx.Cin = nullptr;
-      gx.mode = lce::EpiMode::kStoreF32;
-      gx.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along rows
-      gx.role = lce::GemmRole::kGradX;
-      LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
-      LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(el, gxp, h->splits, gx.split_stride, rows, D,
-                              static_cast<char*>(io->grad_X) + row0 * d.D * es, h->accum,
-                              dl_unscale, s));
+    if (want_x && !h->gx_group) {
+      const lce_status st = grad_x(Tc, row0, rows);
+      if (st != LCE_OK) return st;
     }
     if (want_w) {
       LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xc, D, rows, D,
                                                         static_cast<char*>(Xt) + jj * cp * es,
                                                         h->k_grp, rows_pad, s));
       if (jj + 1 == h->grp || last) {
+        if (want_x && h->gx_group) {
+          // the whole group's rows, back to back in T from row 0
+          const int64_t g_row0 = (ck - jj) * h->c;
+          const lce_status st = grad_x(T, g_row0, static_cast<int>(row0 + rows - g_row0));
+          if (st != LCE_OK) return st;
+        }
         // grad_W[V][D] += dL^T . X over the group's rows, as (X^T)[D][K]
         // against dL^T with the transposed store: in place, dL is T's panels
         // read k-major; staged, the finalize's dL^T[V][K].

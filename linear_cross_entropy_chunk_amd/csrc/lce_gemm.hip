@@ -694,8 +694,10 @@ void launch_grad_w(const GemmNT& g, dim3 grid, dim3 block, hipStream_t s) {
 }
 
 // The layouts and modes the path uses, and no others:
-//   grad_X: fp32 split partials (kStoreF32); A = W^T staged (fp32) or W read
-//           k-major in place (16-bit types); B = T's panels, K-contiguous.
+//   grad_X: fp32 split partials (kStoreF32), or with one split and W read in
+//           place the gradient itself (kStoreOut / kAccumOut); A = W^T
+//           staged (fp32) or W read k-major in place (16-bit types); B = T's
+//           panels, K-contiguous.
 //   grad_W: any mode; A = X^T staged; B = the staged dL^T, or (16-bit types)
 //           T's panels read k-major.
 template <typename T>
@@ -713,12 +715,23 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   if (pan != (g.b_pstride > 0) || (pan && g.ldb != kTile)) return hipErrorInvalidValue;
   constexpr bool k16 = sizeof(T) == 2;
   if (g.role == GemmRole::kGradX) {
-    if (g.b_kmajor || g.mode != EpiMode::kStoreF32 || (g.a_kmajor && !k16))
+    // fp32 split partials; or, for 16-bit types reading W in place with one
+    // split, grad_X itself (stored or added, in the element type).
+    const bool direct = g.mode == EpiMode::kStoreOut || g.mode == EpiMode::kAccumOut;
+    if (g.b_kmajor || (g.a_kmajor && !k16)) return hipErrorInvalidValue;
+    if (g.mode != EpiMode::kStoreF32 && !(direct && k16 && g.a_kmajor && g.splits == 1))
       return hipErrorInvalidValue;
     if constexpr (k16) {
       if (g.a_kmajor) {
-        k_gemm_grad_x<T, static_cast<int>(EpiMode::kStoreF32), true, false>
-            <<<grid, block, 0, s>>>(g);
+        if (g.mode == EpiMode::kStoreOut)
+          k_gemm_grad_x<T, static_cast<int>(EpiMode::kStoreOut), true, false>
+              <<<grid, block, 0, s>>>(g);
+        else if (g.mode == EpiMode::kAccumOut)
+          k_gemm_grad_x<T, static_cast<int>(EpiMode::kAccumOut), true, false>
+              <<<grid, block, 0, s>>>(g);
+        else
+          k_gemm_grad_x<T, static_cast<int>(EpiMode::kStoreF32), true, false>
+              <<<grid, block, 0, s>>>(g);
         return hipGetLastError();
       }
     }
