@@ -148,15 +148,15 @@ void plan(lce_handle* h) {
   h->w_inplace = h->want_w && h->half && (h->c % 64 == 0 || h->grp == 1);
   h->t_rows = h->w_inplace ? h->k_grp : h->c_pad;
 
+  // With the group's dL in T, grad_X runs once per group over all its rows
+  // (fewer, larger launches; one split needs no partials and no split sum).
+  h->gx_group = h->want_x && h->w_inplace;
+  h->gx_rows = h->gx_group ? std::min<int64_t>(h->grp * h->c, d.N) : h->c;
   // split-K for grad_X = dL . W: aim at one workgroup per CU (256; two
   // rounds of 512 measured slower: more partials to sum, twice the tile
   // starts), >= 64 K per split (one stage; a small problem would otherwise
   // leave a few workgroups walking all of K through mostly empty 256 x 256
   // tiles).
-  // With the group's dL in T, grad_X runs once per group over all its rows
-  // (fewer, larger launches; one split needs no partials and no split sum).
-  h->gx_group = h->want_x && h->w_inplace;
-  h->gx_rows = h->gx_group ? std::min<int64_t>(h->grp * h->c, d.N) : h->c;
   const int64_t tiles = cdiv64(h->gx_rows, lce::kTile) * cdiv64(d.D, lce::kTile);
   int64_t splits = std::max<int64_t>(1, cdiv64(256, std::max<int64_t>(tiles, 1)));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, h->V_pad / 64));
