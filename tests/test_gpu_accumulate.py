@@ -77,6 +77,28 @@ def test_accumulate_twice_is_twice_the_gradient(dt):
         _check(out[k], np.zeros_like(ref[k]), 2.0 * ref[k], dt, k)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_accumulate_with_grad_x_stored_by_its_gemm(dt):
+    """4096 rows x D=4096 form one grad_W group of four 1024-row chunks and
+    256 grad_X tiles, so grad_X needs no K split and its GEMM adds into the
+    caller's buffer itself (the fp16 path also unscales dL there)."""
+    require_gpu()
+    N, D, V = 4096, 4096, 512
+    case = li.small_case(N, D, V, dtype=dt, seed=43, ignore_frac=0.05, bias=False)
+    ref = oracle.linear_cross_entropy(case["X"], case["W"], None, case["t"], reduction="mean")
+    log(f"accumulate, grad_X stored by the GEMM, {dt}")
+    op = LinearCrossEntropy(N, D, V, TORCH_DT[dt], reduction="mean", chunk_rows=1024,
+                            accumulate=True)
+    pre = {k: _prefill(ref[k].shape, np.abs(ref[k]).max(), dt, seed)
+           for seed, k in enumerate(("grad_X", "grad_W"))}
+    out = {k: _dev(v, dt) for k, v in pre.items()}
+    op(_dev(case["X"], dt), _dev(case["W"], dt), torch.from_numpy(case["t"]).to("cuda"),
+       out=out)
+    torch.cuda.synchronize()
+    for k in ("grad_X", "grad_W"):
+        _check(out[k], pre[k], ref[k], dt, k)
+
+
 def test_accumulate_empty_batch_leaves_buffers():
     require_gpu()
     D, V = 32, 300
