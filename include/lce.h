@@ -69,14 +69,22 @@ typedef enum {
   LCE_OK = 0,
   LCE_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
   LCE_ERR_DTYPE = 2,        /* dtype not in {LCE_F32, LCE_BF16, LCE_F16} */
-  LCE_ERR_UNSUPPORTED = 3,  /* acc_dtype != LCE_F32, unaligned rows, ... */
+  LCE_ERR_UNSUPPORTED = 3,  /* unsupported acc_dtype, unaligned rows, ... */
   LCE_ERR_WORKSPACE = 4,    /* workspace NULL, misaligned or too small */
   LCE_ERR_HIP = 5           /* a HIP launch or runtime call failed */
 } lce_status;
 
 /* Element types.  bf16 and fp16 accumulate in fp32 (the pages' mixed
  * precision with acc_dtype float32); fp16 keeps the logits gradient scaled by
- * a power of two inside the library so that it stays in fp16's range. */
+ * a power of two inside the library so that it stays in fp16's range.
+ *
+ * acc_dtype (torch.nn.LinearCrossEntropyOptions page: acc_dtype; the module
+ * source's dtype layout) is LCE_F32, or the input dtype itself.  For bf16 /
+ * fp16 inputs the latter is the non-mixed layout: the gradients accumulate
+ * chunk by chunk in the input dtype (grad_W rounded into the 16-bit output
+ * after every chunk, as LCE_COMPACT does, whatever acc_policy says).  The
+ * logits and softmax statistics are still formed in fp32 on chip; the matrix
+ * cores accumulate in fp32 for every input type. */
 typedef enum { LCE_F32 = 0, LCE_BF16 = 1, LCE_F16 = 2 } lce_dtype;
 
 /* Loss reduction (the pages' reduction argument). */
@@ -119,7 +127,7 @@ typedef struct {
   int64_t ignore_index;  /* rows with this target are ignored (default -100) */
   int64_t chunk_rows;    /* > 0 rows per chunk, or LCE_CHUNK_* */
   int32_t dtype;         /* lce_dtype of X, W, b and of the gradients */
-  int32_t acc_dtype;     /* must be LCE_F32 */
+  int32_t acc_dtype;     /* LCE_F32, or equal to dtype (non-mixed) */
   int32_t has_bias;      /* 0 or 1 */
   int32_t reduction;     /* lce_reduction */
   int32_t acc_policy;    /* lce_acc_policy */
@@ -167,7 +175,7 @@ typedef struct {
 /* Validate `d`, resolve the chunk size and build a handle.  Host only.
  * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, bad
  * reduction / acc_policy / has_bias, unknown flag bits, NULL pointers),
- * DTYPE, UNSUPPORTED (acc_dtype != LCE_F32; D not a multiple of 8 for bf16 / fp16
+ * DTYPE, UNSUPPORTED (acc_dtype neither LCE_F32 nor dtype; D not a multiple of 8 for bf16 / fp16
  * or 4 for fp32; N, V or D above 2^31 - 1).  LCE_GRAD_B without a bias is
  * INVALID_ARG. */
 LCE_API lce_status lce_create(const lce_desc* d, lce_handle** out);

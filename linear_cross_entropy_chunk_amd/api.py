@@ -50,9 +50,13 @@ class LinearCrossEntropy:
                  reduction: str = "mean", ignore_index: int = -100, chunk_rows: int = 0,
                  acc_policy: str = "accurate", grad_x: bool = True, grad_w: bool = True,
                  grad_b: bool | None = None, argmax: bool = False, device="cuda",
-                 chunk_divisor: int = 1, accumulate: bool = False):
+                 chunk_divisor: int = 1, accumulate: bool = False, acc_dtype=None):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
+        # None / float32: mixed precision; the input dtype itself: non-mixed
+        acc = torch.float32 if acc_dtype is None else acc_dtype
+        if acc not in _DTYPES:
+            raise TypeError(f"unsupported acc_dtype {acc}")
         grad_b = bias if grad_b is None else grad_b
         flags = ((B.LCE_GRAD_X if grad_x else 0) | (B.LCE_GRAD_W if grad_w else 0) |
                  (B.LCE_GRAD_B if grad_b else 0) | (B.LCE_ARGMAX if argmax else 0) |
@@ -65,7 +69,7 @@ class LinearCrossEntropy:
         self.flags = flags
         self.device = _device(device)
         self.desc = B.lce_desc(N=N, D=D, V=V, ignore_index=ignore_index, chunk_rows=chunk_rows,
-                               dtype=_DTYPES[dtype], acc_dtype=B.LCE_F32, has_bias=int(bias),
+                               dtype=_DTYPES[dtype], acc_dtype=_DTYPES[acc], has_bias=int(bias),
                                reduction=_REDUCTIONS[reduction],
                                acc_policy=_POLICIES[acc_policy], flags=flags,
                                chunk_divisor=chunk_divisor)

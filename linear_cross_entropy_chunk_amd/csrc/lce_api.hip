@@ -134,12 +134,15 @@ void plan(lce_handle* h) {
   // accumulator is touched once per group instead of once per chunk.  ACCURATE
   // stages up to as many bytes as the fp32 V x D accumulator it saves (K up to
   // 4 D / element size); COMPACT keeps one chunk per group (least memory).
+  // A non-mixed 16-bit layout (acc_dtype = the input dtype) accumulates the
+  // gradients in the input dtype chunk by chunk: COMPACT's grouping.
+  const bool accurate = d.acc_policy == LCE_ACCURATE && !(h->half && d.acc_dtype == d.dtype);
   const int64_t k_max = 4 * d.D / h->esize;
-  h->grp = d.acc_policy == LCE_ACCURATE ? std::max<int64_t>(1, k_max / h->c_pad) : 1;
+  h->grp = accurate ? std::max<int64_t>(1, k_max / h->c_pad) : 1;
   h->grp = std::max<int64_t>(1, std::min<int64_t>(h->grp, std::max<int64_t>(h->n_chunks, 1)));
   h->k_grp = h->grp * h->c_pad;
   h->n_groups = h->n_chunks ? cdiv64(h->n_chunks, h->grp) : 0;
-  h->w_acc32 = h->want_w && h->half && d.acc_policy == LCE_ACCURATE && h->n_groups > 1;
+  h->w_acc32 = h->want_w && h->half && accurate && h->n_groups > 1;
   // 2-byte types: the chunks of a group keep their dL in T (chunk j at row j c_pad of
   // every panel) and grad_W reads it there as a k-major operand, so dL^T is
   // not staged.  This needs the chunks back to back (c a multiple of 64, or
@@ -235,8 +238,9 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
       ~static_cast<uint32_t>(LCE_GRAD_X | LCE_GRAD_W | LCE_GRAD_B | LCE_ARGMAX | LCE_ACCUMULATE))
     return LCE_ERR_INVALID_ARG;
   if ((d->flags & LCE_GRAD_B) && !d->has_bias) return LCE_ERR_INVALID_ARG;
-  // Mixed precision is bf16 / fp16 (or fp32) inputs with an fp32 accumulator only.
-  if (d->acc_dtype != LCE_F32) return LCE_ERR_UNSUPPORTED;
+  // Mixed precision is bf16 / fp16 (or fp32) inputs with an fp32 accumulator;
+  // an accumulator of the input dtype itself is the non-mixed layout.
+  if (d->acc_dtype != LCE_F32 && d->acc_dtype != d->dtype) return LCE_ERR_UNSUPPORTED;
   const int64_t vec = d->dtype == LCE_F32 ? 4 : 8;
   if (d->D % vec != 0) return LCE_ERR_UNSUPPORTED;
   const int64_t kMax = 2147483647LL - 1024;

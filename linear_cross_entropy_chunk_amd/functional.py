@@ -42,7 +42,9 @@ class LinearCrossEntropyOptions:
     chunking_method: "auto" (= "aspect_ratio"), "aspect_ratio",
     "aspect_ratio:N" or None (use batch_chunk_size; None there means one
     chunk).  acc_policy: "auto" (= "compact" on the GPU), "accurate" or
-    "compact".  acc_dtype: None or torch.float32 (the only accumulator)."""
+    "compact".  acc_dtype: None or torch.float32 (mixed precision for 16-bit
+    inputs), or the input dtype itself (non-mixed: gradients accumulated chunk
+    by chunk in the input dtype, as "compact")."""
     allow_retain_graph: bool = False
     batch_chunk_size: int | None = None
     chunking_method: str | None = "auto"
@@ -54,27 +56,29 @@ _ASPECT = re.compile(r"^aspect_ratio(?::(\d+))?$")
 
 
 def _resolve(opts: LinearCrossEntropyOptions, N: int, D: int, V: int, dtype) -> dict:
-    """Options -> C descriptor fields (chunk_rows, chunk_divisor, acc_policy)."""
+    """Options -> C descriptor fields (chunk_rows, chunk_divisor, acc_policy,
+    acc_dtype)."""
     if opts.acc_policy not in ("auto", "accurate", "compact"):
         raise ValueError(f"unknown acc_policy {opts.acc_policy!r}")
-    acc = opts.acc_dtype
-    if acc is not None and acc != torch.float32:
-        # [LCE]: acc_dtype must equal the input dtype unless a 16-bit input
-        # accumulates in float32; the 16-bit non-mixed layouts are not built
-        if acc != dtype:
-            raise RuntimeError(f"acc_dtype {acc} does not fit input dtype {dtype}")
-        raise NotImplementedError(f"accumulation in {acc} is not supported; use float32")
+    acc = torch.float32 if opts.acc_dtype is None else opts.acc_dtype
+    # [LCE]: acc_dtype must equal the input dtype unless a 16-bit input
+    # accumulates in float32 (mixed precision)
+    if acc != torch.float32 and acc != dtype:
+        raise RuntimeError(f"acc_dtype {acc} does not fit input dtype {dtype}")
     policy = "compact" if opts.acc_policy == "auto" else opts.acc_policy
+    if acc == dtype and dtype != torch.float32:
+        policy = "compact"           # non-mixed: every gradient buffer in the input dtype
     bcs = opts.batch_chunk_size
     if bcs is not None and (not isinstance(bcs, int) or bcs < 1):
         raise ValueError(f"batch_chunk_size must be a positive int, got {bcs!r}")
     method = opts.chunking_method
     if method is None:
         return {"chunk_rows": bcs if bcs is not None else B.LCE_CHUNK_ALL, "chunk_divisor": 1,
-                "acc_policy": policy}
+                "acc_policy": policy, "acc_dtype": acc}
     if method == "auto":
         if bcs is not None:          # the default method yields to an explicit size
-            return {"chunk_rows": bcs, "chunk_divisor": 1, "acc_policy": policy}
+            return {"chunk_rows": bcs, "chunk_divisor": 1, "acc_policy": policy,
+                    "acc_dtype": acc}
         method = "aspect_ratio"
     m = _ASPECT.match(method)
     if m is None:
@@ -82,7 +86,8 @@ def _resolve(opts: LinearCrossEntropyOptions, N: int, D: int, V: int, dtype) -> 
     div = int(m.group(1) or 1)
     if div < 1:
         raise ValueError("aspect_ratio:N needs N >= 1")
-    res = {"chunk_rows": B.LCE_CHUNK_ASPECT_RATIO, "chunk_divisor": div, "acc_policy": policy}
+    res = {"chunk_rows": B.LCE_CHUNK_ASPECT_RATIO, "chunk_divisor": div, "acc_policy": policy,
+           "acc_dtype": acc}
     if bcs is not None:
         desc = B.lce_desc(N=N, D=D, V=V, ignore_index=-100, chunk_rows=B.LCE_CHUNK_ASPECT_RATIO,
                           dtype=_LCE_DTYPE[dtype], acc_dtype=B.LCE_F32, has_bias=0,
@@ -130,7 +135,8 @@ def _op(N, D, V, dtype, device, *, bias, reduction, ignore_index, cfg, gx, gw, g
     return LinearCrossEntropy(N, D, V, dtype, bias=bias, reduction=reduction,
                               ignore_index=ignore_index, chunk_rows=cfg["chunk_rows"],
                               chunk_divisor=cfg["chunk_divisor"], acc_policy=cfg["acc_policy"],
-                              grad_x=gx, grad_w=gw, grad_b=gb, device=device)
+                              acc_dtype=cfg["acc_dtype"], grad_x=gx, grad_w=gw, grad_b=gb,
+                              device=device)
 
 
 class _ScalarLCE(torch.autograd.Function):

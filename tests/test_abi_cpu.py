@@ -82,7 +82,11 @@ def _desc(**kw):
     ({"V": 0}, B.LCE_ERR_INVALID_ARG),
     ({"chunk_rows": -2}, B.LCE_ERR_INVALID_ARG),
     ({"dtype": 7}, B.LCE_ERR_DTYPE),
-    ({"acc_dtype": B.LCE_BF16}, B.LCE_ERR_UNSUPPORTED),
+    ({"acc_dtype": B.LCE_BF16}, B.LCE_ERR_UNSUPPORTED),           # fp32 input, bf16 acc
+    ({"dtype": B.LCE_BF16, "acc_dtype": B.LCE_BF16}, B.LCE_OK),   # non-mixed
+    ({"dtype": B.LCE_F16, "acc_dtype": B.LCE_F16}, B.LCE_OK),
+    ({"dtype": B.LCE_BF16, "acc_dtype": B.LCE_F16}, B.LCE_ERR_UNSUPPORTED),
+    ({"dtype": B.LCE_BF16, "acc_dtype": 7}, B.LCE_ERR_UNSUPPORTED),
     ({"reduction": 3}, B.LCE_ERR_INVALID_ARG),
     ({"acc_policy": 2}, B.LCE_ERR_INVALID_ARG),
     ({"has_bias": 0}, B.LCE_ERR_INVALID_ARG),            # grad_b requested without bias
@@ -150,6 +154,10 @@ def test_workspace_grows_with_requested_outputs(lib):
     acc = B.lce_create(_desc(dtype=B.LCE_BF16, acc_policy=B.LCE_ACCURATE))
     cmp_ = B.lce_create(_desc(dtype=B.LCE_BF16, acc_policy=B.LCE_COMPACT))
     assert B.lce_workspace_size(acc) - B.lce_workspace_size(cmp_) >= 1000 * 64 * 4
+    # the non-mixed layout (bf16 accumulator) plans like compact, whatever the policy
+    nm = B.lce_create(_desc(dtype=B.LCE_BF16, acc_dtype=B.LCE_BF16, acc_policy=B.LCE_ACCURATE))
+    assert B.lce_workspace_size(nm) == B.lce_workspace_size(cmp_)
+    B.lce_destroy(nm)
     B.lce_destroy(acc)
     B.lce_destroy(cmp_)
 

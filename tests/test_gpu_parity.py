@@ -177,6 +177,47 @@ def test_accurate_and_compact_policies():
     assert ea["grad_W"] <= ec["grad_W"] * 1.05
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_non_mixed_layout(dt):
+    """acc_dtype equal to the 16-bit input dtype (the non-mixed layout)
+    accumulates grad_W chunk by chunk in the input dtype: the oracle's
+    tolerance holds, and the result is compact's bit for bit even when
+    accurate is asked for.  Through the autograd entry point too."""
+    require_gpu()
+    import torch
+
+    from gpu_common import TORCH_DT, to_dev
+    from linear_cross_entropy_chunk_amd import LinearCrossEntropy, LinearCrossEntropyOptions
+    from linear_cross_entropy_chunk_amd.functional import linear_cross_entropy
+
+    N, D, V = 600, 128, 2000
+    case = li.small_case(N, D, V, dtype=dt, seed=17)
+    ref = _ref(case)
+    tdt = TORCH_DT[dt]
+    X, W, b = to_dev(case["X"], dt), to_dev(case["W"], dt), to_dev(case["b"], dt)
+    t = torch.from_numpy(case["t"]).to("cuda")
+    outs = {}
+    for name, acc_dtype, policy in (("non-mixed", tdt, "accurate"), ("compact", None, "compact")):
+        op = LinearCrossEntropy(N, D, V, tdt, bias=True, chunk_rows=128, acc_policy=policy,
+                                acc_dtype=acc_dtype)
+        o = op(X, W, t, b)
+        torch.cuda.synchronize()
+        outs[name] = {k: v.float().cpu().numpy().astype(np.float64) for k, v in o.items()}
+    for k in ("loss", "grad_X", "grad_W", "grad_b"):
+        np.testing.assert_array_equal(outs["non-mixed"][k], outs["compact"][k], err_msg=k)
+    check_all(outs["non-mixed"], ref, dt, "mean")
+
+    Xr, Wr, br = (x.clone().requires_grad_(True) for x in (X, W, b))
+    opts = LinearCrossEntropyOptions(acc_dtype=tdt, batch_chunk_size=128, chunking_method=None)
+    loss = linear_cross_entropy(Xr, Wr, t, br, options=opts)
+    loss.backward()
+    torch.cuda.synchronize()
+    check_loss(float(loss.detach().float().cpu()), ref["loss"], dt, "mean")
+    for name, x in (("grad_X", Xr), ("grad_W", Wr), ("grad_b", br)):
+        np.testing.assert_array_equal(x.grad.float().cpu().numpy().astype(np.float64),
+                                      outs["compact"][name], err_msg=name)
+
+
 def test_zero_weight_closed_form_on_gpu():
     """W = 0, b = 0: loss = log V exactly (to fp32), argmax = 0 on every row,
     grad_X = 0 exactly."""

@@ -49,7 +49,7 @@ def test_options_resolution():
     f32 = torch.float32
     r = _resolve(LinearCrossEntropyOptions(), N, D, V, f32)
     assert r == {"chunk_rows": B.LCE_CHUNK_ASPECT_RATIO, "chunk_divisor": 1,
-                 "acc_policy": "compact"}
+                 "acc_policy": "compact", "acc_dtype": torch.float32}
     r = _resolve(LinearCrossEntropyOptions(chunking_method="aspect_ratio:4",
                                            acc_policy="accurate"), N, D, V, f32)
     assert r["chunk_divisor"] == 4 and r["acc_policy"] == "accurate"
@@ -68,13 +68,20 @@ def test_options_resolution():
         _resolve(LinearCrossEntropyOptions(chunking_method="balanced"), N, D, V, f32)
     with pytest.raises(ValueError):
         _resolve(LinearCrossEntropyOptions(acc_policy="fast"), N, D, V, f32)
-    # acc_dtype: a mismatch with the input dtype is an error, 16-bit non-mixed
-    # accumulation is not built, float32 is the only accumulator
+    # acc_dtype: float32 (mixed precision), or the input dtype itself (the
+    # non-mixed layout, which accumulates like "compact" whatever the policy);
+    # any other dtype is an error
     with pytest.raises(RuntimeError):
         _resolve(LinearCrossEntropyOptions(acc_dtype=torch.bfloat16), N, D, V, f32)
-    with pytest.raises(NotImplementedError):
-        _resolve(LinearCrossEntropyOptions(acc_dtype=torch.bfloat16), N, D, V, torch.bfloat16)
-    _resolve(LinearCrossEntropyOptions(acc_dtype=torch.float32), N, D, V, torch.float16)
+    with pytest.raises(RuntimeError):
+        _resolve(LinearCrossEntropyOptions(acc_dtype=torch.float16), N, D, V, torch.bfloat16)
+    for dt in (torch.bfloat16, torch.float16):
+        r = _resolve(LinearCrossEntropyOptions(acc_dtype=dt, acc_policy="accurate"), N, D, V, dt)
+        assert r["acc_dtype"] == dt and r["acc_policy"] == "compact"
+    r = _resolve(LinearCrossEntropyOptions(acc_dtype=torch.float32, acc_policy="accurate"),
+                 N, D, V, torch.float16)
+    assert r["acc_dtype"] == torch.float32 and r["acc_policy"] == "accurate"
+    assert _resolve(LinearCrossEntropyOptions(acc_dtype=f32), N, D, V, f32)["acc_dtype"] == f32
 
 
 def test_argument_errors_before_any_device_work():
