@@ -174,10 +174,11 @@ typedef struct {
 
 /* Validate `d`, resolve the chunk size and build a handle.  Host only.
  * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, bad
- * reduction / acc_policy / has_bias, unknown flag bits, NULL pointers),
- * DTYPE, UNSUPPORTED (acc_dtype neither LCE_F32 nor dtype; D not a multiple of 8 for bf16 / fp16
- * or 4 for fp32; N, V or D above 2^31 - 1).  LCE_GRAD_B without a bias is
- * INVALID_ARG. */
+ * acc_policy / has_bias, unknown flag bits, NULL pointers), DTYPE,
+ * UNSUPPORTED (a reduction outside lce_reduction, the module source's
+ * NotImplementedError; acc_dtype neither LCE_F32 nor dtype; D not a multiple
+ * of 8 for bf16 / fp16 or 4 for fp32; the size limits above).  LCE_GRAD_B
+ * without a bias is INVALID_ARG. */
 LCE_API lce_status lce_create(const lce_desc* d, lce_handle** out);
 
 /* Bytes of device workspace lce_forward_backward needs (host only). */
@@ -239,7 +240,9 @@ LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
  * overwrites `logits` in place with the gradient g_n (softmax - onehot), g_n
  * as for lce_forward_backward with grad_output = grad_scale on every counted
  * row for NONE.  class_weight ([V] fp32 or NULL) weighs rows as in lce_io.
- * n_valid may be NULL.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+ * n_valid may be NULL.  Errors: INVALID_ARG (N < 0, V < 1, NULL pointers),
+ * UNSUPPORTED (a reduction outside lce_reduction, V % 4 != 0, misaligned
+ * logits, N or V above 2^31 - 1), WORKSPACE, HIP. */
 LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets,
                           const float* class_weight, int64_t N,
                           int64_t V, int64_t ignore_index, int32_t reduction,

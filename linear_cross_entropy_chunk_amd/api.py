@@ -53,6 +53,8 @@ class LinearCrossEntropy:
                  chunk_divisor: int = 1, accumulate: bool = False, acc_dtype=None):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
+        if reduction not in _REDUCTIONS:
+            raise NotImplementedError(f"reduction={reduction!r} is not supported")
         # None / float32: mixed precision; the input dtype itself: non-mixed
         acc = torch.float32 if acc_dtype is None else acc_dtype
         if acc not in _DTYPES:
@@ -202,6 +204,8 @@ class CrossEntropyInplace:
 
     def __init__(self, N: int, V: int, *, reduction: str = "mean", ignore_index: int = -100,
                  device="cuda"):
+        if reduction not in _REDUCTIONS:
+            raise NotImplementedError(f"reduction={reduction!r} is not supported")
         self.N, self.V = N, V
         self.reduction = reduction
         self.ignore_index = ignore_index

@@ -231,7 +231,8 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
       d->chunk_divisor < 0)
     return LCE_ERR_INVALID_ARG;
   if (d->dtype != LCE_F32 && d->dtype != LCE_BF16 && d->dtype != LCE_F16) return LCE_ERR_DTYPE;
-  if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
+  // an unknown reduction is the pages' NotImplementedError
+  if (d->reduction < LCE_MEAN || d->reduction > LCE_NONE) return LCE_ERR_UNSUPPORTED;
   if (d->acc_policy != LCE_ACCURATE && d->acc_policy != LCE_COMPACT) return LCE_ERR_INVALID_ARG;
   if (d->has_bias != 0 && d->has_bias != 1) return LCE_ERR_INVALID_ARG;
   if (d->flags &
@@ -545,7 +546,8 @@ lce_status lce_ce_inplace(float* logits, const int64_t* targets, const float* cl
                           int64_t N, int64_t V, int64_t ignore_index, int32_t reduction,
                           float grad_scale, float* loss, int64_t* n_valid, void* workspace,
                           size_t ws_bytes, void* stream) {
-  if (N < 0 || V < 1 || reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_INVALID_ARG;
+  if (N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
+  if (reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_UNSUPPORTED;
   if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
   if (!loss) return LCE_ERR_INVALID_ARG;
   if (V % 4 != 0 || (logits && !aligned16(logits))) return LCE_ERR_UNSUPPORTED;

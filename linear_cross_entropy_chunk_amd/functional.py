@@ -106,7 +106,8 @@ def _resolve(opts: LinearCrossEntropyOptions, N: int, D: int, V: int, dtype) -> 
 
 def _check_args(X, W, t, b, cw, reduction, label_smoothing):
     if reduction not in ("mean", "sum", "none"):
-        raise ValueError(f"{reduction!r} is not a valid value for reduction")
+        # [LCE] _ChunkContext's validation: an unsupported reduction
+        raise NotImplementedError(f"reduction={reduction!r} is not supported")
     if label_smoothing != 0.0:
         raise NotImplementedError("label_smoothing is not supported")
     if t.dtype != torch.int64:
@@ -279,7 +280,8 @@ def cross_entropy_inplace(logits, target, weight=None, reduction: str = "mean",
     with the gradient of the loss (declared to autograd with mark_dirty).
     Returns the loss; logits must not be a leaf that requires grad."""
     if reduction not in ("mean", "sum", "none"):
-        raise ValueError(f"{reduction!r} is not a valid value for reduction")
+        # [LCE] _ChunkContext's validation: an unsupported reduction
+        raise NotImplementedError(f"reduction={reduction!r} is not supported")
     if target.dtype != torch.int64:
         raise TypeError(f"target dtype must be torch.int64, got {target.dtype}")
     cw = None if weight is None else weight.detach().to(torch.float32).contiguous()

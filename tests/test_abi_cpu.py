@@ -87,7 +87,7 @@ def _desc(**kw):
     ({"dtype": B.LCE_F16, "acc_dtype": B.LCE_F16}, B.LCE_OK),
     ({"dtype": B.LCE_BF16, "acc_dtype": B.LCE_F16}, B.LCE_ERR_UNSUPPORTED),
     ({"dtype": B.LCE_BF16, "acc_dtype": 7}, B.LCE_ERR_UNSUPPORTED),
-    ({"reduction": 3}, B.LCE_ERR_INVALID_ARG),
+    ({"reduction": 3}, B.LCE_ERR_UNSUPPORTED),          # the pages' NotImplementedError
     ({"acc_policy": 2}, B.LCE_ERR_INVALID_ARG),
     ({"has_bias": 0}, B.LCE_ERR_INVALID_ARG),            # grad_b requested without bias
     ({"flags": 32}, B.LCE_ERR_INVALID_ARG),
