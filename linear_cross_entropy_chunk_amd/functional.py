@@ -158,7 +158,9 @@ class _ScalarLCE(torch.autograd.Function):
         ctx.device = X.device
         ctx.allow_retain_graph = retain
         ctx.consumed = False
-        return out["loss"].reshape(())
+        # the op's output contract (its fake-tensor registration in [LCE]): a
+        # scalar of the input dtype, rounded once from the fp32 loss
+        return out["loss"].reshape(()).to(X.dtype)
 
     @staticmethod
     @once_differentiable
@@ -196,7 +198,7 @@ class _NoneLCE(torch.autograd.Function):
         ctx.save_for_backward(X, W, t, b, cw)
         ctx.ignore_index = ignore_index
         ctx.cfg = cfg
-        return out["loss"]
+        return out["loss"].to(X.dtype)            # [LCE]: (N,) of the input dtype
 
     @staticmethod
     @once_differentiable
