@@ -466,14 +466,23 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       if (st != LCE_OK) return st;
     }
     if (want_w) {
-      LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xc, D, rows, D,
-                                                        static_cast<char*>(Xt) + jj * cp * es,
-                                                        h->k_grp, rows_pad, s));
+      // X^T of the group for grad_W: per chunk when dL^T is staged, else once
+      // for the whole group at its end (its rows back to back, as in T)
+      if (!h->w_inplace)
+        LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xc, D, rows, D,
+                                                          static_cast<char*>(Xt) + jj * cp * es,
+                                                          h->k_grp, rows_pad, s));
       if (jj + 1 == h->grp || last) {
+        const int64_t g_row0 = (ck - jj) * h->c;
+        const int g_rows = static_cast<int>(row0 + rows - g_row0);
+        if (h->w_inplace)
+          LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xb + g_row0 * d.D * es, D, g_rows,
+                                                            D, Xt, h->k_grp,
+                                                            static_cast<int>(round_up(g_rows, 64)),
+                                                            s));
         if (want_x && h->gx_group) {
           // the whole group's rows, back to back in T from row 0
-          const int64_t g_row0 = (ck - jj) * h->c;
-          const lce_status st = grad_x(T, g_row0, static_cast<int>(row0 + rows - g_row0));
+          const lce_status st = grad_x(T, g_row0, g_rows);
           if (st != LCE_OK) return st;
         }
         // grad_W[V][D] += dL^T . X over the group's rows, as (X^T)[D][K]
