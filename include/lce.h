@@ -203,7 +203,9 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
  * `workspace` is a device buffer of at least lce_workspace_size bytes,
  * 256-byte aligned; its contents on entry are irrelevant and on return are
  * unspecified.  Calls that share a workspace or outputs must be ordered on
- * one stream.  Errors: INVALID_ARG (NULL required pointer, grad_output set
+ * one stream.  The handle itself is read-only here, so host threads may share
+ * it, except while the timing hook below is enabled (its event pool is not
+ * locked).  Errors: INVALID_ARG (NULL required pointer, grad_output set
  * for MEAN / SUM, grad_b requested without bias), WORKSPACE, HIP. */
 LCE_API lce_status lce_forward_backward(lce_handle* h, const lce_io* io,
                                 void* workspace, size_t ws_bytes,
