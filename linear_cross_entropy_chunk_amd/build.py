@@ -57,7 +57,31 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+    build_c_client(verbose)
     return LIB_PATH
+
+
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "lce_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_abi", "lce_client")
+
+
+def build_c_client(verbose: bool = True) -> str | None:
+    """The plain C client the GPU tests use to call liblce.so without
+    PyTorch (host code only; it finds the library through its rpath)."""
+    if not os.path.exists(C_CLIENT_SRC):
+        return None
+    rpath = "$ORIGIN/" + os.path.relpath(PKG_DIR, os.path.dirname(C_CLIENT))
+    rocm = os.environ.get("ROCM_PATH") or os.path.dirname(os.path.dirname(
+        os.path.realpath(HIPCC)))
+    tmp = C_CLIENT + ".tmp"
+    _run([HIPCC, "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+          C_CLIENT_SRC, "-o", tmp, "-L", PKG_DIR, "-llce", "-L", os.path.join(rocm, "lib"),
+          "-lamdhip64", f"-Wl,-rpath,{rpath}"])
+    os.replace(tmp, C_CLIENT)
+    if verbose:
+        print(f"built {C_CLIENT}")
+    return C_CLIENT
 
 
 if __name__ == "__main__":
