@@ -4,18 +4,23 @@
  * writes seeded inputs to a file, runs this program, and compares what it
  * writes back with the fp64 oracle and with the Python binding.
  *
- *   lce_client IN OUT
+ *   lce_client IN OUT        fused forward+backward (lce_forward_backward)
+ *   lce_client ce IN OUT     standalone in-place cross-entropy (lce_ce_inplace)
  *
  * IN:  int64 N, D, V, chunk_rows, dtype (lce_dtype), reduction, has_bias,
  *      then X [N][D], W [V][D], b [V] (if has_bias) as raw elements of dtype
  *      (4-byte fp32 or 2-byte bf16 / fp16), then int64 targets [N].
  * OUT: float loss [1, or N for LCE_NONE], int64 n_valid, int64 n_bad, then
  *      grad_X [N][D], grad_W [V][D], grad_b [V] (if has_bias) as raw elements.
+ * ce IN:  int64 N, V, reduction, then fp32 logits [N][V], int64 targets [N].
+ * ce OUT: float loss [1, or N], int64 n_valid, then the fp32 gradient [N][V]
+ *         that lce_ce_inplace wrote over the logits.
  * Exit status 0 on success; a message on stderr otherwise.
  */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -65,9 +70,60 @@ static int download(FILE* f, const void* dev, size_t bytes) {
   return bad;
 }
 
+static int run_ce(const char* in_path, const char* out_path) {
+  FILE* in = fopen(in_path, "rb");
+  if (!in) {
+    fprintf(stderr, "cannot open %s\n", in_path);
+    return 1;
+  }
+  int64_t hdr[3];
+  if (fread(hdr, sizeof(int64_t), 3, in) != 3) {
+    fprintf(stderr, "short header\n");
+    return 1;
+  }
+  const int64_t N = hdr[0], V = hdr[1];
+  const int32_t reduction = (int32_t)hdr[2];
+  void* z = read_block(in, (size_t)(N * V) * sizeof(float));
+  void* t = read_block(in, (size_t)N * sizeof(int64_t));
+  fclose(in);
+  if (!z || !t) {
+    fprintf(stderr, "short input\n");
+    return 1;
+  }
+  size_t ws_bytes = 0;
+  CHECK_LCE(lce_ce_workspace_size(N, V, &ws_bytes));
+  const size_t n_loss = reduction == LCE_NONE ? (size_t)N : 1;
+  void *dz, *dt, *dloss, *dnv, *ws;
+  if (upload(&dz, z, (size_t)(N * V) * sizeof(float)) ||
+      upload(&dt, t, (size_t)N * sizeof(int64_t)))
+    return 1;
+  CHECK_HIP(hipMalloc(&dloss, n_loss * sizeof(float) + 16));
+  CHECK_HIP(hipMalloc(&dnv, sizeof(int64_t)));
+  CHECK_HIP(hipMalloc(&ws, ws_bytes ? ws_bytes : 256));
+  CHECK_LCE(lce_ce_inplace((float*)dz, (const int64_t*)dt, NULL, N, V, -100, reduction, 1.0f,
+                           (float*)dloss, (int64_t*)dnv, ws, ws_bytes, NULL));
+  CHECK_HIP(hipDeviceSynchronize());
+  FILE* out = fopen(out_path, "wb");
+  if (!out) {
+    fprintf(stderr, "cannot open %s\n", out_path);
+    return 1;
+  }
+  if (download(out, dloss, n_loss * sizeof(float)) || download(out, dnv, sizeof(int64_t)) ||
+      download(out, dz, (size_t)(N * V) * sizeof(float))) {
+    fprintf(stderr, "writing %s failed\n", out_path);
+    return 1;
+  }
+  fclose(out);
+  hipFree(dz); hipFree(dt); hipFree(dloss); hipFree(dnv); hipFree(ws);
+  free(z); free(t);
+  printf("lce_client ce: ok\n");
+  return 0;
+}
+
 int main(int argc, char** argv) {
+  if (argc == 4 && strcmp(argv[1], "ce") == 0) return run_ce(argv[2], argv[3]);
   if (argc != 3) {
-    fprintf(stderr, "usage: %s IN OUT\n", argv[0]);
+    fprintf(stderr, "usage: %s IN OUT | %s ce IN OUT\n", argv[0], argv[0]);
     return 2;
   }
   FILE* in = fopen(argv[1], "rb");

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import lce_inputs as li
-from gpu_common import check_all, log, oracle, require_gpu, run_gpu
+from gpu_common import check_all, log, oracle, rel_err, require_gpu, run_ce, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +76,40 @@ def test_c_client_matches_oracle_and_binding(dt, reduction, tmp_path):
     py = run_gpu(case, dt, reduction=reduction, chunk_rows=chunk, argmax=False, upstream=up)
     for key in ("loss", "grad_X", "grad_W", "grad_b", "n_valid", "n_bad"):
         np.testing.assert_array_equal(got[key], py[key], err_msg=key)
+
+
+@pytest.mark.parametrize("V", [1000, 100000])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_c_client_ce_inplace(V, reduction, tmp_path):
+    """lce_ce_inplace from C: streamed rows (V = 1000) and on-chip rows
+    (V = 100000)."""
+    require_gpu()
+    assert os.path.exists(CLIENT), f"{CLIENT} is missing: run __graft_entry__.build()"
+    N = 37
+    rng = np.random.default_rng(V + 52)
+    z = (rng.standard_normal((N, V)) * 2.0).astype(np.float32)
+    t = rng.integers(0, V, N).astype(np.int64)
+    t[[0, 9]] = -100
+    inp, out = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        f.write(np.array([N, V, REDUCTION[reduction]], np.int64).tobytes())
+        f.write(z.tobytes())
+        f.write(t.tobytes())
+    log(f"C client ce V={V} {reduction}")
+    r = subprocess.run([CLIENT, "ce", str(inp), str(out)], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    buf = out.read_bytes()
+    n_loss = N if reduction == "none" else 1
+    loss = np.frombuffer(buf, np.float32, n_loss, 0).astype(np.float64)
+    nv = int(np.frombuffer(buf, np.int64, 1, 4 * n_loss)[0])
+    dl = np.frombuffer(buf, np.float32, N * V, 4 * n_loss + 8).reshape(N, V).astype(np.float64)
+    assert 4 * n_loss + 8 + 4 * N * V == len(buf)
+    ref_loss, ref_dl = oracle.softmax_cross_entropy(z, t, reduction=reduction)
+    assert nv == N - 2
+    assert rel_err(loss, np.atleast_1d(ref_loss)) <= 1e-5
+    assert rel_err(dl, ref_dl) <= 1e-4
+    py_loss, py_nv, py_dl = run_ce(z, t, reduction=reduction)
+    np.testing.assert_array_equal(loss, py_loss)
+    np.testing.assert_array_equal(dl, py_dl)
+    assert nv == py_nv
