@@ -10,7 +10,15 @@ grad_W, with the inputs already resident in HBM.
 Prints one JSON line: tokens/s (value), TFLOP/s counting 6*N*V*D, the
 roofline of the dominant kernel (its average launch duration measured with
 HIP events recorded on the library's stream during the timed steps), and the
-fp64 CPU oracle timed on a bounded row sample of the same workload.
+fp64 CPU oracle timed on a bounded row sample of the same workload.  The
+default run adds three records to the same line:
+  per_chunk  the same workload on the per-chunk path (group_rows = 2048: each
+             chunk's dL consumed by both gradient GEMMs right after its
+             finalize, grad_W carried across chunks in an fp32 accumulator);
+  ce         the standalone in-place softmax cross-entropy on fp32 logits
+             [16384, 131072] (GB/s against 8 TB/s);
+  copy       a plain 1 GiB device-to-device copy in the same process, the
+             achievable read + write bandwidth.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -71,6 +79,25 @@ def blas_threads() -> int:
         return os.cpu_count() or 1
 
 
+def host_cpu() -> dict:
+    """The host's logical CPU count (all of them, and those this process may
+    run on) and the CPU model, for the CPU baseline's record."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"nproc": os.cpu_count(), "nproc_usable": usable, "cpu_model": model}
+
+
 def cpu_baseline_lce(inputs: dict, rows: int, label: str) -> dict:
     """The fp64 oracle as it stands on the first `rows` rows (full W)."""
     import numpy as np
@@ -82,9 +109,74 @@ def cpu_baseline_lce(inputs: dict, rows: int, label: str) -> dict:
     r = oracle.linear_cross_entropy(X, inputs["W"], inputs["b"], t, reduction="mean")
     dt = time.perf_counter() - t0
     assert np.isfinite(r["loss"])
+    # `cores` is the number of threads the oracle ran on: numpy's matmul
+    # (the oracle's only library primitive, and nearly all of its time) uses
+    # the BLAS thread pool; its elementwise passes use one core.
     return {"value": rows / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            **host_cpu(),
             "sample": f"rows 0-{rows - 1} of the {label} workload with the full W: "
                       f"loss, grad_X, grad_W, grad_b in float64 ({dt:.1f} s)"}
+
+
+GEMM_MASK = (1 << 1) | (1 << 4) | (1 << 7)          # logits, gemm_x, gemm_w
+
+
+def time_steps(op, io, steps: int, warmup: int, breakdown: bool = False):
+    """Run `warmup` untimed steps, then time `steps` steps between
+    synchronisations with events on torch's current stream (the library's
+    stream), and the selected kernel classes with the library's timing hook.
+    Returns (ms per step, per-class timing, wall seconds)."""
+    import torch
+
+    from linear_cross_entropy_chunk_amd import _binding as B
+    for _ in range(warmup):
+        op.run_io(io)
+    torch.cuda.synchronize()
+    mask = (1 << B.LCE_K_COUNT) - 1 if breakdown else GEMM_MASK
+    B.lce_timing_enable(op.handle, mask)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        op.run_io(io)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    timing = B.lce_timing_read(op.handle)
+    B.lce_timing_enable(op.handle, 0)
+    return start.elapsed_time(end) / steps, timing, wall
+
+
+def bench_per_chunk(args, cfg, X, W, t, b, group_rows: int) -> dict:
+    """The same workload on the per-chunk path: group_rows rows of dL per
+    grad_W GEMM (one chunk when it equals the chunk rows), grad_W carried
+    across chunks in an fp32 accumulator."""
+    import torch
+
+    from linear_cross_entropy_chunk_amd import LinearCrossEntropy
+    op = LinearCrossEntropy(cfg.N, cfg.D, cfg.V, X.dtype, bias=b is not None,
+                            reduction=cfg.reduction, chunk_rows=cfg.chunk_rows,
+                            acc_policy="accurate", grad_x=True, grad_w=True,
+                            grad_b=b is not None, device=X.device, group_rows=group_rows)
+    out = op.make_outputs(grads=True)
+    io = op.make_io(X, W, t, b, out=out)
+    ms_step, timing, _ = time_steps(op, io, args.steps, args.warmup)
+    loss = float(out["loss"].cpu()[0])
+    N, D, V = cfg.N, cfg.D, cfg.V
+    rec = {"group_rows": group_rows, "chunk_rows": op.chunk_rows, "ms_per_step": ms_step,
+           "tokens_per_s": N / (ms_step / 1e3),
+           "tflops": 6.0 * N * V * D / (ms_step / 1e3) / 1e12,
+           "workspace_bytes": op.ws_bytes, "loss": loss,
+           "kernels": {k: round(ms / args.steps, 4) for k, (ms, n) in timing.items() if n},
+           "launches_per_step": {k: n // args.steps for k, (ms, n) in timing.items() if n}}
+    rec["frac_of_peak"] = rec["tflops"] / PEAK_16BIT_TFLOPS
+    log(f"per-chunk path (group_rows={group_rows}): {ms_step:.3f} ms/step, "
+        f"{rec['tflops']:.0f} TFLOP/s, workspace {op.ws_bytes / 2**30:.2f} GiB, "
+        f"kernels {rec['kernels']}")
+    del op, out, io
+    torch.cuda.empty_cache()
+    return rec
 
 
 def bench_lce(args) -> dict:
@@ -114,30 +206,12 @@ def bench_lce(args) -> dict:
     op = LinearCrossEntropy(cfg.N, cfg.D, cfg.V, dt, bias=b is not None,
                             reduction=cfg.reduction, chunk_rows=chunk,
                             acc_policy=args.acc_policy, grad_x=True, grad_w=True,
-                            grad_b=b is not None, device=dev)
+                            grad_b=b is not None, device=dev, group_rows=args.group_rows)
     out = op.make_outputs(grads=True)
     io = op.make_io(X, W, t, b, out=out, grad_output=u)
-    log(f"chunk_rows={op.chunk_rows} chunks={op.n_chunks} workspace={op.ws_bytes / 2**30:.2f} GiB")
-
-    for _ in range(args.warmup):
-        op.run_io(io)
-    torch.cuda.synchronize()
-
-    gemm_mask = (1 << 1) | (1 << 4) | (1 << 7)          # logits, gemm_x, gemm_w
-    mask = (1 << B.LCE_K_COUNT) - 1 if args.breakdown else gemm_mask
-    B.lce_timing_enable(op.handle, mask)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        op.run_io(io)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / args.steps
-    timing = B.lce_timing_read(op.handle)
-    B.lce_timing_enable(op.handle, 0)
+    log(f"chunk_rows={op.chunk_rows} chunks={op.n_chunks} group_rows={args.group_rows} "
+        f"workspace={op.ws_bytes / 2**30:.2f} GiB")
+    ms_step, timing, wall = time_steps(op, io, args.steps, args.warmup, args.breakdown)
     loss = float(out["loss"].cpu()[0]) if cfg.reduction != "none" else float("nan")
     log(f"{ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
     eager_ms = ms_step
@@ -160,6 +234,7 @@ def bench_lce(args) -> dict:
         log(f"graph replay: {ms_step:.3f} ms/step (eager {eager_ms:.3f})")
 
     N, D, V = cfg.N, cfg.D, cfg.V
+    op_chunk_rows = op.chunk_rows
     per_kernel = {}
     for name, (ms, n) in timing.items():
         if n:
@@ -191,6 +266,8 @@ def bench_lce(args) -> dict:
                    "acc_policy": args.acc_policy, "parallelism": "single GPU"},
         "tflops": tflops,
         "frac_of_peak": tflops / peak,
+        "workspace_bytes": op.ws_bytes,
+        "group_rows": args.group_rows,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": load_traffic(dom, cfg.name) if label == cfg.name else None,
@@ -201,6 +278,11 @@ def bench_lce(args) -> dict:
     if args.graph:
         result["graph"] = True
         result["eager_ms_per_step"] = eager_ms
+    if args.per_chunk and cfg.dtype != "f32" and args.group_rows == 0 \
+            and args.acc_policy == "accurate":
+        del op, out, io
+        torch.cuda.empty_cache()
+        result["per_chunk"] = bench_per_chunk(args, cfg, X, W, t, b, op_chunk_rows)
     if not args.no_cpu_baseline:
         rows = args.cpu_rows
         log(f"cpu baseline: oracle on {rows} rows")
@@ -209,8 +291,11 @@ def bench_lce(args) -> dict:
     return result
 
 
-def bench_ce(args) -> dict:
-    import numpy as np
+def time_ce(steps: int, warmup: int):
+    """The standalone in-place CE on the [16384, 131072] fp32 workload:
+    (config, inputs, ms per call, GB/s, loss).  Each call overwrites the
+    logits, so they are restored before each call; only the in-place CE call
+    is inside the events."""
     import torch
 
     import lce_inputs as li
@@ -224,14 +309,12 @@ def bench_ce(args) -> dict:
     z = torch.empty_like(pristine)
     t = torch.from_numpy(inputs["t"]).to(dev)
     op = CrossEntropyInplace(cfg.N, cfg.V, reduction=cfg.reduction, device=dev)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         z.copy_(pristine)
         op(z, t)
     torch.cuda.synchronize()
-    # Each step overwrites the logits, so they are restored before each step;
-    # only the in-place CE call is inside the events.
     times = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         z.copy_(pristine)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
@@ -244,7 +327,28 @@ def bench_ce(args) -> dict:
     nbytes = 2.0 * cfg.N * cfg.V * 4          # logits read once, gradient written once
     gbs = nbytes / (ms_step / 1e3) / 1e9
     loss = float(op.loss.cpu()[0])
-    log(f"{ms_step:.3f} ms/call, {gbs:.0f} GB/s, loss {loss:.6f}")
+    log(f"standalone CE: {ms_step:.3f} ms/call, {gbs:.0f} GB/s, loss {loss:.6f}")
+    del pristine, z, t, op
+    torch.cuda.empty_cache()
+    return cfg, inputs, ms_step, gbs, loss
+
+
+def ce_record(args) -> dict:
+    """The standalone CE as a record of the default line, with the plain copy
+    measured in the same process as the achievable-bandwidth yardstick."""
+    cfg, _, ms_step, gbs, loss = time_ce(args.steps, args.warmup)
+    copy = copy_calibration()
+    log(f"copy: {copy['gbs_read_plus_write']:.0f} GB/s (read + write)")
+    return {"workload": f"{cfg.name} N={cfg.N} V={cfg.V} reduction={cfg.reduction}, "
+                        "gradient written over the logits",
+            "kernel": "ce_rows", "ms_per_call": ms_step, "bytes_per_call": 2 * cfg.N * cfg.V * 4,
+            "gbs": gbs, "peak_gbs": PEAK_HBM_GBS, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+            "frac_of_copy": gbs / copy["gbs_read_plus_write"], "loss": loss,
+            "steps": args.steps, "warmup": args.warmup, "copy": copy}
+
+
+def bench_ce(args) -> dict:
+    cfg, inputs, ms_step, gbs, loss = time_ce(args.steps, args.warmup)
     result = {
         "metric": "standalone in-place softmax CE GB/s (2*N*V*4 bytes) at N=16384,V=131072 fp32",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -270,7 +374,7 @@ def bench_ce(args) -> dict:
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": rows * cfg.V * 8.0 / dt / 1e9, "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": f"rows 0-{rows - 1} of {cfg.name} in float64, 512-row blocks ({dt:.1f} s)"}
     return result
 
@@ -358,6 +462,13 @@ def main() -> int:
                     help="time replays of one call captured into a HIP graph")
     ap.add_argument("--acc-policy", default="accurate", choices=["accurate", "compact"])
     ap.add_argument("--chunk-rows", type=int, default=None)
+    ap.add_argument("--group-rows", type=int, default=0,
+                    help="rows of dL held per grad_W GEMM (0: the library's default; the "
+                         "chunk rows: the per-chunk path with an fp32 accumulator)")
+    ap.add_argument("--no-per-chunk", dest="per_chunk", action="store_false",
+                    help="skip the per-chunk record of the default line")
+    ap.add_argument("--no-ce", dest="ce", action="store_false",
+                    help="skip the standalone-CE record of the default line")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
@@ -382,6 +493,8 @@ def main() -> int:
         print("bench.py needs the GPU", file=sys.stderr)
         return 1
     result = bench_ce(args) if args.workload == "ce-f32" else bench_lce(args)
+    if args.ce and args.workload == "large-vocab-bf16" and args.dtype in (None, "bf16"):
+        result["ce"] = ce_record(args)
     if args.calibrate_copy:
         result["copy_calibration"] = copy_calibration()
         log(f"copy: {result['copy_calibration']['gbs_read_plus_write']:.0f} GB/s (read + write)")

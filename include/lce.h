@@ -8,9 +8,25 @@
  * lse_n - z[n, t_n] (0 on ignored rows), its mean / sum / per-row value, and
  * the gradients grad_X = dL W, grad_W = dL^T X and grad_b = sum_n dL[n, :],
  * where dL = g (softmax(z) - onehot(t)) and g is the per-row weight of the
- * reduction.  It walks the batch rows in chunks of chunk_rows rows, so the
- * full N x V logit matrix never exists; the gradients are formed during the
- * same pass as the loss.
+ * reduction.  It walks the batch rows in chunks of chunk_rows rows and forms
+ * the gradients during the same pass as the loss.  The fp32 logits of a chunk
+ * exist only in registers, one 256 x 256 output tile at a time, and are never
+ * written to memory; what a chunk leaves in the workspace is its tile of
+ * exp(z - block max), rewritten in place into dL, in the input dtype
+ * (chunk rows x V).  Which rows' dL the workspace holds at once depends on
+ * the grad_W accumulation (lce_acc_policy, lce_desc.group_rows):
+ *   - ACCURATE with group_rows = 0 (the default) keeps the dL of a group of
+ *     consecutive chunks, up to 4 D / sizeof(element) rows (as many bytes as
+ *     an fp32 V x D accumulator), and runs one grad_X and one grad_W GEMM
+ *     over the whole group.  When that covers every row (e.g. N = 8192,
+ *     D = 4096, bf16: one group of N rows, 2.1 GB of bf16 dL), no fp32
+ *     accumulator is needed and grad_W is rounded once from fp32 registers.
+ *   - ACCURATE with group_rows <= chunk rows keeps one chunk's dL: both
+ *     gradient GEMMs consume it right after its finalize, and grad_W is
+ *     carried across chunks in an fp32 V x D accumulator in the workspace,
+ *     rounded once after the last chunk.
+ *   - COMPACT keeps one chunk's dL and adds each chunk's grad_W into the
+ *     16-bit output (no V x D accumulator).
  *
  * Sources: the PyTorch module source torch/nn/modules/linear_cross_entropy.py
  * (custom ops _linear_cross_entropy_batch_chunked and
@@ -91,9 +107,12 @@ typedef enum { LCE_F32 = 0, LCE_BF16 = 1, LCE_F16 = 2 } lce_dtype;
 typedef enum { LCE_MEAN = 0, LCE_SUM = 1, LCE_NONE = 2 } lce_reduction;
 
 /* How grad_W is accumulated across chunks when the input dtype is bf16 or
- * fp16 (the pages' acc_policy).  ACCURATE keeps an fp32 V x D accumulator in
- * the workspace across all chunks and rounds once at the end; COMPACT adds
- * each chunk's fp32 tile straight into the 16-bit grad_W (one rounding
+ * fp16 (torch.nn.LinearCrossEntropyOptions page: acc_policy "accurate" /
+ * "compact").  ACCURATE accumulates grad_W in fp32 over every row and rounds
+ * it once: within a group of chunks in the GEMM's fp32 registers, across
+ * groups in an fp32 V x D accumulator in the workspace (see the file comment
+ * and lce_desc.group_rows for how many chunks form a group).  COMPACT adds
+ * each chunk's fp32 product straight into the 16-bit grad_W (one rounding
  * per chunk) and needs no V x D accumulator.  Identical for fp32 input. */
 typedef enum { LCE_ACCURATE = 0, LCE_COMPACT = 1 } lce_acc_policy;
 
@@ -134,6 +153,16 @@ typedef struct {
   uint32_t flags;        /* LCE_GRAD_* | LCE_ARGMAX | LCE_ACCUMULATE */
   int64_t chunk_divisor; /* "aspect_ratio:N" with LCE_CHUNK_ASPECT_RATIO: the
                             N >= 1 (0 is read as 1); ignored otherwise */
+  int64_t group_rows;    /* ACCURATE with 16-bit inputs only: at most this
+                            many rows of dL are held for one grad_W GEMM
+                            (rounded down to whole chunks, at least one
+                            chunk).  0 = up to 4 D / sizeof(element) rows.
+                            A value <= the chunk rows gives one chunk per
+                            group: the per-chunk path with an fp32 V x D
+                            accumulator carried across chunks.  Ignored by
+                            COMPACT, fp32 inputs and non-mixed layouts.
+                            An implementation choice (memory against
+                            speed), not an option of the pages. */
 } lce_desc;
 
 /* Buffers of one call.  All pointers are device pointers. */
@@ -173,7 +202,11 @@ typedef struct {
 } lce_io;
 
 /* Validate `d`, resolve the chunk size and build a handle.  Host only.
- * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, bad
+ * The validation follows the PyTorch module source
+ * torch/nn/modules/linear_cross_entropy.py (_ChunkContext.build), the chunk
+ * size the torch.nn.LinearCrossEntropyOptions page (batch_chunk_size,
+ * chunking_method "aspect_ratio").
+ * Errors: INVALID_ARG (N < 0, D < 1, V < 1, chunk_rows < -1, group_rows < 0, bad
  * acc_policy / has_bias, unknown flag bits, NULL pointers), DTYPE,
  * UNSUPPORTED (a reduction outside lce_reduction, the module source's
  * NotImplementedError; acc_dtype neither LCE_F32 nor dtype; D not a multiple
@@ -181,14 +214,24 @@ typedef struct {
  * without a bias is INVALID_ARG. */
 LCE_API lce_status lce_create(const lce_desc* d, lce_handle** out);
 
-/* Bytes of device workspace lce_forward_backward needs (host only). */
+/* Bytes of device workspace lce_forward_backward needs (host only).  An
+ * implementation entry with no counterpart on the pages (their op allocates
+ * its scratch itself); the layout is private.  Errors: INVALID_ARG (NULL). */
 LCE_API lce_status lce_workspace_size(const lce_handle* h, size_t* bytes);
 
-/* The resolved rows per chunk (0 when N == 0) and the chunk count. */
+/* The resolved rows per chunk (0 when N == 0) and the chunk count (host
+ * only): the torch.nn.LinearCrossEntropyOptions page's batch_chunk_size as
+ * resolved by its chunking_method.  Either output may be NULL.  Errors:
+ * INVALID_ARG (NULL handle). */
 LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
                           int64_t* n_chunks);
 
-/* Enqueue the whole chunked forward+backward on `stream`.
+/* Enqueue the whole chunked forward+backward on `stream`: the batch-chunked
+ * accumulator of the PyTorch module source
+ * torch/nn/modules/linear_cross_entropy.py, with the weight, input and bias
+ * gradients of the PyTorch commit "Fix NJT linear_backward() memory usage"
+ * (linear_backward: grad_input = dL W, grad_weight = dL^T X,
+ * grad_bias = column sums of dL).
  *
  * Per-row weight g_n (the negated neg_weight_target of the pages), with
  * w_n = class_weight[t_n] (1 without class weights) on counted rows:
@@ -229,10 +272,14 @@ LCE_API lce_status lce_scale(const void* in, void* out, int32_t dtype, int64_t r
                              int64_t cols, const float* scale, int64_t scale_stride,
                              void* stream);
 
-/* Release the handle (NULL is accepted). */
+/* Release the handle (NULL is accepted).  Host only; an implementation
+ * entry (the pages' op has no handle).  Always LCE_OK. */
 LCE_API lce_status lce_destroy(lce_handle* h);
 
-/* Bytes of device workspace for lce_ce_inplace on N rows. */
+/* Bytes of device workspace for lce_ce_inplace on N rows (host only): four
+ * N-element row arrays and three counters.  An implementation entry (the
+ * pages' kernel allocates nothing here, the caller's buffer replaces torch's
+ * allocator).  Errors: INVALID_ARG (NULL, N < 0, V < 1). */
 LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
 
 /* Standalone softmax cross-entropy on precomputed fp32 logits [N, V]
@@ -259,14 +306,18 @@ enum {
   LCE_K_FINALIZE = 3,   /* dL = g (softmax - onehot) in place, dL^T, bias partials */
   LCE_K_GEMM_X = 4,     /* grad_X = dL . W (split-K partials) */
   LCE_K_SPLIT_SUM = 5,  /* split-K reduction into grad_X */
-  LCE_K_TRANSPOSE = 6,  /* W^T once per call, X_chunk^T per chunk */
+  LCE_K_TRANSPOSE = 6,  /* W^T once per call (fp32 inputs with grad_X); X^T
+                           of a grad_W group once per group when the group's
+                           dL stays in T (16-bit inputs), else X_chunk^T per
+                           chunk beside the staged dL^T */
   LCE_K_GEMM_W = 7,     /* grad_W += dL^T . X_chunk */
   LCE_K_BIAS = 8,       /* grad_b reduction */
   LCE_K_LOSS = 9,       /* final loss reduction, zero fills */
   LCE_K_COUNT = 10
 };
 
-/* Timing hook for benchmarks.  While enabled, every launch of a kernel class
+/* Timing hook for benchmarks (an implementation entry: the pages measure
+ * with a profiler, Liger-Kernel issue #343's proton run).  While enabled, every launch of a kernel class
  * whose bit (1u << LCE_K_*) is in `kernel_mask` is bracketed by two
  * hipEventRecord calls on the call's stream (events come from a fixed pool
  * created here; launches beyond the pool are not timed).  mask 0 disables
@@ -278,10 +329,12 @@ LCE_API lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask);
  * pointer may be NULL), and restart the count. */
 LCE_API lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code (an implementation entry; the
+ * pages raise Python exceptions instead of returning codes). */
 LCE_API const char* lce_status_string(lce_status s);
 
-/* Text of the last HIP error seen by this thread's calls ("" if none). */
+/* Text of the last HIP error seen by this thread's calls ("" if none); an
+ * implementation entry that complements LCE_ERR_HIP. */
 LCE_API const char* lce_last_error(void);
 
 #ifdef __cplusplus

@@ -32,7 +32,7 @@ class lce_desc(ctypes.Structure):
     _fields_ = [("N", c_int64), ("D", c_int64), ("V", c_int64), ("ignore_index", c_int64),
                 ("chunk_rows", c_int64), ("dtype", c_int32), ("acc_dtype", c_int32),
                 ("has_bias", c_int32), ("reduction", c_int32), ("acc_policy", c_int32),
-                ("flags", c_uint32), ("chunk_divisor", c_int64)]
+                ("flags", c_uint32), ("chunk_divisor", c_int64), ("group_rows", c_int64)]
 
 
 class lce_io(ctypes.Structure):

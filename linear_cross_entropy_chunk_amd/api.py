@@ -6,6 +6,11 @@ The argument checks mirror the pages' Python validation that a C pointer
 cannot carry: the target dtype (int64, a TypeError on the pages) and the bias
 shape (a RuntimeError on the pages). Per-class weights, when given, are one
 float32 value per class on the problem's device.
+
+Every tensor whose pointer reaches a kernel is checked on the host before
+anything is enqueued: its device (the op's), its shape and its contiguity.
+A host tensor or a short buffer would otherwise be read by the kernels out
+of bounds.
 """
 from __future__ import annotations
 
@@ -33,6 +38,20 @@ def _check_class_weight(w, V: int, device: torch.device) -> None:
                            f"on {device}")
 
 
+def _check_tensor(name: str, x, shape: tuple, dtype, device: torch.device) -> None:
+    """x must be a contiguous tensor of `shape` and `dtype` on `device`."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(x).__name__}")
+    if x.device != device:
+        raise RuntimeError(f"{name} is on {x.device}, expected {device}")
+    if tuple(x.shape) != tuple(shape):
+        raise RuntimeError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if x.dtype != dtype:
+        raise RuntimeError(f"{name} must be {dtype}, got {x.dtype}")
+    if not x.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+
+
 def _device(device) -> torch.device:
     d = torch.device(device)
     if d.type == "cuda" and d.index is None:
@@ -50,7 +69,8 @@ class LinearCrossEntropy:
                  reduction: str = "mean", ignore_index: int = -100, chunk_rows: int = 0,
                  acc_policy: str = "accurate", grad_x: bool = True, grad_w: bool = True,
                  grad_b: bool | None = None, argmax: bool = False, device="cuda",
-                 chunk_divisor: int = 1, accumulate: bool = False, acc_dtype=None):
+                 chunk_divisor: int = 1, accumulate: bool = False, acc_dtype=None,
+                 group_rows: int = 0):
         if dtype not in _DTYPES:
             raise TypeError(f"unsupported dtype {dtype}")
         if reduction not in _REDUCTIONS:
@@ -74,7 +94,7 @@ class LinearCrossEntropy:
                                dtype=_DTYPES[dtype], acc_dtype=_DTYPES[acc], has_bias=int(bias),
                                reduction=_REDUCTIONS[reduction],
                                acc_policy=_POLICIES[acc_policy], flags=flags,
-                               chunk_divisor=chunk_divisor)
+                               chunk_divisor=chunk_divisor, group_rows=group_rows)
         self.handle = B.lce_create(self.desc)
         self.ws_bytes = B.lce_workspace_size(self.handle)
         self.chunk_rows, self.n_chunks = B.lce_chunk_info(self.handle)
@@ -121,22 +141,21 @@ class LinearCrossEntropy:
         if tuple(X.shape) != (N, D) or tuple(W.shape) != (V, D) or tuple(t.shape) != (N,):
             raise RuntimeError(f"shape mismatch: X{tuple(X.shape)} W{tuple(W.shape)} "
                                f"t{tuple(t.shape)} vs planned N={N} D={D} V={V}")
-        for name, x in (("X", X), ("W", W), ("b", b)):
-            if x is not None and (x.dtype != self.dtype or not x.is_contiguous()
-                                  or x.device != self.device):
-                raise RuntimeError(f"{name} must be a contiguous {self.dtype} tensor on "
-                                   f"{self.device}")
-        if grad_output is not None and (grad_output.dtype != torch.float32
-                                        or tuple(grad_output.shape) != (N,)):
-            raise RuntimeError("grad_output must be a float32 tensor of shape (N,)")
+        _check_tensor("X", X, (N, D), self.dtype, self.device)
+        _check_tensor("W", W, (V, D), self.dtype, self.device)
+        _check_tensor("target", t, (N,), torch.int64, self.device)
+        if b is not None:
+            _check_tensor("b", b, (V,), self.dtype, self.device)
+        if grad_output is not None:
+            _check_tensor("grad_output", grad_output, (N,), torch.float32, self.device)
 
-    def check_outputs(self, out: dict) -> None:
+    def check_outputs(self, out: dict, grads: bool = True) -> None:
         """Caller-supplied outputs: the requested gradients with their shapes."""
         N, D, V = self.shape
         want = (("grad_X", B.LCE_GRAD_X, (N, D)), ("grad_W", B.LCE_GRAD_W, (V, D)),
                 ("grad_b", B.LCE_GRAD_B, (V,)))
         for name, flag, shape in want:
-            if not self.flags & flag:
+            if not grads or not self.flags & flag:
                 continue
             g = out.get(name)
             if (g is None or tuple(g.shape) != shape or g.dtype != self.dtype
@@ -144,10 +163,13 @@ class LinearCrossEntropy:
                 raise RuntimeError(f"out[{name!r}] must be a contiguous {self.dtype} tensor of "
                                    f"shape {shape} on {self.device}")
         for name, n, dt in (("loss", N if self.reduction == "none" else 1, torch.float32),
-                            ("n_valid", 1, torch.int64), ("n_bad", 1, torch.int64)):
+                            ("n_valid", 1, torch.int64), ("n_bad", 1, torch.int64),
+                            ("argmax", N, torch.int32)):
             x = out.get(name)
-            if x is not None and (x.numel() != n or x.dtype != dt or x.device != self.device):
-                raise RuntimeError(f"out[{name!r}] must hold {n} {dt} on {self.device}")
+            if x is not None and (x.numel() != n or x.dtype != dt or x.device != self.device
+                                  or not x.is_contiguous()):
+                raise RuntimeError(f"out[{name!r}] must hold {n} contiguous {dt} on "
+                                   f"{self.device}")
 
     def make_io(self, X, W, t, b=None, *, out: dict, grad_output=None,
                 grad_scale: float = 1.0, class_weight=None) -> B.lce_io:
@@ -174,8 +196,7 @@ class LinearCrossEntropy:
             full = self.make_outputs(grads=False)   # loss, counts, argmax the caller left out
             full.update(out)
             out = full
-            if grads:
-                self.check_outputs(out)
+            self.check_outputs(out, grads)
         io = self.make_io(X, W, t, b, out=out, grad_output=grad_output, grad_scale=grad_scale,
                           class_weight=class_weight)
         self.run_io(io)
@@ -186,14 +207,16 @@ def linear_cross_entropy(X, W, t, b=None, *, reduction: str = "mean", ignore_ind
                          chunk_rows: int = 0, acc_policy: str = "accurate",
                          grad_output=None, grad_scale: float = 1.0, argmax: bool = False,
                          grad_x: bool = True, grad_w: bool = True,
-                         grad_b: bool | None = None, class_weight=None) -> dict:
+                         grad_b: bool | None = None, class_weight=None,
+                         group_rows: int = 0) -> dict:
     """One-shot chunked forward+backward; returns loss, gradients, counts."""
     N, D = X.shape
     V = W.shape[0]
     op = LinearCrossEntropy(N, D, V, X.dtype, bias=b is not None, reduction=reduction,
                             ignore_index=ignore_index, chunk_rows=chunk_rows,
                             acc_policy=acc_policy, grad_x=grad_x, grad_w=grad_w,
-                            grad_b=grad_b, argmax=argmax, device=X.device)
+                            grad_b=grad_b, argmax=argmax, device=X.device,
+                            group_rows=group_rows)
     return op(X, W, t, b, grad_output=grad_output, grad_scale=grad_scale,
               class_weight=class_weight)
 
@@ -222,9 +245,8 @@ class CrossEntropyInplace:
         _check_class_weight(class_weight, self.V, self.device)
         if t.dtype != torch.int64:
             raise TypeError(f"target dtype must be torch.int64, got {t.dtype}")
-        if (logits.dtype != torch.float32 or not logits.is_contiguous()
-                or tuple(logits.shape) != (self.N, self.V)):
-            raise RuntimeError("logits must be a contiguous float32 tensor of shape (N, V)")
+        _check_tensor("logits", logits, (self.N, self.V), torch.float32, self.device)
+        _check_tensor("target", t, (self.N,), torch.int64, self.device)
         B.lce_ce_inplace(logits.data_ptr(), t.data_ptr(), _ptr(class_weight), self.N, self.V,
                          self.ignore_index,
                          _REDUCTIONS[self.reduction], grad_scale, self.loss.data_ptr(),

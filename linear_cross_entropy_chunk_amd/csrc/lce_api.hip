@@ -129,15 +129,20 @@ void plan(lce_handle* h) {
   h->accum = d.flags & LCE_ACCUMULATE;
   h->want_any = h->want_x || h->want_w || h->want_b;
 
-  // grad_W groups.  The dL^T of `grp` consecutive chunks is staged and one
-  // GEMM with K = grp * c_pad rows forms their grad_W contribution, so the
-  // accumulator is touched once per group instead of once per chunk.  ACCURATE
-  // stages up to as many bytes as the fp32 V x D accumulator it saves (K up to
-  // 4 D / element size); COMPACT keeps one chunk per group (least memory).
-  // A non-mixed 16-bit layout (acc_dtype = the input dtype) accumulates the
-  // gradients in the input dtype chunk by chunk: COMPACT's grouping.
+  // grad_W groups.  The dL of `grp` consecutive chunks stays in T (or is
+  // staged as dL^T) and one GEMM with K = grp * c_pad rows forms their grad_W
+  // contribution, so the accumulator is touched once per group instead of
+  // once per chunk.  ACCURATE holds, by default, up to as many bytes of dL as
+  // the fp32 V x D accumulator it saves (K up to 4 D / element size), or at
+  // most group_rows rows when the descriptor sets it (group_rows <= the chunk
+  // rows gives one chunk per group: each chunk's dL is consumed by both
+  // gradient GEMMs right after its finalize, and grad_W is carried across
+  // chunks in an fp32 accumulator).  COMPACT keeps one chunk per group (least
+  // memory).  A non-mixed 16-bit layout (acc_dtype = the input dtype)
+  // accumulates the gradients in the input dtype chunk by chunk: COMPACT's
+  // grouping.
   const bool accurate = d.acc_policy == LCE_ACCURATE && !(h->half && d.acc_dtype == d.dtype);
-  const int64_t k_max = 4 * d.D / h->esize;
+  const int64_t k_max = d.group_rows > 0 ? d.group_rows : 4 * d.D / h->esize;
   h->grp = accurate ? std::max<int64_t>(1, k_max / h->c_pad) : 1;
   h->grp = std::max<int64_t>(1, std::min<int64_t>(h->grp, std::max<int64_t>(h->n_chunks, 1)));
   h->k_grp = h->grp * h->c_pad;
@@ -228,7 +233,7 @@ lce_status lce_create(const lce_desc* d, lce_handle** out) {
   if (!d || !out) return LCE_ERR_INVALID_ARG;
   *out = nullptr;
   if (d->N < 0 || d->D < 1 || d->V < 1 || d->chunk_rows < LCE_CHUNK_ALL ||
-      d->chunk_divisor < 0)
+      d->chunk_divisor < 0 || d->group_rows < 0)
     return LCE_ERR_INVALID_ARG;
   if (d->dtype != LCE_F32 && d->dtype != LCE_BF16 && d->dtype != LCE_F16) return LCE_ERR_DTYPE;
   // an unknown reduction is the pages' NotImplementedError

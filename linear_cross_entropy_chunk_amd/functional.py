@@ -224,10 +224,11 @@ def linear_cross_entropy(input, linear_weight, target, linear_bias=None, weight=
     """cross_entropy(input @ linear_weight.T + linear_bias, target) without
     the logits, differentiable in input, linear_weight and linear_bias.
 
-    input (*, D) float32 or bfloat16, linear_weight (V, D), target (*)
-    int64, linear_bias (V,) or None, weight (V,) per-class weights or None.
-    Returns a float32 scalar (mean / sum) or the float32 per-row loss of
-    target's shape (none)."""
+    input (*, D) float32, bfloat16 or float16, linear_weight (V, D), target
+    (*) int64, linear_bias (V,) or None, weight (V,) per-class weights or
+    None.  Returns the loss in the input dtype (the module source's output
+    contract: the fp32 loss rounded once): a scalar for mean / sum, the
+    per-row loss of target's shape for none."""
     opts = options or LinearCrossEntropyOptions()
     _check_args(input, linear_weight, target, linear_bias, weight, reduction, label_smoothing)
     lead = tuple(target.shape)

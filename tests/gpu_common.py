@@ -12,6 +12,8 @@ leaves a wide margin); a gradient carries one fp16 rounding of dL and one of
 the output, together at most ~2 x 2^-11 ~ 1e-3 of max|G| when the target
 term dominates a row, so 5e-3 is about five times that bound.
   n_valid, n_bad  bit-exact
+  zero-weight rows (ignored, out-of-range target, class weight 0): per-row
+                  loss ('none') and grad_X row bit-exact 0
   argmax          bit-exact where the oracle's top-2 gap exceeds
                   1e-4 * max(1, |row max|); elsewhere the GPU's class must
                   lie within that margin of the row max (a valid near-tie).
@@ -122,10 +124,29 @@ def check_argmax(got, ref, gap, rowmax, z_at_got) -> int:
     return int(near.sum())
 
 
+def check_zero_rows(gpu: dict, ref: dict, reduction: str) -> int:
+    """Rows that weigh nothing (ignored, target out of range, or a class of
+    weight 0) give a per-row loss of exactly 0 ('none') and, where the row
+    weight g is exactly 0, a grad_X row of exactly 0: bit-exact, not within a
+    tolerance.  Returns the number of such rows."""
+    w = np.asarray(ref["w"])
+    zero = w == 0.0
+    if reduction == "none" and "loss" in gpu:
+        bad = np.nonzero(zero & (np.asarray(gpu["loss"]) != 0.0))[0]
+        assert bad.size == 0, f"per-row loss not exactly 0 on zero-weight rows {bad[:10]}"
+    if "grad_X" in gpu and gpu["grad_X"].shape[0]:
+        gz = np.asarray(ref["g"]) == 0.0
+        bad = np.nonzero(gz & np.any(gpu["grad_X"] != 0.0, axis=1))[0]
+        assert bad.size == 0, f"grad_X row not exactly 0 on rows of weight 0 {bad[:10]}"
+    return int(zero.sum())
+
+
 def check_all(gpu: dict, ref: dict, dt: str, reduction: str, z=None, grads="xwb") -> dict:
     errs = {"loss": check_loss(gpu["loss"], ref["loss"], dt, reduction)}
     assert int(gpu["n_valid"][0]) == ref["n_valid"]
     assert int(gpu["n_bad"][0]) == ref["n_bad"]
+    if "w" in ref:
+        errs["zero_rows"] = check_zero_rows(gpu, ref, reduction)
     for key, flag in (("grad_X", "x"), ("grad_W", "w"), ("grad_b", "b")):
         if key in gpu and flag in grads:
             errs[key] = check_grad(gpu[key], ref[key], dt, key)
@@ -152,4 +173,4 @@ def run_ce(z: np.ndarray, t: np.ndarray, *, reduction: str = "mean", ignore_inde
 
 
 __all__ = ["TOL", "log", "require_gpu", "run_gpu", "check_all", "check_loss", "check_grad",
-           "check_argmax", "rel_err", "run_ce", "oracle"]
+           "check_argmax", "check_zero_rows", "rel_err", "run_ce", "oracle"]

@@ -202,3 +202,86 @@ def test_torch_wrapper_type_checks():
         op.check_inputs(X, W, torch.zeros(4, dtype=torch.int32), torch.zeros(10))
     with pytest.raises(RuntimeError):
         op.check_inputs(X, W, torch.zeros(4, dtype=torch.int64), torch.zeros(9))
+
+
+def _ws(**kw) -> int:
+    h = B.lce_create(_desc(**kw))
+    try:
+        return B.lce_workspace_size(h)
+    finally:
+        B.lce_destroy(h)
+
+
+def test_group_rows_selects_the_per_chunk_path(lib):
+    """group_rows caps the rows of dL held for one grad_W GEMM.  At the
+    large-vocabulary shape (N=8192, D=4096, V=128256, bf16, 2048-row chunks):
+    the default groups all four chunks (T holds all 8192 rows of dL, no fp32
+    accumulator); group_rows=2048 holds one chunk of dL and an fp32 V x D
+    accumulator; 4096 holds two chunks and the accumulator; compact ignores
+    it.  Small regions (row statistics, staged X^T) stay below 0.2 GB."""
+    N, D, V, c = 8192, 4096, 128256, 2048
+    kw = dict(N=N, D=D, V=V, chunk_rows=c, dtype=B.LCE_BF16, has_bias=0,
+              flags=B.LCE_GRAD_X | B.LCE_GRAD_W)
+    slack = 0.2e9
+    grouped = _ws(**kw)
+    assert N * V * 2 <= grouped < N * V * 2 + slack
+    assert _ws(group_rows=0, **kw) == grouped
+    assert _ws(group_rows=N, **kw) == grouped
+    acc = V * D * 4
+    per_chunk = _ws(group_rows=c, **kw)
+    assert c * V * 2 + acc <= per_chunk < c * V * 2 + acc + slack
+    assert _ws(group_rows=1, **kw) == per_chunk          # below a chunk: one chunk
+    assert _ws(group_rows=c + 100, **kw) == per_chunk    # rounded down to whole chunks
+    two = _ws(group_rows=2 * c, **kw)
+    assert 2 * c * V * 2 + acc <= two < 2 * c * V * 2 + acc + slack
+    compact = _ws(acc_policy=B.LCE_COMPACT, **kw)
+    assert _ws(acc_policy=B.LCE_COMPACT, group_rows=c, **kw) == compact
+    assert compact < c * V * 2 + slack
+    assert B.lce_create_status(_desc(group_rows=-1)) == B.LCE_ERR_INVALID_ARG
+
+
+def test_torch_wrapper_device_shape_and_layout_checks():
+    """Every tensor whose pointer reaches a kernel is checked on the host:
+    device, shape, dtype and contiguity (a host or short target buffer
+    would otherwise be read by the kernels).  'meta' tensors stand for the
+    op's device here, where no GPU exists."""
+    import torch
+    from linear_cross_entropy_chunk_amd.api import CrossEntropyInplace, LinearCrossEntropy
+    meta = torch.device("meta")
+    op = LinearCrossEntropy.__new__(LinearCrossEntropy)
+    op.shape, op.dtype, op.bias, op.device = (4, 8, 10), torch.float32, False, meta
+    X, W = torch.empty(4, 8, device=meta), torch.empty(10, 8, device=meta)
+    t = torch.empty(4, dtype=torch.int64, device=meta)
+    op.check_inputs(X, W, t)                                   # all good: no error
+    with pytest.raises(RuntimeError, match="target is on cpu"):
+        op.check_inputs(X, W, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(RuntimeError, match="contiguous"):
+        op.check_inputs(X, W, torch.empty(8, dtype=torch.int64, device=meta)[::2])
+    with pytest.raises(RuntimeError):
+        op.check_inputs(X, W, torch.empty(3, dtype=torch.int64, device=meta))
+    with pytest.raises(RuntimeError, match="X is on cpu"):
+        op.check_inputs(torch.zeros(4, 8), W, t)
+    with pytest.raises(RuntimeError, match="contiguous"):
+        op.check_inputs(torch.empty(8, 4, device=meta).t(), W, t)
+    with pytest.raises(RuntimeError, match="grad_output is on cpu"):
+        op.check_inputs(X, W, t, grad_output=torch.zeros(4))
+    with pytest.raises(RuntimeError, match="grad_output must have shape"):
+        op.check_inputs(X, W, t, grad_output=torch.empty(5, device=meta))
+    with pytest.raises(RuntimeError, match="contiguous"):
+        op.check_inputs(X, W, t, grad_output=torch.empty(8, device=meta)[::2])
+    with pytest.raises(RuntimeError, match="grad_output must be torch.float32"):
+        op.check_inputs(X, W, t, grad_output=torch.empty(4, dtype=torch.float16, device=meta))
+
+    ce = CrossEntropyInplace.__new__(CrossEntropyInplace)
+    ce.N, ce.V, ce.device, ce.reduction, ce.ignore_index = 4, 16, meta, "mean", -100
+    z = torch.empty(4, 16, device=meta)
+    with pytest.raises(RuntimeError, match="target is on cpu"):
+        ce(z, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(RuntimeError, match="logits is on cpu"):
+        ce(torch.zeros(4, 16), t)
+    with pytest.raises(RuntimeError, match="target must have shape"):
+        ce(z, torch.empty(3, dtype=torch.int64, device=meta))
+    with pytest.raises(RuntimeError, match="contiguous"):
+        ce(z, torch.empty(8, dtype=torch.int64, device=meta)[::2])
+    with pytest.raises(RuntimeError, match="logits must have shape"):
+        ce(torch.empty(4, 12, device=meta), t)

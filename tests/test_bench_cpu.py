@@ -84,3 +84,22 @@ def test_no_copy_calibration_means_no_traffic(tmp_path, traffic_file):
     _write_csv(fetch, "FETCH_SIZE", [("k_logits_lse", 10.0)])
     _write_csv(write, "WRITE_SIZE", [("k_logits_lse", 10.0)])
     assert bench.summarize_counters(str(fetch), str(write), "w1", "cmd") == {}
+
+
+def test_host_cpu_record():
+    """The CPU baseline states the host's logical CPU count and model next to
+    the threads the oracle used."""
+    h = bench.host_cpu()
+    assert h["nproc"] == os.cpu_count() and h["nproc"] >= 1
+    assert h["nproc_usable"] is None or 1 <= h["nproc_usable"] <= h["nproc"]
+    assert "cpu_model" in h
+
+
+def test_bench_flags_parse():
+    """The default line's extra records can be switched off; --group-rows
+    reaches the op."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0
+    for flag in ("--group-rows", "--no-per-chunk", "--no-ce"):
+        assert flag in r.stdout

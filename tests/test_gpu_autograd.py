@@ -106,6 +106,8 @@ def test_none_reduction_recomputes_in_backward(dt):
                                       reduction="none", upstream=u, class_weight=cw)
     tol = TOL[dt]
     assert rel_err(_np(loss).reshape(-1), ref["loss"]) <= tol["loss"] + OUT_ROUND[dt]
+    zero = ref["w"] == 0.0                  # ignored rows and zero-weight classes
+    assert zero.any() and np.all(_np(loss).reshape(-1)[zero] == 0.0)
     assert rel_err(_np(X.grad).reshape(-1, X.shape[-1]), ref["grad_X"]) <= tol["grad"]
     assert rel_err(_np(W.grad), ref["grad_W"]) <= tol["grad"]
     assert rel_err(_np(b.grad), ref["grad_b"]) <= tol["grad"]

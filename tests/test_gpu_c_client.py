@@ -109,6 +109,9 @@ def test_c_client_ce_inplace(V, reduction, tmp_path):
     assert nv == N - 2
     assert rel_err(loss, np.atleast_1d(ref_loss)) <= 1e-5
     assert rel_err(dl, ref_dl) <= 1e-4
+    assert np.all(dl[[0, 9]] == 0.0)
+    if reduction == "none":
+        assert np.all(loss[[0, 9]] == 0.0)     # ignored rows: exactly 0
     py_loss, py_nv, py_dl = run_ce(z, t, reduction=reduction)
     np.testing.assert_array_equal(loss, py_loss)
     np.testing.assert_array_equal(dl, py_dl)

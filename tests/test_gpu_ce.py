@@ -25,6 +25,7 @@ def test_ce_inplace_matches_oracle(V, reduction):
     assert nv == N - 2
     if reduction == "none":
         assert rel_err(loss, ref_loss) <= 1e-5
+        assert np.all(loss[[0, 50]] == 0.0)      # ignored rows: exactly 0
     else:
         assert abs(loss[0] - ref_loss) <= 1e-5 * abs(ref_loss)
     assert rel_err(dl, ref_dl) <= 1e-4
@@ -63,6 +64,7 @@ def test_ce_long_rows_on_chip(V, reduction):
     assert nv == N - 1
     if reduction == "none":
         assert rel_err(loss, ref_loss) <= 1e-5
+        assert loss[4] == 0.0                    # the ignored row: exactly 0
     else:
         assert abs(loss[0] - ref_loss) <= 1e-5 * abs(ref_loss)
     assert rel_err(dl, ref_dl) <= 1e-4

@@ -1,5 +1,5 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times.  The oracle evaluates the plain definition on sampled
+benchmark times (and the per-chunk path beside it).  The oracle evaluates the plain definition on sampled
 outputs: per-row loss, argmax and grad_X on sampled rows (each depends on its
 row only), grad_W / grad_b on sampled classes (sums over every row, so the
 oracle walks all rows in blocks), and the mean loss over all rows; plus
@@ -39,7 +39,34 @@ def _sample_cols(V, t, k=24, seed=1):
     return np.array(sorted(cols))
 
 
-def _run_fused(cfg, inputs, upstream=None, reduction=None):
+def _tile_cols(V, t, seed=2):
+    """Whole 256-class tiles of grad_W (one workgroup's output tile each): the
+    first, the last, the tile of the most frequent target, and a random one;
+    when two of these coincide, the tile of the next most frequent target
+    takes the place, so there are always four distinct tiles."""
+    n_tiles = -(-V // 256)
+    rng = np.random.default_rng(seed)
+    tiles = [0, n_tiles - 1]
+    valid = t[t >= 0]
+    vals, cnt = np.unique(valid, return_counts=True)
+    ranked = [int(v) // 256 for v in vals[np.argsort(-cnt, kind="stable")]]
+    for tile in ranked:
+        if tile not in tiles:
+            tiles.append(tile)
+            break
+    while len(tiles) < 4:
+        tile = int(rng.integers(1, n_tiles - 1))
+        if tile not in tiles:
+            tiles.append(tile)
+    cols = np.concatenate([np.arange(256 * k, min(V, 256 * (k + 1))) for k in sorted(tiles)])
+    return sorted(tiles), cols
+
+
+def _run_fused(cfg, inputs, cols, upstream=None, *, argmax=True, group_rows=0):
+    """One call in the benchmark's launch configuration (argmax=False is the
+    benchmark's own kernel instantiation).  grad_W comes back on the sampled
+    classes only, with its per-feature class sums and absolute sums taken on
+    the device."""
     dt = TORCH_DT[cfg.dtype]
     dev = torch.device("cuda", 0)
     X = torch.from_numpy(inputs["X"]).to(dev).to(dt)
@@ -47,14 +74,25 @@ def _run_fused(cfg, inputs, upstream=None, reduction=None):
     b = None if inputs["b"] is None else torch.from_numpy(inputs["b"]).to(dev).to(dt)
     t = torch.from_numpy(inputs["t"]).to(dev)
     op = LinearCrossEntropy(cfg.N, cfg.D, cfg.V, dt, bias=b is not None,
-                            reduction=reduction or cfg.reduction, chunk_rows=cfg.chunk_rows,
-                            acc_policy="accurate", argmax=True, device=dev)
+                            reduction=cfg.reduction, chunk_rows=cfg.chunk_rows,
+                            acc_policy="accurate", argmax=argmax, device=dev,
+                            group_rows=group_rows)
     u = None if upstream is None else torch.from_numpy(upstream).to(dev)
     out = op(X, W, t, b, grad_output=u)
     torch.cuda.synchronize()
-    res = {k: (v.cpu().numpy() if v.dtype in (torch.int32, torch.int64)
-               else v.float().cpu().numpy().astype(np.float64)) for k, v in out.items()}
-    res["chunk_rows"] = op.chunk_rows
+    res = {"chunk_rows": op.chunk_rows, "ws_bytes": op.ws_bytes}
+    for k, v in out.items():
+        if k == "grad_W":
+            gw = v.float()
+            res["grad_W_cols"] = gw[torch.from_numpy(cols).to(dev)].cpu().numpy().astype(
+                np.float64)
+            res["grad_W_colsum"] = gw.sum(0).cpu().numpy().astype(np.float64)
+            res["grad_W_abssum"] = gw.abs().sum(0).cpu().numpy().astype(np.float64)
+            del gw
+        elif v.dtype in (torch.int32, torch.int64):
+            res[k] = v.cpu().numpy()
+        else:
+            res[k] = v.float().cpu().numpy().astype(np.float64)
     del X, W, b, t, out, op
     torch.cuda.empty_cache()
     return res
@@ -83,45 +121,66 @@ def _check_rows(gpu, inputs, rows, g, W64, tol, key_loss="loss_rows"):
                          grad_x=True, return_z=True)
     e_gx = rel_err(gpu["grad_X"][rows], r["grad_X"])
     assert e_gx <= tol["grad"], f"grad_X rows error {e_gx:.3e}"
-    z_at = r["z"][np.arange(len(rows)), gpu["argmax"][rows]]
-    near = check_argmax(gpu["argmax"][rows], r["argmax"], r["top2_gap"], r["rowmax"], z_at)
+    near = None
+    if "argmax" in gpu:
+        z_at = r["z"][np.arange(len(rows)), gpu["argmax"][rows]]
+        near = check_argmax(gpu["argmax"][rows], r["argmax"], r["top2_gap"], r["rowmax"], z_at)
     return r, e_gx, near
+
+
+def _check_large_vocab(gpu, what, inputs, rows, g, W64, tol, cols, L, gw, ignored):
+    """One GPU result of the large-vocabulary workload against the oracle."""
+    _, e_gx, near = _check_rows(gpu, inputs, rows, g, W64, tol)
+    assert np.all(gpu["grad_X"][ignored] == 0.0)
+    e_loss = abs(gpu["loss"][0] - L) / abs(L)
+    e_gw = rel_err(gpu["grad_W_cols"], gw)
+    log(f"{what}: loss {gpu['loss'][0]:.6f} vs {L:.6f} (rel {e_loss:.2e}); grad_X rows "
+        f"{e_gx:.2e}; grad_W classes {e_gw:.2e}; argmax near-ties {near}")
+    assert e_loss <= tol["loss"]
+    assert e_gw <= tol["grad"]
+    # every dL row sums to zero, so the class sum of grad_W vanishes
+    assert np.all(np.abs(gpu["grad_W_colsum"]) <= 2e-2 * gpu["grad_W_abssum"] + 1e-6)
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_large_vocab_full_size(dt):
     """N=8192, D=4096, V=128256, Zipf targets, 410 ignored, mean, 2048-row
-    chunks, fp32 grad_W accumulation: the benchmark's launch with bf16 inputs,
-    and the same workload with its inputs rounded to fp16 or kept in fp32."""
+    chunks, fp32 grad_W accumulation, with bf16 inputs and with the same draws
+    rounded to fp16 or kept in fp32.  bf16 runs three launches: the default
+    grouped path with the argmax output, the benchmark's own launch (no
+    argmax: the max-only epilogue), and the per-chunk path (group_rows = 2048:
+    one chunk per grad_W GEMM, an fp32 grad_W accumulator across chunks).
+    grad_W is compared on four whole 256-class tiles plus scattered classes."""
     require_gpu()
     cfg = dataclasses.replace(li.LARGE_VOCAB_BF16, dtype=dt)
     log(f"{cfg.name} with {dt} inputs: generating inputs")
     inputs = li.lce_inputs(cfg)
-    gpu = _run_fused(cfg, inputs)
-    assert gpu["chunk_rows"] == 2048
-    log("GPU done; oracle")
+    tiles, tcols = _tile_cols(cfg.V, inputs["t"])
+    cols = np.union1d(_sample_cols(cfg.V, inputs["t"]), tcols)
+    runs = {"grouped, argmax": _run_fused(cfg, inputs, cols)}
+    if dt == "bf16":
+        runs["grouped, benchmark launch"] = _run_fused(cfg, inputs, cols, argmax=False)
+        runs["per-chunk (group_rows=2048)"] = _run_fused(cfg, inputs, cols, argmax=False,
+                                                         group_rows=2048)
+        # the per-chunk path holds one chunk of dL and the fp32 accumulator
+        ws_grouped = runs["grouped, benchmark launch"]["ws_bytes"]
+        ws_chunk = runs["per-chunk (group_rows=2048)"]["ws_bytes"]
+        assert ws_grouped >= cfg.N * cfg.V * 2
+        assert ws_chunk >= cfg.V * cfg.D * 4 + 2048 * cfg.V * 2
+    log(f"GPU done ({len(runs)} launches); oracle; grad_W tiles {tiles}")
     valid, bad, nv, nb = oracle.target_masks(inputs["t"], cfg.V, -100)
-    assert int(gpu["n_valid"][0]) == nv == cfg.N - 410 and int(gpu["n_bad"][0]) == nb == 0
     g = oracle.row_weights(valid, "mean")
     W64 = inputs["W"].astype(np.float64)
     tol = TOL[cfg.dtype]
     rows = _sample_rows(cfg.N, inputs["t"])
-    _, e_gx, near = _check_rows(gpu, inputs, rows, g, W64, tol)
-    ign = inputs["t"] == -100
-    assert np.all(gpu["grad_X"][ign] == 0.0)
-    cols = _sample_cols(cfg.V, inputs["t"])
     loss_rows, gw, gb = _oracle_all_rows(inputs, g, cols, W64)
     L = oracle.reduce_loss(loss_rows, nv, "mean")
-    e_loss = abs(gpu["loss"][0] - L) / abs(L)
-    e_gw = rel_err(gpu["grad_W"][cols], gw)
-    log(f"loss {gpu['loss'][0]:.6f} vs {L:.6f} (rel {e_loss:.2e}); grad_X rows {e_gx:.2e}; "
-        f"grad_W cols {e_gw:.2e}; argmax near-ties {near}")
-    assert e_loss <= tol["loss"]
-    assert e_gw <= tol["grad"]
-    # every dL row sums to zero, so the class sum of grad_W vanishes
-    colsum = np.abs(gpu["grad_W"].sum(axis=0))
-    assert np.all(colsum <= 2e-2 * np.abs(gpu["grad_W"]).sum(axis=0) + 1e-6)
+    ignored = inputs["t"] == -100
+    for what, gpu in runs.items():
+        assert gpu["chunk_rows"] == 2048
+        assert int(gpu["n_valid"][0]) == nv == cfg.N - 410 and int(gpu["n_bad"][0]) == nb == 0
+        _check_large_vocab(gpu, what, inputs, rows, g, W64, tol, cols, L, gw, ignored)
 
 
 @pytest.mark.timeout(1100)
@@ -133,9 +192,10 @@ def test_none_reduction_full_size():
     cfg = li.NONE_BF16
     log(f"{cfg.name}: generating inputs")
     inputs = li.lce_inputs(cfg)
-    fwd = _run_fused(cfg, inputs)
+    cols = _sample_cols(cfg.V, inputs["t"])
+    fwd = _run_fused(cfg, inputs, cols)
     assert fwd["chunk_rows"] == 512
-    bwd = _run_fused(cfg, inputs, upstream=inputs["u"])
+    bwd = _run_fused(cfg, inputs, cols, upstream=inputs["u"])
     log("GPU done; oracle")
     valid, _, nv, _ = oracle.target_masks(inputs["t"], cfg.V, -100)
     assert int(bwd["n_valid"][0]) == nv == cfg.N
@@ -147,10 +207,9 @@ def test_none_reduction_full_size():
     e_lr = rel_err(fwd["loss"][rows], r["loss_rows"])
     assert e_lr <= tol["loss"], e_lr
     np.testing.assert_array_equal(fwd["argmax"], bwd["argmax"])
-    cols = _sample_cols(cfg.V, inputs["t"])
     loss_rows, gw, gb = _oracle_all_rows(inputs, g, cols, W64)
     e_all = rel_err(fwd["loss"], loss_rows)
-    e_gw = rel_err(bwd["grad_W"][cols], gw)
+    e_gw = rel_err(bwd["grad_W_cols"], gw)
     e_gb = rel_err(bwd["grad_b"][cols], gb)
     log(f"per-row loss {e_all:.2e}; grad_X rows {e_gx:.2e}; grad_W cols {e_gw:.2e}; "
         f"grad_b cols {e_gb:.2e}; argmax near-ties {near}")
