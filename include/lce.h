@@ -298,6 +298,28 @@ LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets,
                           float grad_scale, float* loss, int64_t* n_valid,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* Most rows lce_ce_inplace_noalloc accepts (its static scratch: 16 MiB and
+ * 256 bytes per device). */
+#define LCE_CE_NOALLOC_MAX_ROWS (1LL << 20)
+
+/* lce_ce_inplace without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * kernels as lce_ce_inplace; its scratch is a static device array of the
+ * library, one per GPU, that lives until the process ends.  It calls no
+ * hipMalloc / hipFree; the first call on a device looks the array's address
+ * up (hipGetSymbolAddress).  Every call on one GPU shares that GPU's array,
+ * so calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe.  Nothing in the array needs clearing between calls.
+ * Errors: as lce_ce_inplace, plus UNSUPPORTED for N > LCE_CE_NOALLOC_MAX_ROWS
+ * (the reason is in lce_last_error) and HIP if the address lookup fails. */
+LCE_API lce_status lce_ce_inplace_noalloc(float* logits, const int64_t* targets,
+                                          const float* class_weight, int64_t N, int64_t V,
+                                          int64_t ignore_index, int32_t reduction,
+                                          float grad_scale, float* loss, int64_t* n_valid,
+                                          void* stream);
+
 /* Kernel classes of lce_forward_backward, for the timing hook below. */
 enum {
   LCE_K_PREP = 0,       /* target counts and row weights */
@@ -333,8 +355,9 @@ LCE_API lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches)
  * pages raise Python exceptions instead of returning codes). */
 LCE_API const char* lce_status_string(lce_status s);
 
-/* Text of the last HIP error seen by this thread's calls ("" if none); an
- * implementation entry that complements LCE_ERR_HIP. */
+/* Text of the last HIP error seen by this thread's calls, or of the last
+ * size refusal of lce_ce_inplace_noalloc ("" if none); an implementation
+ * entry that complements the status codes. */
 LCE_API const char* lce_last_error(void);
 
 #ifdef __cplusplus

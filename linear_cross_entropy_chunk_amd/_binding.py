@@ -20,7 +20,9 @@ LCE_CHUNK_ASPECT_RATIO, LCE_CHUNK_ALL = 0, -1
 # Every exported function of include/lce.h.
 EXPORTS = ("lce_create", "lce_workspace_size", "lce_chunk_info", "lce_forward_backward",
            "lce_destroy", "lce_ce_workspace_size", "lce_ce_inplace", "lce_timing_enable",
-           "lce_timing_read", "lce_status_string", "lce_last_error", "lce_scale")
+           "lce_timing_read", "lce_status_string", "lce_last_error", "lce_scale",
+           "lce_ce_inplace_noalloc")
+LCE_CE_NOALLOC_MAX_ROWS = 1 << 20
 
 # kernel classes of the timing hook
 KERNEL_CLASSES = ("prep", "logits", "combine", "finalize", "gemm_x", "split_sum", "transpose",
@@ -74,6 +76,9 @@ def lib() -> ctypes.CDLL:
                                      c_void_p]
         L.lce_scale.argtypes = [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_void_p, c_int64,
                                 c_void_p]
+        L.lce_ce_inplace_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                             c_int64, c_int32, c_float, c_void_p, c_void_p,
+                                             c_void_p]
         L.lce_timing_enable.argtypes = [c_void_p, c_uint32]
         L.lce_timing_read.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int64)]
         L.lce_status_string.argtypes = [c_int32]
@@ -156,6 +161,23 @@ def lce_ce_inplace(logits: int, targets: int, class_weight: int | None, N: int, 
                                 reduction, grad_scale, c_void_p(loss), c_void_p(n_valid or None),
                                 c_void_p(workspace), ws_bytes, c_void_p(stream)),
            "lce_ce_inplace")
+
+
+def lce_ce_inplace_noalloc(logits: int, targets: int, class_weight: int | None, N: int, V: int,
+                           ignore_index: int, reduction: int, grad_scale: float, loss: int,
+                           n_valid: int, stream: int) -> None:
+    _check(lib().lce_ce_inplace_noalloc(c_void_p(logits), c_void_p(targets),
+                                        c_void_p(class_weight or None), N, V, ignore_index,
+                                        reduction, grad_scale, c_void_p(loss),
+                                        c_void_p(n_valid or None), c_void_p(stream)),
+           "lce_ce_inplace_noalloc")
+
+
+def lce_ce_inplace_noalloc_status(logits: int, targets: int, N: int, V: int, reduction: int,
+                                  loss: int) -> int:
+    """lce_ce_inplace_noalloc returning the raw status (host validation tests)."""
+    return lib().lce_ce_inplace_noalloc(c_void_p(logits), c_void_p(targets), None, N, V, -100,
+                                        reduction, 1.0, c_void_p(loss), None, None)
 
 
 def lce_scale(src: int, dst: int, dtype: int, rows: int, cols: int, scale: int,

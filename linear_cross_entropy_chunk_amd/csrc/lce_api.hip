@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -60,7 +61,7 @@ namespace {
 thread_local char g_last_error[256] = "";
 
 constexpr size_t kAlign = 256;
-inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -210,6 +211,83 @@ T* at(void* ws, size_t off) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Scratch of the standalone CE on N rows: corrected targets, row weights g,
+// per-row losses and class weights (N each, 4 bytes), then the counters
+// (n_valid, n_bad, the weight sum).
+size_t ce_scratch_bytes(int64_t N) {
+  const int64_t n = std::max<int64_t>(N, 1);
+  return align_up(n * 4) * 4 + align_up(24);
+}
+
+// Host validation shared by both CE entry points.
+lce_status ce_check(const float* logits, const int64_t* targets, int64_t N, int64_t V,
+                    int32_t reduction, const float* loss) {
+  if (N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
+  if (reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_UNSUPPORTED;
+  if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
+  if (!loss) return LCE_ERR_INVALID_ARG;
+  if (V % 4 != 0 || (logits && !aligned16(logits))) return LCE_ERR_UNSUPPORTED;
+  if (N > 2147483647LL || V > 2147483647LL) return LCE_ERR_UNSUPPORTED;
+  return LCE_OK;
+}
+
+// The standalone CE's launches on scratch `ws` (ce_scratch_bytes(N) bytes):
+// target prep (row weights, counts), the in-place rows, the loss reduction.
+// Every scratch element a launch reads was written by an earlier launch of
+// the same call, so the scratch needs no clearing.
+lce_status ce_enqueue(float* logits, const int64_t* targets, const float* class_weight,
+                      int64_t N, int64_t V, int64_t ignore_index, int32_t reduction,
+                      float grad_scale, float* loss, int64_t* n_valid, char* ws,
+                      hipStream_t s) {
+  const int64_t n = std::max<int64_t>(N, 1);
+  int* tc = reinterpret_cast<int*>(ws);
+  float* g = reinterpret_cast<float*>(ws + align_up(n * 4));
+  float* lrows = reinterpret_cast<float*>(ws + 2 * align_up(n * 4));
+  float* wrow = reinterpret_cast<float*>(ws + 3 * align_up(n * 4));
+  int64_t* cnt = reinterpret_cast<int64_t*>(ws + 4 * align_up(n * 4));
+  const bool none = reduction == LCE_NONE;
+  // Per-row weights: 'none' takes grad_scale on every counted row, which is
+  // the weight the 'sum' reduction gives.
+  LCE_HIP(lce::prep_targets(targets, static_cast<int>(N), static_cast<int>(V), ignore_index,
+                            none ? LCE_SUM : reduction, grad_scale, nullptr, class_weight, tc, g,
+                            wrow, cnt, n_valid, nullptr, nullptr, s));
+  LCE_HIP(lce::ce_inplace_rows(logits, static_cast<int>(N), static_cast<int>(V), tc, g,
+                               class_weight ? wrow : nullptr, none ? loss : lrows, s));
+  if (!none) LCE_HIP(lce::loss_reduce(lrows, static_cast<int>(N), cnt, reduction, loss, s));
+  return LCE_OK;
+}
+
+// The allocation-free CE's scratch: one static array per device, sized for
+// LCE_CE_NOALLOC_MAX_ROWS rows.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes =
+    (LCE_CE_NOALLOC_MAX_ROWS * 4 + kAlign - 1) / kAlign * kAlign * 4 + kAlign;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on the first call there.
+lce_status noalloc_scratch(char** out) {
+  int dev = 0;
+  LCE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return LCE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    LCE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return LCE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return LCE_OK;
+}
+static_assert(kNoAllocScratchBytes >= align_up(LCE_CE_NOALLOC_MAX_ROWS * 4) * 4 + align_up(24),
+              "the static scratch holds ce_scratch_bytes(LCE_CE_NOALLOC_MAX_ROWS)");
 
 }  // namespace
 
@@ -534,8 +612,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
 
 lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes) {
   if (!bytes || N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
-  const int64_t n = std::max<int64_t>(N, 1);
-  *bytes = align_up(n * 4) * 4 + align_up(24);
+  *bytes = ce_scratch_bytes(N);
   return LCE_OK;
 }
 
@@ -560,34 +637,33 @@ lce_status lce_ce_inplace(float* logits, const int64_t* targets, const float* cl
                           int64_t N, int64_t V, int64_t ignore_index, int32_t reduction,
                           float grad_scale, float* loss, int64_t* n_valid, void* workspace,
                           size_t ws_bytes, void* stream) {
-  if (N < 0 || V < 1) return LCE_ERR_INVALID_ARG;
-  if (reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_UNSUPPORTED;
-  if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
-  if (!loss) return LCE_ERR_INVALID_ARG;
-  if (V % 4 != 0 || (logits && !aligned16(logits))) return LCE_ERR_UNSUPPORTED;
-  if (N > 2147483647LL || V > 2147483647LL) return LCE_ERR_UNSUPPORTED;
-  size_t need = 0;
-  lce_ce_workspace_size(N, V, &need);
-  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+  const lce_status st = ce_check(logits, targets, N, V, reduction, loss);
+  if (st != LCE_OK) return st;
+  if (!workspace || ws_bytes < ce_scratch_bytes(N) ||
+      (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return LCE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t n = std::max<int64_t>(N, 1);
-  char* ws = static_cast<char*>(workspace);
-  int* tc = reinterpret_cast<int*>(ws);
-  float* g = reinterpret_cast<float*>(ws + align_up(n * 4));
-  float* lrows = reinterpret_cast<float*>(ws + 2 * align_up(n * 4));
-  float* wrow = reinterpret_cast<float*>(ws + 3 * align_up(n * 4));
-  int64_t* cnt = reinterpret_cast<int64_t*>(ws + 4 * align_up(n * 4));
-  const bool none = reduction == LCE_NONE;
-  // Per-row weights: 'none' takes grad_scale on every counted row, which is
-  // the weight the 'sum' reduction gives.
-  LCE_HIP(lce::prep_targets(targets, static_cast<int>(N), static_cast<int>(V), ignore_index,
-                            none ? LCE_SUM : reduction, grad_scale, nullptr, class_weight, tc, g,
-                            wrow, cnt, n_valid, nullptr, nullptr, s));
-  LCE_HIP(lce::ce_inplace_rows(logits, static_cast<int>(N), static_cast<int>(V), tc, g,
-                               class_weight ? wrow : nullptr, none ? loss : lrows, s));
-  if (!none) LCE_HIP(lce::loss_reduce(lrows, static_cast<int>(N), cnt, reduction, loss, s));
-  return LCE_OK;
+  return ce_enqueue(logits, targets, class_weight, N, V, ignore_index, reduction, grad_scale,
+                    loss, n_valid, static_cast<char*>(workspace),
+                    static_cast<hipStream_t>(stream));
+}
+
+lce_status lce_ce_inplace_noalloc(float* logits, const int64_t* targets,
+                                  const float* class_weight, int64_t N, int64_t V,
+                                  int64_t ignore_index, int32_t reduction, float grad_scale,
+                                  float* loss, int64_t* n_valid, void* stream) {
+  const lce_status st = ce_check(logits, targets, N, V, reduction, loss);
+  if (st != LCE_OK) return st;
+  if (N > LCE_CE_NOALLOC_MAX_ROWS) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "lce_ce_inplace_noalloc: N = %lld rows exceeds the static scratch of %lld rows",
+             static_cast<long long>(N), static_cast<long long>(LCE_CE_NOALLOC_MAX_ROWS));
+    return LCE_ERR_UNSUPPORTED;
+  }
+  char* ws = nullptr;
+  const lce_status sst = noalloc_scratch(&ws);
+  if (sst != LCE_OK) return sst;
+  return ce_enqueue(logits, targets, class_weight, N, V, ignore_index, reduction, grad_scale,
+                    loss, n_valid, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
