@@ -294,7 +294,11 @@ static_assert(kNoAllocScratchBytes >= align_up(LCE_CE_NOALLOC_MAX_ROWS * 4) * 4 
 extern "C" {
 
 const char* lce_status_string(lce_status s) {
-  switch (s) {
+  // A caller may pass any int (C, or the Python binding); a C++ load of an
+  // lce_status outside its enumerators is undefined, so read the bits.
+  int code = 0;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case LCE_OK: return "LCE_OK";
     case LCE_ERR_INVALID_ARG: return "LCE_ERR_INVALID_ARG";
     case LCE_ERR_DTYPE: return "LCE_ERR_DTYPE";
