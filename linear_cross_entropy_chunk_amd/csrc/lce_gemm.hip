@@ -448,6 +448,45 @@ __device__ __forceinline__ void store4(T* p, f32x4_t v) {
   }
 }
 
+// 16-bit outputs: two accumulator blocks i0 = 2p and i1 = 2p + 1 of one
+// column (lane group q holds M values 4q .. 4q + 3 of each 16-value block),
+// rounded to the element type and traded between lane groups q and q ^ 1
+// with v_permlane16_swap (vdst's rows 1 and 3 swap with src's rows 0 and 2;
+// lane layout checked on the chip).  Afterwards lane group q holds the 8
+// consecutive M values pair_off(p, q) .. + 7 of the pair's 32, so a column's
+// 32 values leave in four 16-byte stores instead of eight 8-byte ones.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ uint2 pack4(f32x4_t v) {
+  static_assert(sizeof(T) == 2, "16-bit element types");
+  if constexpr (std::is_same_v<T, _Float16>) {
+    f16x4_t o;
+    o[0] = static_cast<_Float16>(v[0]);
+    o[1] = static_cast<_Float16>(v[1]);
+    o[2] = static_cast<_Float16>(v[2]);
+    o[3] = static_cast<_Float16>(v[3]);
+    return __builtin_bit_cast(uint2, o);
+  } else {
+    bf16x4_t o;
+    o[0] = static_cast<__bf16>(v[0]);
+    o[1] = static_cast<__bf16>(v[1]);
+    o[2] = static_cast<__bf16>(v[2]);
+    o[3] = static_cast<__bf16>(v[3]);
+    return __builtin_bit_cast(uint2, o);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4_t pair_rows8(f32x4_t v0, f32x4_t v1) {
+  const uint2 a = pack4<T>(v0), b = pack4<T>(v1);
+  const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  return u32x4_t{x[0], y[0], x[1], y[1]};
+}
+
+__device__ __forceinline__ int pair_off(int p, int q) { return 16 * (2 * p + (q & 1)) + 8 * (q >> 1); }
+
 template <typename T, int kMode, bool kATr, bool kBTr, bool kBPan>
 __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
@@ -470,6 +509,35 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   const int nb = tn * kTile + wn * kWaveN + (lane & 15);
   const int64_t ldc = g.ldc;
   const float osc = g.out_scale ? g.out_scale[0] : 1.0f;   // product scale, element-type stores
+  constexpr bool kWide = sizeof(T) == 2 && (kMode == static_cast<int>(EpiMode::kStoreOut) ||
+                                            kMode == static_cast<int>(EpiMode::kFinalOut));
+  if constexpr (kWide) {
+    // M is a multiple of 8 for 16-bit types, so a lane's 8 values are all
+    // inside M or all outside.  The trade pairs lanes of the same column,
+    // which share the n test.
+    const int mw = tm * kTile + wm * kWaveM;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int n = nb + kBlk * j;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int p = 0; p < kI / 2; ++p) {
+        f32x4_t v0 = acc[2 * p][j], v1 = acc[2 * p + 1][j];
+        if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
+          const float* cin = static_cast<const float*>(g.Cin) + static_cast<int64_t>(n) * ldc;
+          const int m0 = mb + kBlk * 2 * p, m1 = m0 + kBlk;
+          v0 = m0 < g.M ? load4(cin + m0) + v0 : v0;
+          v1 = m1 < g.M ? load4(cin + m1) + v1 : v1;
+        }
+        const u32x4_t w = pair_rows8<T>(v0 * osc, v1 * osc);
+        const int m = mw + pair_off(p, q);
+        if (m < g.M)
+          *reinterpret_cast<u32x4_t*>(static_cast<T*>(g.C) + static_cast<int64_t>(n) * ldc + m) = w;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const int n = nb + kBlk * j;
@@ -651,11 +719,20 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
         a.s_part[kblk + n] = sum;
         if constexpr (kArgmax) a.i_part[kblk + n] = mi;
       }
-      // 6. the exp tile T[n][v], 4 consecutive classes per store.
+      // 6. the exp tile T[n][v]: 16-bit types trade halves between lane
+      //    groups (pair_rows8) and store 8 consecutive classes at a time;
+      //    fp32 stores 4.
       if constexpr (kStoreT) {
         T* row = Tm + static_cast<int64_t>(n) * kTile;
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int i = 0; i < kI; ++i) store4(row + vpan + kBlk * i, acc[i][j]);
+          for (int p = 0; p < kI / 2; ++p)
+            *reinterpret_cast<u32x4_t*>(row + wm * kWaveM + pair_off(p, q)) =
+                pair_rows8<T>(acc[2 * p][j], acc[2 * p + 1][j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kI; ++i) store4(row + vpan + kBlk * i, acc[i][j]);
+        }
       }
     }
     // keep the blocks apart so only one block's values are live at a time
