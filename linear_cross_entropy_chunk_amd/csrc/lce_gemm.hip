@@ -175,6 +175,7 @@ __device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
 }
 
 // C tile [m0, m0+256) x [n0, n0+256) = A[m0.., k_begin..k_end) . B[n0.., ...]^T
+// (added to the accumulators' values on entry with kAccInit, else from zero)
 //
 // Rows past M (N) read as zero (each copy's descriptor covers only the
 // tile's existing rows); so do k-rows of a k-major operand past its valid
@@ -198,7 +199,8 @@ __device__ __forceinline__ i32x4_t read_tr_pair(const char* lds_p) {
 // A stage's B thus has most of a stage to land and its A about seven
 // quarters.  An MFMA slot carries at most one read or one copy: a slot with
 // both stretches the gap between two MFMAs past the 16 cycles one takes.
-template <typename T, bool kKTail, bool kATr, bool kBTr, bool kBPan = false>
+template <typename T, bool kKTail, bool kATr, bool kBTr, bool kBPan = false,
+          bool kAccInit = false>
 __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, int m0, int M,
                                          int a_krows,
                                          const T* __restrict__ B, int64_t ldb, int n0, int N,
@@ -216,10 +218,12 @@ __device__ __forceinline__ void mainloop(const T* __restrict__ A, int64_t lda, i
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy bases in SGPRs
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  if constexpr (!kAccInit) {   // kAccInit: the caller has loaded the accumulators
 #pragma unroll
-  for (int i = 0; i < kI; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < kJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   if (nk <= 0) return;
 
@@ -498,17 +502,45 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
   tile_coords(logical - split * per_split, tiles_m, tiles_n, g.group_m, tm, tn);
   const int kb = split * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
-  Acc acc;
-  mainloop<T, false, kATr, kBTr, kBPan>(static_cast<const T*>(g.A), g.lda, tm * kTile, g.M,
-                                        g.a_krows, static_cast<const T*>(g.B), g.ldb, tn * kTile,
-                                        g.N, g.b_krows, g.b_pstride, kb, ke, lds, acc);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int mb = tm * kTile + wm * kWaveM + 4 * (lane >> 4);
   const int nb = tn * kTile + wn * kWaveN + (lane & 15);
   const int64_t ldc = g.ldc;
   const float osc = g.out_scale ? g.out_scale[0] : 1.0f;   // product scale, element-type stores
+
+  // The fp32 read-modify-write modes start the accumulators from the fp32
+  // values in memory instead of reading them in the epilogue: these loads
+  // overlap the wait for the tile's first operand stage, where an epilogue
+  // read would come when every tile of a wave finishes at once.  The loads
+  // are unconditional, through a descriptor over the tile's rows of the
+  // stored matrix (rows past N read as 0; columns past M read neighbouring
+  // values that are never stored), so they go straight to the accumulation
+  // registers.
+  constexpr bool kInit = kMode == static_cast<int>(EpiMode::kAccumF32) ||
+                         kMode == static_cast<int>(EpiMode::kFinalOut);
+  Acc acc;
+  if constexpr (kInit) {
+    const float* src = static_cast<const float*>(
+        kMode == static_cast<int>(EpiMode::kFinalOut) ? g.Cin : g.C);
+    const int n0 = tn * kTile, m0 = tm * kTile;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        src + static_cast<int64_t>(n0) * ldc + m0,
+        (static_cast<int64_t>(min(g.N - n0, kTile)) * ldc - m0) * 4);
+    const int nl = wn * kWaveN + (lane & 15), ml = wm * kWaveM + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int i = 0; i < kI; ++i)
+        acc[i][j] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, ((nl + kBlk * j) * static_cast<int>(ldc) + ml + kBlk * i) * 4, 0, 0));
+  }
+  mainloop<T, false, kATr, kBTr, kBPan, kInit>(static_cast<const T*>(g.A), g.lda, tm * kTile,
+                                               g.M, g.a_krows, static_cast<const T*>(g.B), g.ldb,
+                                               tn * kTile, g.N, g.b_krows, g.b_pstride, kb, ke,
+                                               lds, acc);
+
   constexpr bool kWide = sizeof(T) == 2 && (kMode == static_cast<int>(EpiMode::kStoreOut) ||
                                             kMode == static_cast<int>(EpiMode::kFinalOut));
   if constexpr (kWide) {
@@ -517,29 +549,35 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
     // which share the n test.
     const int mw = tm * kTile + wm * kWaveM;
     const int q = lane >> 4;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
+      // Column blocks not yet stored stay in the accumulator registers, so
+      // only one block's values are copied to VGPRs at a time.
+#pragma unroll
+      for (int jj = j + 1; jj < kJ; ++jj)
+#pragma unroll
+        for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
       const int n = nb + kBlk * j;
       if (n >= g.N) continue;
 #pragma unroll
       for (int p = 0; p < kI / 2; ++p) {
-        f32x4_t v0 = acc[2 * p][j], v1 = acc[2 * p + 1][j];
-        if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
-          const float* cin = static_cast<const float*>(g.Cin) + static_cast<int64_t>(n) * ldc;
-          const int m0 = mb + kBlk * 2 * p, m1 = m0 + kBlk;
-          v0 = m0 < g.M ? load4(cin + m0) + v0 : v0;
-          v1 = m1 < g.M ? load4(cin + m1) + v1 : v1;
-        }
-        const u32x4_t w = pair_rows8<T>(v0 * osc, v1 * osc);
+        const u32x4_t w = pair_rows8<T>(acc[2 * p][j] * osc, acc[2 * p + 1][j] * osc);
         const int m = mw + pair_off(p, q);
         if (m < g.M)
           *reinterpret_cast<u32x4_t*>(static_cast<T*>(g.C) + static_cast<int64_t>(n) * ldc + m) = w;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     return;
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
+#pragma unroll
+    for (int jj = j + 1; jj < kJ; ++jj)   // blocks not yet stored stay in AGPRs
+#pragma unroll
+      for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
     const int n = nb + kBlk * j;
     if (n >= g.N) continue;
 #pragma unroll
@@ -551,11 +589,9 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
       if constexpr (kMode == static_cast<int>(EpiMode::kStoreF32)) {
         store4(static_cast<float*>(g.C) + split * g.split_stride + off, v);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kAccumF32)) {
-        float* c = static_cast<float*>(g.C) + off;
-        store4(c, load4(c) + v);
+        store4(static_cast<float*>(g.C) + off, v);          // started from C's value
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
-        store4(static_cast<T*>(g.C) + off,
-               (load4(static_cast<const float*>(g.Cin) + off) + v) * osc);
+        store4(static_cast<T*>(g.C) + off, v * osc);        // started from Cin's value
       } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
         store4(static_cast<T*>(g.C) + off, v * osc);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalAccum)) {

@@ -28,6 +28,9 @@ constexpr int kSmallTile = 64;
 // consecutive memory, and the grad_W GEMM reads the classes of its tile over
 // all rows as one contiguous panel.
 
+// kAccumF32 and kFinalOut load the stored fp32 values into the accumulators
+// before the K loop and only store at the end; kAccumOut and kFinalAccum read
+// their inputs in the epilogue.
 enum class EpiMode : int {
   kStoreF32 = 0,     // C = acc                      (fp32 out, e.g. split-K parts)
   kAccumF32 = 1,     // C = C + acc                  (fp32 in/out)
