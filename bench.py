@@ -202,7 +202,12 @@ def bench_lce(args) -> dict:
     W = torch.from_numpy(inputs["W"]).to(dev).to(dt)
     b = None if inputs["b"] is None else torch.from_numpy(inputs["b"]).to(dev).to(dt)
     t = torch.from_numpy(inputs["t"]).to(dev)
-    u = None if not cfg.upstream else torch.from_numpy(inputs["u"]).to(dev)
+    if args.forward_only and cfg.reduction != "none":
+        raise SystemExit("--forward-only applies to the reduction='none' workload")
+    # 'none' with --forward-only: the loss-only forward (logits, row statistics,
+    # per-row loss; 2*N*V*D flops); otherwise the call forms the gradients
+    u = None if not cfg.upstream or args.forward_only else \
+        torch.from_numpy(inputs["u"]).to(dev)
     op = LinearCrossEntropy(cfg.N, cfg.D, cfg.V, dt, bias=b is not None,
                             reduction=cfg.reduction, chunk_rows=chunk,
                             acc_policy=args.acc_policy, grad_x=True, grad_w=True,
@@ -225,6 +230,8 @@ def bench_lce(args) -> dict:
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
         start.record()
         for _ in range(args.steps):
             graph.replay()
@@ -254,7 +261,8 @@ def bench_lce(args) -> dict:
     achieved = flops_per_launch / avg_s / 1e12
     peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_16BIT_TFLOPS
     tokens_s = N / (ms_step / 1e3)
-    tflops = 6.0 * N * V * D / (ms_step / 1e3) / 1e12
+    flop_factor = 2.0 if args.forward_only else 6.0     # 2NVD forward only, 6NVD with grads
+    tflops = flop_factor * N * V * D / (ms_step / 1e3) / 1e12
     result = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
@@ -265,6 +273,7 @@ def bench_lce(args) -> dict:
                    "N": N, "D": D, "V": V, "chunk_rows": op.chunk_rows,
                    "acc_policy": args.acc_policy, "parallelism": "single GPU"},
         "tflops": tflops,
+        "flops_counted": f"{int(flop_factor)}NVD",
         "frac_of_peak": tflops / peak,
         "workspace_bytes": op.ws_bytes,
         "group_rows": args.group_rows,
@@ -278,8 +287,8 @@ def bench_lce(args) -> dict:
     if args.graph:
         result["graph"] = True
         result["eager_ms_per_step"] = eager_ms
-    if args.per_chunk and cfg.dtype != "f32" and args.group_rows == 0 \
-            and args.acc_policy == "accurate":
+    if args.per_chunk and args.workload == "large-vocab-bf16" and cfg.dtype != "f32" \
+            and args.group_rows == 0 and args.acc_policy == "accurate":
         del op, out, io
         torch.cuda.empty_cache()
         result["per_chunk"] = bench_per_chunk(args, cfg, X, W, t, b, op_chunk_rows)
@@ -458,6 +467,8 @@ def main() -> int:
                     choices=["tiny-f32", "mid-bf16", "large-vocab-bf16", "none-bf16", "ce-f32"])
     ap.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"],
                     help="round the workload's inputs to this type instead of its own")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="reduction='none' workload: time the loss-only forward")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one call captured into a HIP graph")
     ap.add_argument("--acc-policy", default="accurate", choices=["accurate", "compact"])
