@@ -57,7 +57,7 @@ def to_dev(a, dt: str):
 def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0,
             acc_policy: str = "accurate", ignore_index: int = -100, grads: str = "xwb",
             argmax: bool = True, upstream=None, grad_scale: float = 1.0, bias: bool | None = None,
-            repeat: int = 1, class_weight=None) -> dict | list:
+            repeat: int = 1, class_weight=None, group_rows: int = 0) -> dict | list:
     X, W, b, t = case["X"], case["W"], case["b"], case["t"]
     if bias is False:
         b = None
@@ -66,7 +66,8 @@ def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0
     op = LinearCrossEntropy(N, D, V, TORCH_DT[dt], bias=b is not None, reduction=reduction,
                             ignore_index=ignore_index, chunk_rows=chunk_rows,
                             acc_policy=acc_policy, grad_x="x" in grads, grad_w="w" in grads,
-                            grad_b=("b" in grads) and b is not None, argmax=argmax)
+                            grad_b=("b" in grads) and b is not None, argmax=argmax,
+                            group_rows=group_rows)
     Xd, Wd, bd = to_dev(X, dt), to_dev(W, dt), to_dev(b, dt)
     td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
     ud = None if upstream is None else torch.from_numpy(
@@ -82,6 +83,7 @@ def run_gpu(case: dict, dt: str, *, reduction: str = "mean", chunk_rows: int = 0
             res[k] = v.cpu().numpy() if v.dtype in (torch.int32, torch.int64) else \
                 v.float().cpu().numpy().astype(np.float64)
         res["chunk_rows"] = op.chunk_rows
+        res["ws_bytes"] = op.ws_bytes
         results.append(res)
     return results[0] if repeat == 1 else results
 

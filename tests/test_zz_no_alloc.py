@@ -88,3 +88,46 @@ def test_noalloc_ce_refuses_more_rows_than_its_scratch():
         B.LCE_ERR_UNSUPPORTED                                  # unknown reduction
     assert B.lce_ce_inplace_noalloc_status(fake, fake, 16, 1024, B.LCE_MEAN, 0) == \
         B.LCE_ERR_INVALID_ARG                                  # no loss buffer
+
+
+@pytest.mark.gpu
+def test_noalloc_ce_replays_from_a_graph():
+    """Captured into a HIP graph (the callers it is for), after one eager call
+    on the device: each replay on new logits equals an eager call bit for
+    bit, with eager work and synchronisations between the replays."""
+    import torch
+
+    from gpu_common import log, require_gpu
+    require_gpu()
+    dev = torch.device("cuda", 0)
+    N, V = 64, 4096
+    z, t, _ = _inputs(N, V, False, seed=80)
+    zd = torch.from_numpy(z).to(dev)
+    td = torch.from_numpy(t).to(dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int64, device=dev)
+
+    def call():
+        B.lce_ce_inplace_noalloc(zd.data_ptr(), td.data_ptr(), None, N, V, -100, B.LCE_MEAN,
+                                 1.0, loss.data_ptr(), nv.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+
+    call()                                    # eager: the scratch address is looked up here
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    zd.copy_(torch.from_numpy(z).to(dev))
+    with torch.cuda.graph(graph):
+        call()
+    log("no-alloc CE graph captured")
+    for k in range(3):
+        zk, tk, _ = _inputs(N, V, False, seed=81 + k)
+        want = _call("noalloc", zk, tk, None, "mean", 1.0)      # eager, own buffers
+        zd.copy_(torch.from_numpy(zk).to(dev))
+        td.copy_(torch.from_numpy(tk).to(dev))
+        loss.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(loss.cpu().numpy(), want[0])
+        assert int(nv.cpu()[0]) == want[1]
+        np.testing.assert_array_equal(zd.cpu().numpy(), want[2])
