@@ -11,10 +11,20 @@
  * reduction.  It walks the batch rows in chunks of chunk_rows rows and forms
  * the gradients during the same pass as the loss.  The fp32 logits of a chunk
  * exist only in registers, one 256 x 256 output tile at a time, and are never
- * written to memory; what a chunk leaves in the workspace is its tile of
- * exp(z - block max), rewritten in place into dL, in the input dtype
- * (chunk rows x V).  Which rows' dL the workspace holds at once depends on
- * the grad_W accumulation (lce_acc_policy, lce_desc.group_rows):
+ * written to memory; what a chunk leaves in the workspace is a tile of
+ * (chunk rows x V) in the input dtype:
+ *   - bf16 gradients: exp(z - r_n) with one reference r_n per row, its
+ *     target logit, and S_n = sum_v exp(z - r_n) taken off the target entry.
+ *     That is dL up to the row factor g_n / S_n, which the gradient products
+ *     apply (grad_X's rows as they are stored, X's rows as they are staged
+ *     for grad_W, the rows of the grad_b sums), so no pass rewrites the
+ *     tile.  A row whose largest logit exceeds r_n by more than 40 (a loss
+ *     above 40 nats, where exp(z - r_n) could overflow) has its chunk
+ *     recomputed, on the device, with the row max as its reference.
+ *   - fp16 and fp32 (and bf16 with the staged dL^T below): exp(z - block
+ *     max), rewritten in place into dL by a finalize pass.
+ * Which rows of that tile the workspace holds at once depends on the grad_W
+ * accumulation (lce_acc_policy, lce_desc.group_rows):
  *   - ACCURATE with group_rows = 0 (the default) keeps the dL of a group of
  *     consecutive chunks, up to 4 D / sizeof(element) rows (as many bytes as
  *     an fp32 V x D accumulator), and runs one grad_X and one grad_W GEMM
@@ -22,7 +32,7 @@
  *     D = 4096, bf16: one group of N rows, 2.1 GB of bf16 dL), no fp32
  *     accumulator is needed and grad_W is rounded once from fp32 registers.
  *   - ACCURATE with group_rows <= chunk rows keeps one chunk's dL: both
- *     gradient GEMMs consume it right after its finalize, and grad_W is
+ *     gradient GEMMs consume it as soon as it is complete, and grad_W is
  *     carried across chunks in an fp32 V x D accumulator in the workspace,
  *     rounded once after the last chunk.
  *   - COMPACT keeps one chunk's dL and adds each chunk's grad_W into the
@@ -322,7 +332,7 @@ LCE_API lce_status lce_ce_inplace_noalloc(float* logits, const int64_t* targets,
 
 /* Kernel classes of lce_forward_backward, for the timing hook below. */
 enum {
-  LCE_K_PREP = 0,       /* target counts and row weights */
+  LCE_K_PREP = 0,       /* target counts, row weights, per-row references */
   LCE_K_LOGITS = 1,     /* logits GEMM with the fused softmax-statistics epilogue */
   LCE_K_COMBINE = 2,    /* per-row log-sum-exp, loss, argmax */
   LCE_K_FINALIZE = 3,   /* dL = g (softmax - onehot) in place, dL^T, bias partials */
@@ -335,7 +345,10 @@ enum {
   LCE_K_GEMM_W = 7,     /* grad_W += dL^T . X_chunk */
   LCE_K_BIAS = 8,       /* grad_b reduction */
   LCE_K_LOSS = 9,       /* final loss reduction, zero fills */
-  LCE_K_COUNT = 10
+  LCE_K_REPAIR = 10,    /* bf16 gradients: the gated recompute of a chunk with
+                           a row whose reference was too low (logits GEMM and
+                           combine; empty launches when no row needs it) */
+  LCE_K_COUNT = 11
 };
 
 /* Timing hook for benchmarks (an implementation entry: the pages measure

@@ -26,7 +26,7 @@ LCE_CE_NOALLOC_MAX_ROWS = 1 << 20
 
 # kernel classes of the timing hook
 KERNEL_CLASSES = ("prep", "logits", "combine", "finalize", "gemm_x", "split_sum", "transpose",
-                  "gemm_w", "bias", "loss")
+                  "gemm_w", "bias", "loss", "repair")
 LCE_K_COUNT = len(KERNEL_CLASSES)
 
 

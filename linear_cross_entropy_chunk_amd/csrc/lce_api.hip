@@ -48,11 +48,12 @@ struct lce_handle {
   bool w_acc32;       // fp32 grad_W accumulator in the workspace
   bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
   bool gx_group;      // one grad_X GEMM per grad_W group (its rows all in T)
+  bool rowref;        // one reference per row: T holds dL / beta, no finalize pass
   int64_t gx_rows;    // most rows of one grad_X GEMM
   int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
-      o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, total;
+      o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, o_rref, o_beta, o_flag, total;
   TimingPool timing;
 };
 
@@ -160,6 +161,15 @@ void plan(lce_handle* h) {
   // With the group's dL in T, grad_X runs once per group over all its rows
   // (fewer, larger launches; one split needs no partials and no split sum).
   h->gx_group = h->want_x && h->w_inplace;
+
+  // One reference per row (bf16 gradients): the logits epilogue stores
+  // exp(z - r_n) with r_n the row's target logit, so that
+  // dL = beta_n (T with S_n taken off the target entry), beta_n = g_n / S_n.
+  // beta then scales grad_X's columns in its epilogue, X^T's columns when it
+  // is staged and T's rows in the grad_b column sums, and no pass rewrites T.
+  // bf16 only: T's entries may exceed 1 (up to e^kRefGap), which fp16 cannot
+  // hold.  Not with a staged dL^T, which the finalize pass forms.
+  h->rowref = h->elem == lce::Elem::kBF16 && h->want_any && (!h->want_w || h->w_inplace);
   h->gx_rows = h->gx_group ? std::min<int64_t>(h->grp * h->c, d.N) : h->c;
   // split-K for grad_X = dL . W: aim at one workgroup per CU (256; two
   // rounds of 512 measured slower: more partials to sum, twice the tile
@@ -201,6 +211,9 @@ void plan(lce_handle* h) {
   h->o_wrow = take(std::max<int64_t>(N, 1) * 4, true);
   // n_valid, n_bad, row-weight sum (double), then the fp16 dL scale 2^k and 2^-k
   h->o_cnt = take(3 * 8 + 2 * 4, true);
+  h->o_rref = take(std::max<int64_t>(N, 1) * 4, h->rowref);
+  h->o_beta = take(std::max<int64_t>(N, 1) * 4, h->rowref);
+  h->o_flag = take(std::max<int64_t>(h->n_chunks, 1) * 4, h->rowref);
   h->total = o;
 }
 
@@ -458,6 +471,10 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   float* lrows = at<float>(workspace, h->o_lrows);
   float* wrow = at<float>(workspace, h->o_wrow);
   int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
+  const bool rowref = h->rowref && grads;
+  float* rref = at<float>(workspace, h->o_rref);
+  float* beta = at<float>(workspace, h->o_beta);
+  int* flags = at<int>(workspace, h->o_flag);
   // fp16 keeps dL times a power of two 2^k (from the largest row weight) so
   // that it stays inside fp16's range; the gradients' element-type stores
   // multiply by 2^-k.  Exact scalings: no rounding is added.
@@ -477,6 +494,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
 
   if (want_x && !half)
     LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
+  if (rowref)
+    LCE_LAUNCH(h, LCE_K_PREP, lce::target_logits(el, io->X, D, io->W, D, io->b, tc, N, D, rref,
+                                                 flags, static_cast<int>(h->n_chunks), s));
 
   // grad_X[xrow0 .. + nrows) = dL . W for dL rows held in T from Tb on, with
   // M = D against dL[rows][V] (K = V): the transposed store writes grad_X
@@ -500,10 +520,13 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     gx.group_m = 4;   // an XCD's 32 concurrent tiles: 4 along D x 8 along rows
     gx.role = lce::GemmRole::kGradX;
     char* out = static_cast<char*>(io->grad_X) + xrow0 * d.D * es;
+    // one-reference plan: grad_X row n = beta_n (T . W)[n]
+    const float* rs = rowref ? beta + xrow0 : nullptr;
     if (half && h->splits == 1) {
       gx.C = out;
       gx.mode = h->accum ? lce::EpiMode::kAccumOut : lce::EpiMode::kStoreOut;
       gx.out_scale = dl_unscale;
+      gx.n_scale = rs;
       LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
       return LCE_OK;
     }
@@ -511,7 +534,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     gx.mode = lce::EpiMode::kStoreF32;
     LCE_LAUNCH(h, LCE_K_GEMM_X, lce::gemm_nt(el, gx, s));
     LCE_LAUNCH(h, LCE_K_SPLIT_SUM, lce::sum_splits(el, gxp, h->splits, gx.split_stride, nrows, D,
-                                                   out, h->accum, dl_unscale, s));
+                                                   out, h->accum, dl_unscale, s, rs));
     return LCE_OK;
   };
 
@@ -535,19 +558,41 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.T = grads ? Tc : nullptr; la.tps = tps;
     la.m_part = mp; la.s_part = sp; la.i_part = h->want_argmax ? ip : nullptr; la.ldp = cp;
     la.zt = zt;
+    // one-reference plan: the padding rows up to rows_pad are written as 0
+    // (grad_W's K range covers them)
+    la.rref = rowref ? rref + row0 : nullptr;
+    la.t_rows = rowref ? rows_pad : rows;
+    la.gate = nullptr;
     LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
 
     float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
-    LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
-                             io->class_weight ? wrow + row0 : nullptr, rows, lse, loss_rows,
-                             h->want_argmax ? io->argmax + row0 : nullptr, s));
-    if (!grads) continue;
-
-    char* dLt_j = dLt ? static_cast<char*>(dLt) + jj * cp * es : nullptr;
-    LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(el, Tc, tps,
-                                  want_w && !h->w_inplace ? dLt_j : nullptr,
-                                  h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
-                                  V, static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale, s));
+    const float* wrow_c = io->class_weight ? wrow + row0 : nullptr;
+    int* amax_c = h->want_argmax ? io->argmax + row0 : nullptr;
+    if (rowref) {
+      // combine, then the repair of rows whose reference was too low: both
+      // launches do nothing unless the combine raised the chunk's flag
+      int* flag = flags + ck;
+      LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine_ref(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
+                                                        wrow_c, g + row0, rows, rref + row0, Tc,
+                                                        tps, loss_rows, beta + row0, amax_c,
+                                                        flag, nullptr, s));
+      lce::LogitsLse lr = la;
+      lr.gate = flag;
+      LCE_LAUNCH(h, LCE_K_REPAIR, lce::logits_lse(el, lr, s));
+      LCE_LAUNCH(h, LCE_K_REPAIR, lce::row_combine_ref(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
+                                                       wrow_c, g + row0, rows, rref + row0, Tc,
+                                                       tps, loss_rows, beta + row0, amax_c,
+                                                       flag, flag, s));
+    } else {
+      LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
+                                                    wrow_c, rows, lse, loss_rows, amax_c, s));
+      if (!grads) continue;
+      char* dLt_j = dLt ? static_cast<char*>(dLt) + jj * cp * es : nullptr;
+      LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(el, Tc, tps,
+                                    want_w && !h->w_inplace ? dLt_j : nullptr,
+                                    h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
+                                    V, static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale, s));
+    }
     if (want_x && !h->gx_group) {
       const lce_status st = grad_x(Tc, row0, rows);
       if (st != LCE_OK) return st;
@@ -562,11 +607,12 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       if (jj + 1 == h->grp || last) {
         const int64_t g_row0 = (ck - jj) * h->c;
         const int g_rows = static_cast<int>(row0 + rows - g_row0);
+        // (one-reference plan: X^T's column k times beta_k)
         if (h->w_inplace)
           LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xb + g_row0 * d.D * es, D, g_rows,
                                                             D, Xt, h->k_grp,
                                                             static_cast<int>(round_up(g_rows, 64)),
-                                                            s));
+                                                            s, rowref ? beta + g_row0 : nullptr));
         if (want_x && h->gx_group) {
           // the whole group's rows, back to back in T from row 0
           const lce_status st = grad_x(T, g_row0, g_rows);
@@ -606,6 +652,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gw, s));
       }
     }
+    if (want_b && rowref)
+      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(Tc, tps, beta + row0, rows, rows_pad,
+                                               static_cast<int>(Vp), gbp, s));
     if (want_b)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
                                     last, h->accum, s));

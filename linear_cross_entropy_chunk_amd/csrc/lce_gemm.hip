@@ -33,6 +33,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace lce {
@@ -61,6 +62,7 @@ constexpr int kSlotBytes = kTile * kRowBytes; // one operand of one stage: 32 Ki
 constexpr int kSlots = 5;
 constexpr int kLdsOperandBytes = kSlots * kSlotBytes;        // 160 KiB ring
 constexpr int kCopies = kTile / 8 / kWaves;   // 8-row copies per operand per wave per stage
+constexpr uint32_t kRepairGrid = 256;         // workgroups of the gated repair pass (one per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Accumulator layout of a 16 x 16 MFMA block, lane l, register r:
@@ -543,6 +545,21 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
 
   constexpr bool kWide = sizeof(T) == 2 && (kMode == static_cast<int>(EpiMode::kStoreOut) ||
                                             kMode == static_cast<int>(EpiMode::kFinalOut));
+  // Column factors of the element-type store modes, all eight loaded at once.
+  constexpr bool kColScale = kMode == static_cast<int>(EpiMode::kStoreOut) ||
+                             kMode == static_cast<int>(EpiMode::kAccumOut);
+  float csc[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) csc[j] = osc;
+  if constexpr (kColScale) {
+    if (g.n_scale) {
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int n = nb + kBlk * j;
+        if (n < g.N) csc[j] = osc * g.n_scale[n];
+      }
+    }
+  }
   if constexpr (kWide) {
     // M is a multiple of 8 for 16-bit types, so a lane's 8 values are all
     // inside M or all outside.  The trade pairs lanes of the same column,
@@ -562,7 +579,7 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
       if (n >= g.N) continue;
 #pragma unroll
       for (int p = 0; p < kI / 2; ++p) {
-        const u32x4_t w = pair_rows8<T>(acc[2 * p][j] * osc, acc[2 * p + 1][j] * osc);
+        const u32x4_t w = pair_rows8<T>(acc[2 * p][j] * csc[j], acc[2 * p + 1][j] * csc[j]);
         const int m = mw + pair_off(p, q);
         if (m < g.M)
           *reinterpret_cast<u32x4_t*>(static_cast<T*>(g.C) + static_cast<int64_t>(n) * ldc + m) = w;
@@ -593,13 +610,13 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalOut)) {
         store4(static_cast<T*>(g.C) + off, v * osc);        // started from Cin's value
       } else if constexpr (kMode == static_cast<int>(EpiMode::kStoreOut)) {
-        store4(static_cast<T*>(g.C) + off, v * osc);
+        store4(static_cast<T*>(g.C) + off, v * csc[j]);
       } else if constexpr (kMode == static_cast<int>(EpiMode::kFinalAccum)) {
         T* c = static_cast<T*>(g.C) + off;
         store4(c, load4(c) + (load4(static_cast<const float*>(g.Cin) + off) + v) * osc);
       } else {
         T* c = static_cast<T*>(g.C) + off;
-        store4(c, load4(c) + v * osc);
+        store4(c, load4(c) + v * csc[j]);
       }
     }
   }
@@ -611,14 +628,11 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmNT& g) {
 // exchange and no barrier.
 static_assert(kWaveM == kStatCols, "one statistics block per wave");
 
-template <typename T, bool kStoreT, bool kArgmax, bool kKTail>
-__global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
-  const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  int tm, tn;
-  tile_coords(logical, tiles_m, tiles_n, 4, tm, tn);
-
+// One logits tile (tm over classes, tn over chunk rows) with its epilogue.
+// kRef: one reference per row (a.rref) instead of the block max.
+template <typename T, bool kStoreT, bool kArgmax, bool kKTail, bool kRef>
+__device__ __forceinline__ void logits_tile(const LogitsLse& a, int tm, int tn, char* lds) {
+  static_assert(!kRef || kStoreT, "the per-row reference serves the gradient path");
   Acc acc;
   // M = classes (rows of W), N = chunk rows (rows of X), K = D.
   mainloop<T, kKTail, false, false>(static_cast<const T*>(a.W), a.ldw, tm * kTile, a.V, 0,
@@ -635,13 +649,18 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   const T* bias = static_cast<const T*>(a.bias);
   const bool v_tail = vbase + kWaveM > a.V;               // uniform: classes past V in this wave
 
-  // Targets of the lane's eight columns, fetched once (-1: none / past the chunk).
+  // Targets (and references) of the lane's eight columns, fetched once
+  // (-1: none / past the chunk).  A row past the chunk takes reference +inf,
+  // so its T row is exp(-inf) = 0.
   int tcol[kJ];
+  float rcol[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const int n = nbase + kBlk * j;
     tcol[j] = n < a.rows ? a.tc[n] : -1;
+    if constexpr (kRef) rcol[j] = n < a.rows ? a.rref[n] : INFINITY;
   }
+  const int t_rows = kRef ? a.t_rows : a.rows;            // rows of T written
 
   // The epilogue walks the eight 16-column blocks j one at a time so that
   // only 32 accumulators per lane are live in VGPRs.
@@ -658,9 +677,9 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     for (int jj = j + 1; jj < kJ; ++jj)
 #pragma unroll
       for (int i = 0; i < kI; ++i) asm volatile("" : "+a"(acc[i][jj]));
-    // A block wholly past the chunk's rows (a short or ragged last chunk)
-    // has nothing to store, and neither have the blocks after it.
-    if (tn * kTile + wn * kWaveN + kBlk * j >= a.rows) break;   // uniform
+    // A block wholly past the rows of T (a short or ragged last chunk) has
+    // nothing to store, and neither have the blocks after it.
+    if (tn * kTile + wn * kWaveN + kBlk * j >= t_rows) break;   // uniform
     const int n = nbase + kBlk * j;         // chunk row
     const bool nin = n < a.rows;
 
@@ -731,9 +750,10 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
     }
 
-    // 4. e = exp(z - block max) in place, column sums.  A block wholly past
-    //    V (max -inf) stores e = 0 and sum 0.
-    const float ref = mx == -INFINITY ? 0.0f : mx;
+    // 4. e = exp(z - ref) in place, column sums; ref is the block max, or the
+    //    row's reference.  A block wholly past V (max -inf) stores e = 0 and
+    //    sum 0.
+    const float ref = kRef ? rcol[j] : (mx == -INFINITY ? 0.0f : mx);
     float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < kI; ++i)
@@ -748,13 +768,13 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
 
-    if (nin) {
-      // 5. per-(row, statistics block) partials.
-      if (q == 0) {
-        a.m_part[kblk + n] = mx;
-        a.s_part[kblk + n] = sum;
-        if constexpr (kArgmax) a.i_part[kblk + n] = mi;
-      }
+    // 5. per-(row, statistics block) partials.
+    if (nin && q == 0) {
+      a.m_part[kblk + n] = mx;
+      a.s_part[kblk + n] = sum;
+      if constexpr (kArgmax) a.i_part[kblk + n] = mi;
+    }
+    if (kRef ? n < t_rows : nin) {
       // 6. the exp tile T[n][v]: 16-bit types trade halves between lane
       //    groups (pair_rows8) and store 8 consecutive classes at a time;
       //    fp32 stores 4.
@@ -773,6 +793,35 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
     }
     // keep the blocks apart so only one block's values are live at a time
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename T, bool kStoreT, bool kArgmax, bool kKTail, bool kRef>
+__global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
+  const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  int tm, tn;
+  tile_coords(logical, tiles_m, tiles_n, 4, tm, tn);
+  logits_tile<T, kStoreT, kArgmax, kKTail, kRef>(a, tm, tn, lds);
+}
+
+// The repair pass of the one-reference plan: nothing unless the chunk's flag
+// is set (the common case costs one launch), else every tile of the chunk
+// again, walked by a grid of at most one workgroup per CU.  The flag is read
+// by every wave of the workgroup alike, so the exit is uniform; each tile
+// ends with the main loop's barrier, after which the LDS ring is free for the
+// next tile.
+template <typename T, bool kArgmax, bool kKTail>
+__global__ __launch_bounds__(kThreads) void k_logits_repair(LogitsLse a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
+  if (*a.gate == 0) return;
+  const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
+  const int tiles = tiles_m * tiles_n;
+  for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
+    int tm, tn;
+    tile_coords(t, tiles_m, tiles_n, 4, tm, tn);
+    logits_tile<T, true, kArgmax, kKTail, true>(a, tm, tn, lds);
   }
 }
 
@@ -826,6 +875,9 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
   // B in the panel layout exactly where the kernel expects it.
   const bool pan = g.role == GemmRole::kGradX || g.b_kmajor;
   if (pan != (g.b_pstride > 0) || (pan && g.ldb != kTile)) return hipErrorInvalidValue;
+  // Column factors only where the epilogue applies them.
+  if (g.n_scale && g.mode != EpiMode::kStoreOut && g.mode != EpiMode::kAccumOut)
+    return hipErrorInvalidValue;
   constexpr bool k16 = sizeof(T) == 2;
   if (g.role == GemmRole::kGradX) {
     // fp32 split partials; or, for 16-bit types reading W in place with one
@@ -867,10 +919,24 @@ hipError_t launch_gemm(const GemmNT& g, hipStream_t s) {
 template <typename T, bool kKTail>
 void launch_logits_k(const LogitsLse& a, dim3 grid, dim3 block, hipStream_t s) {
   const bool st = a.T != nullptr, am = a.i_part != nullptr;
-  if (st && am) k_logits_lse<T, true, true, kKTail><<<grid, block, 0, s>>>(a);
-  else if (st) k_logits_lse<T, true, false, kKTail><<<grid, block, 0, s>>>(a);
-  else if (am) k_logits_lse<T, false, true, kKTail><<<grid, block, 0, s>>>(a);
-  else k_logits_lse<T, false, false, kKTail><<<grid, block, 0, s>>>(a);
+  if constexpr (std::is_same_v<T, uint16_t>) {
+    if (a.rref) {
+      if (a.gate) {
+        grid.x = std::min<uint32_t>(grid.x, kRepairGrid);
+        if (am) k_logits_repair<T, true, kKTail><<<grid, block, 0, s>>>(a);
+        else k_logits_repair<T, false, kKTail><<<grid, block, 0, s>>>(a);
+      } else if (am) {
+        k_logits_lse<T, true, true, kKTail, true><<<grid, block, 0, s>>>(a);
+      } else {
+        k_logits_lse<T, true, false, kKTail, true><<<grid, block, 0, s>>>(a);
+      }
+      return;
+    }
+  }
+  if (st && am) k_logits_lse<T, true, true, kKTail, false><<<grid, block, 0, s>>>(a);
+  else if (st) k_logits_lse<T, true, false, kKTail, false><<<grid, block, 0, s>>>(a);
+  else if (am) k_logits_lse<T, false, true, kKTail, false><<<grid, block, 0, s>>>(a);
+  else k_logits_lse<T, false, false, kKTail, false><<<grid, block, 0, s>>>(a);
 }
 
 template <typename T>
@@ -879,6 +945,12 @@ hipError_t launch_logits(const LogitsLse& a, hipStream_t s) {
                         ((a.rows + kTile - 1) / kTile);
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT32_MAX) return hipErrorInvalidValue;     // workgroup ids are int
+  // The per-row reference: bf16 with T only; rows of T between rows and
+  // t_rows stay inside the chunk's last tile row; the repair needs the flag.
+  if (a.rref && (!std::is_same_v<T, uint16_t> || a.T == nullptr || a.t_rows < a.rows ||
+                 static_cast<int64_t>(a.t_rows) > ((a.rows + kTile - 1) / kTile) * kTile))
+    return hipErrorInvalidValue;
+  if (a.gate && !a.rref) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(tiles)), block(kThreads);
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   if (a.D % kBK == 0) launch_logits_k<T, false>(a, grid, block, s);

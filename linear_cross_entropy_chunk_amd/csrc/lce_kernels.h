@@ -68,17 +68,28 @@ struct GemmNT {
   // element type (modes kStoreOut, kAccumOut, kFinalOut, kFinalAccum; the
   // fp32 modes store it unscaled); null means 1.
   const float* out_scale;
+  // Per-column factors n_scale[n] (n < N) that also multiply column n of the
+  // product in modes kStoreOut and kAccumOut (grad_X: one factor per batch
+  // row); null means 1.
+  const float* n_scale;
 };
 hipError_t gemm_nt(Elem e, const GemmNT& g, hipStream_t s);
 
 // Logits GEMM with the fused softmax-statistics epilogue.  Computes, for the
 // chunk's rows n < rows and classes v < V, z[n, v] = X[n] . W[v] + b[v]; per
 // block k of kStatCols classes it writes the block max m_part[k][n], the block
-// sum of exp(z - m_part) s_part[k][n], the lowest class index attaining the
+// sum of exp(z - ref) s_part[k][n], the lowest class index attaining the
 // block max i_part[k][n] (if i_part != null), z[n, tc[n]] into zt[n]
-// (tc[n] < 0: none), and when T != null, T(n, v) = exp(z[n, v] - m_part[k][n])
+// (tc[n] < 0: none), and when T != null, T(n, v) = exp(z[n, v] - ref)
 // rounded to the element type, for v < V_pad (0 beyond V), in the panel
 // layout with panel stride tps (T points at the chunk's row 0).
+//   ref = m_part[k][n] (the block max) when rref is null;
+//   ref = rref[n], one reference per row for all its classes, when rref is
+//         set (bf16 with T only).  Rows rows <= n < t_rows of T are then
+//         written as 0 (a ragged chunk's padding, read by grad_W's K range).
+// With `gate` set the launch does nothing unless *gate != 0, and then walks
+// the tiles with a grid of at most one workgroup per CU (the repair pass of
+// rows whose reference was too low).
 struct LogitsLse {
   const void* X; int64_t ldx;     // chunk rows [rows][D]
   const void* W; int64_t ldw;     // [V][D]
@@ -88,6 +99,9 @@ struct LogitsLse {
   void* T; int64_t tps;           // panel layout, or null
   float* m_part; float* s_part; int* i_part; int64_t ldp;   // [V_pad / kStatCols][ldp]
   float* zt;                      // [rows]
+  const float* rref;              // [rows] per-row reference, or null
+  int t_rows;                     // rows of T written (rref set: >= rows)
+  const int* gate;                // null, or the repair flag of the chunk
 };
 hipError_t logits_lse(Elem e, const LogitsLse& a, hipStream_t s);
 
@@ -116,6 +130,37 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
                        const float* wrow, int rows, float* lse, float* loss_rows,
                        int* argmax_out, hipStream_t s);
 
+// Per-row reference of the one-reference plan (bf16): rref[n] = X[n] .
+// W[tc[n]] + b[tc[n]] in fp32 (the target logit, up to rounding order), +inf
+// where tc[n] < 0; also clears flags[0 .. nflags) (nflags <= 64 N).
+hipError_t target_logits(Elem e, const void* X, int64_t ldx, const void* W, int64_t ldw,
+                         const void* bias, const int* tc, int N, int D, float* rref,
+                         int* flags, int nflags, hipStream_t s);
+
+// Row combine of the one-reference plan (bf16): for the chunk's rows, with
+// S = sum_k s_part[k][n] (sums of exp(z - rref[n])) and M the row max,
+//   - tc < 0: loss_rows 0, beta = g * 0;
+//   - M - rref > kRefGap: the reference is too far below the row max (a row
+//     whose loss exceeds kRefGap nats): rref[n] = M and *flag = 1, so that
+//     the gated repair pass recomputes the chunk with that row's max;
+//   - otherwise loss_rows = w (log S + rref - zt), beta = g / S, and the
+//     target entry of T becomes exp(zt - rref) - S, so that
+//     dL[n][v] = beta[n] T(n, v) (softmax times S, minus S at the target).
+// argmax_out as row_combine.  With `gate` set the launch does nothing unless
+// *gate != 0 (the repair's combine).
+constexpr float kRefGap = 40.0f;
+hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* i_part,
+                           int64_t ldp, int n_vt, const float* zt, const int* tc,
+                           const float* wrow, const float* g, int rows, float* rref,
+                           void* T, int64_t tps, float* loss_rows, float* beta,
+                           int* argmax_out, int* flag, const int* gate, hipStream_t s);
+
+// grad_b partials of the one-reference plan (bf16): gb_part[n / 64][v] (ld =
+// V_pad) = sum of beta[n] T(n, v) over the 64-row block, for n < rows_pad
+// (rows past `rows` count 0) and v < V_pad; T in the panel layout.
+hipError_t bias_cols(const void* T, int64_t tps, const float* beta, int rows, int rows_pad,
+                     int V_pad, float* gb_part, hipStream_t s);
+
 // In-place finalize: T(n, v) <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
 // - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V), T
 // in the panel layout with panel stride tps; optionally writes dLt[v][n]
@@ -128,15 +173,18 @@ hipError_t finalize_dlogits(Elem e, void* T, int64_t tps, void* dLt, int64_t ldl
                             int V, int V_pad, float* gb_part, const float* dl_scale,
                             hipStream_t s);
 
-// out[c][r] = r < rows ? in[r][c] : 0 for r < rows_pad, c < cols.
+// out[c][r] = r < rows ? in[r][c] : 0 for r < rows_pad, c < cols; with
+// row_scale (bf16 only) in[r][c] * row_scale[r], rounded once.
 hipError_t transpose_pad(Elem e, const void* in, int64_t ldi, int rows, int cols,
-                         void* out, int64_t ldo, int rows_pad, hipStream_t s);
+                         void* out, int64_t ldo, int rows_pad, hipStream_t s,
+                         const float* row_scale = nullptr);
 
-// out[r][c] = cvt(f * sum_s parts[s][r][c] (+ out[r][c] if accum)) for
-// r < rows, c < cols (ld = cols), f = scale[0] (1 when scale is null).
+// out[r][c] = cvt(f_r * sum_s parts[s][r][c] (+ out[r][c] if accum)) for
+// r < rows, c < cols (ld = cols), f_r = scale[0] (1 when scale is null) times
+// row_scale[r] (1 when row_scale is null).
 hipError_t sum_splits(Elem e, const float* parts, int splits, int64_t stride,
                       int rows, int cols, void* out, bool accum, const float* scale,
-                      hipStream_t s);
+                      hipStream_t s, const float* row_scale = nullptr);
 
 // acc[v] = (first ? 0 : acc[v]) + sum_b parts[b][v]; if last:
 // out[v] = cvt(acc (+ out[v] if accum)).

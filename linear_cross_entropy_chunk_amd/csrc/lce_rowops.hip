@@ -195,6 +195,162 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
   }
 }
 
+// ---------------------------------------------- one-reference plan (bf16)
+// The reference of row n is its target logit, so that T(n, v) = exp(z - ref)
+// holds the softmax up to the row factor 1/S, and the target entry sits at 1.
+// One wave per row: lanes over 16-byte vectors of the row, then the wave's
+// butterfly (a fixed order).  The first nflags threads clear the repair
+// flags of the call's chunks.
+template <typename T>
+__global__ __launch_bounds__(256) void k_target_logit(
+    const T* __restrict__ X, int64_t ldx, const T* __restrict__ W, int64_t ldw,
+    const T* __restrict__ bias, const int* __restrict__ tc, int N, int D,
+    float* __restrict__ rref, int* __restrict__ flags, int nflags) {
+  constexpr int kVec = 16 / sizeof(T);
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid < nflags) flags[gid] = 0;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);     // uniform per wave
+  const int lane = threadIdx.x & 63;
+  if (n >= N) return;
+  const int t = tc[n];
+  if (t < 0) {
+    // no target: exp(z - inf) = 0 leaves the row's T at 0
+    if (lane == 0) rref[n] = INFINITY;
+    return;
+  }
+  const T* x = X + static_cast<int64_t>(n) * ldx;
+  const T* w = W + static_cast<int64_t>(t) * ldw;
+  float acc = 0.0f;
+  for (int d = lane * kVec; d < D; d += 64 * kVec) {
+    const i32x4_t xa = *reinterpret_cast<const i32x4_t*>(x + d);
+    const i32x4_t wa = *reinterpret_cast<const i32x4_t*>(w + d);
+    const T* xe = reinterpret_cast<const T*>(&xa);
+    const T* we = reinterpret_cast<const T*>(&wa);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc += to_f32(xe[e]) * to_f32(we[e]);
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) rref[n] = acc + (bias ? to_f32(bias[t]) : 0.0f);
+}
+
+// The combine of the one-reference plan: the blocks' sums share the row's
+// reference, so they add without rescaling; the row max only checks the
+// reference (and gives the argmax).  Same part layout and fixed merge order
+// as k_row_combine.
+template <typename T>
+__global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine_ref(
+    const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
+    int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
+    const float* __restrict__ wrow, const float* __restrict__ g, int rows,
+    float* __restrict__ rref, T* __restrict__ Tm, int64_t tps, float* __restrict__ loss_rows,
+    float* __restrict__ beta, int* __restrict__ amax, int* flag, const int* gate) {
+  if (gate && *gate == 0) return;                      // uniform: one flag per launch
+  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
+  __shared__ int sk[kCombParts][kCombRows];
+  const int r = threadIdx.x % kCombRows, p = threadIdx.x / kCombRows;
+  const int n = blockIdx.x * kCombRows + r;
+  float m = -INFINITY, s = 0.0f;
+  int kb = 0x7fffffff;
+  if (n < rows) {
+    for (int k0 = p; k0 < n_vt; k0 += kCombBatch * kCombParts) {
+      float mb[kCombBatch], sb[kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const int k = k0 + u * kCombParts;
+        mb[u] = k < n_vt ? mp[k * ldp + n] : -INFINITY;
+        sb[u] = k < n_vt ? sp[k * ldp + n] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (mb[u] > m) {
+          m = mb[u];
+          kb = k0 + u * kCombParts;
+        }
+        s += sb[u];
+      }
+    }
+  }
+  sm[p][r] = m;
+  ss[p][r] = s;
+  sk[p][r] = kb;
+  __syncthreads();
+  if (p != 0 || n >= rows) return;
+  float M = sm[0][r];
+  for (int q = 1; q < kCombParts; ++q) M = fmaxf(M, sm[q][r]);
+  float S = 0.0f;
+  int K = 0x7fffffff;
+  for (int q = 0; q < kCombParts; ++q) {
+    S += ss[q][r];
+    if (sm[q][r] == M && sk[q][r] < K) K = sk[q][r];
+  }
+  // K stays unset only if every block maximum is NaN; read block 0 then.
+  if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
+  const int t = tc[n];
+  const float gn = g[n];
+  if (t < 0) {
+    loss_rows[n] = 0.0f;
+    beta[n] = gn * 0.0f;          // 0, or NaN when the mean has no rows
+    return;
+  }
+  const float ref = rref[n];
+  if (M - ref > kRefGap) {
+    // exp(z - ref) may overflow, or beta underflow: recompute the chunk with
+    // this row's max as its reference
+    rref[n] = M;
+    *flag = 1;
+    return;
+  }
+  const float z = zt[n];
+  loss_rows[n] = (wrow ? wrow[n] : 1.0f) * (logf(S) + (ref - z));
+  beta[n] = gn / S;
+  // dL = g (e / S - onehot) = (g / S) (e - S onehot): the target entry takes
+  // its fp32 e minus S, rounded once
+  Tm[static_cast<int64_t>(t / kTile) * tps + static_cast<int64_t>(n) * kTile + t % kTile] =
+      from_f32<T>(fast_exp(z - ref) - S);
+}
+
+// grad_b partials of the one-reference plan: gb_part[n / 64][v] = sum over
+// 64 rows of beta_n T(n, v), read from T where the logits epilogue and the
+// combine left it (T is not rewritten).  64 rows x 64 classes per workgroup,
+// summed in a fixed order: rows of a quarter in order, then the quarters.
+template <typename T>
+__global__ __launch_bounds__(256) void k_bias_cols(const T* __restrict__ Tm, int64_t tps,
+                                                   const float* __restrict__ beta, int rows,
+                                                   float* __restrict__ gbp, int64_t ldgb) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kVecPerRow = 64 / kVec;
+  constexpr int kPer = 64 * kVecPerRow / 256;          // vectors per thread
+  __shared__ float tile[64][65];
+  __shared__ float bs[64];
+  __shared__ float red[4][64];
+  const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const T* const pan = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile;
+  if (tid < 64) bs[tid] = n0 + tid < rows ? beta[n0 + tid] : 0.0f;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = tid + 256 * u;
+    const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
+    const int n = n0 + rl;
+    i32x4_t raw = i32x4_t{0, 0, 0, 0};
+    if (n < rows) raw = *reinterpret_cast<const i32x4_t*>(pan + static_cast<int64_t>(n) * kTile + cv * kVec);
+    const T* x = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) tile[rl][cv * kVec + e] = n < rows ? bs[rl] * to_f32(x[e]) : 0.0f;
+  }
+  __syncthreads();
+  const int c = tid & 63, qr = tid >> 6;
+  float part = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part += tile[16 * qr + r][c];
+  red[qr][c] = part;
+  __syncthreads();
+  if (tid < 64)
+    gbp[static_cast<int64_t>(blockIdx.y) * ldgb + v0 + tid] =
+        ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
 // ------------------------------------------------------- in-place finalize
 // 64 rows x 64 classes per workgroup; the 64 classes sit in one statistics
 // block of kStatCols classes and in one panel of T.  Writes dL over T, dL^T
@@ -281,10 +437,12 @@ __global__ __launch_bounds__(256) void k_finalize(
 }
 
 // ------------------------------------------------------- padded transpose
-template <typename T>
+// kScale (bf16): row r of the input times row_scale[r], rounded once.
+template <typename T, bool kScale>
 __global__ __launch_bounds__(256) void k_transpose_pad(const T* __restrict__ in, int64_t ldi,
                                                       int rows, int cols, T* __restrict__ out,
-                                                      int64_t ldo, int rows_pad) {
+                                                      int64_t ldo, int rows_pad,
+                                                      const float* __restrict__ row_scale) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kVecPerRow = 64 / kVec;
   __shared__ T tile[64][64 + kVec];
@@ -295,7 +453,14 @@ __global__ __launch_bounds__(256) void k_transpose_pad(const T* __restrict__ in,
     const int r = r0 + rl, c = c0 + cv * kVec;
     i32x4_t raw = i32x4_t{0, 0, 0, 0};
     if (r < rows && c < cols) raw = *reinterpret_cast<const i32x4_t*>(in + static_cast<int64_t>(r) * ldi + c);
-    const T* x = reinterpret_cast<const T*>(&raw);
+    T* x = reinterpret_cast<T*>(&raw);
+    if constexpr (kScale) {
+      if (r < rows) {
+        const float f = row_scale[r];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) x[e] = from_f32<T>(to_f32(x[e]) * f);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < kVec; ++e) tile[rl][cv * kVec + e] = x[e];
   }
@@ -317,12 +482,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ parts, int splits,
                                                    int64_t stride, int64_t count4,
                                                    T* __restrict__ out, int accum,
-                                                   const float* __restrict__ scale) {
+                                                   const float* __restrict__ scale,
+                                                   const float* __restrict__ row_scale,
+                                                   int cols) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= count4) return;
   f32x4_t acc = reinterpret_cast<const f32x4_t*>(parts)[i];
   for (int s = 1; s < splits; ++s) acc += reinterpret_cast<const f32x4_t*>(parts + s * stride)[i];
   if (scale) acc *= scale[0];
+  if (row_scale) acc *= row_scale[4 * i / cols];     // cols % 4 == 0: one row per vector
   if constexpr (sizeof(T) == 4) {
     if (accum) acc += reinterpret_cast<const f32x4_t*>(out)[i];
     reinterpret_cast<f32x4_t*>(out)[i] = acc;
@@ -650,6 +818,38 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
     else { using T = float; KERNEL_CALL; }                 \
   } while (0)
 
+hipError_t target_logits(Elem e, const void* X, int64_t ldx, const void* W, int64_t ldw,
+                         const void* bias, const int* tc, int N, int D, float* rref,
+                         int* flags, int nflags, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (nflags > 64 * static_cast<int64_t>(N)) return hipErrorInvalidValue;
+  LCE_BY_ELEM(e, (k_target_logit<T><<<cdiv_u(N, 4), 256, 0, s>>>(
+                     static_cast<const T*>(X), ldx, static_cast<const T*>(W), ldw,
+                     static_cast<const T*>(bias), tc, N, D, rref, flags, nflags)));
+  return hipGetLastError();
+}
+
+hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* i_part,
+                           int64_t ldp, int n_vt, const float* zt, const int* tc,
+                           const float* wrow, const float* g, int rows, float* rref, void* Tb,
+                           int64_t tps, float* loss_rows, float* beta, int* argmax_out,
+                           int* flag, const int* gate, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  k_row_combine_ref<uint16_t><<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(
+      m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref,
+      static_cast<uint16_t*>(Tb), tps, loss_rows, beta, argmax_out, flag, gate);
+  return hipGetLastError();
+}
+
+hipError_t bias_cols(const void* Tb, int64_t tps, const float* beta, int rows, int rows_pad,
+                     int V_pad, float* gb_part, hipStream_t s) {
+  if (rows_pad <= 0) return hipSuccess;
+  const dim3 grid(V_pad / 64, rows_pad / 64);
+  k_bias_cols<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(Tb), tps, beta, rows,
+                                             gb_part, V_pad);
+  return hipGetLastError();
+}
+
 hipError_t finalize_dlogits(Elem e, void* Tb, int64_t tps, void* dLt, int64_t ldlt,
                             const float* m_part, int64_t ldp, const float* lse, const float* g,
                             const int* tc, int rows, int rows_pad, int V, int V_pad,
@@ -676,26 +876,35 @@ hipError_t scale(Elem e, const void* in, void* out, int64_t n, int64_t cols,
 }
 
 hipError_t transpose_pad(Elem e, const void* in, int64_t ldi, int rows, int cols, void* out,
-                         int64_t ldo, int rows_pad, hipStream_t s) {
+                         int64_t ldo, int rows_pad, hipStream_t s, const float* row_scale) {
   if (rows_pad <= 0 || cols <= 0) return hipSuccess;
+  if (row_scale && e != Elem::kBF16) return hipErrorInvalidValue;
   const dim3 grid(cdiv_u(cols, 64), cdiv_u(rows_pad, 64));
   // a bit copy: both 2-byte types go through the uint16_t instance
-  if (elem_size(e) == 2)
-    k_transpose_pad<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in), ldi, rows,
-                                                   cols, static_cast<uint16_t*>(out), ldo,
-                                                   rows_pad);
+  if (row_scale)
+    k_transpose_pad<uint16_t, true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in), ldi,
+                                                         rows, cols, static_cast<uint16_t*>(out),
+                                                         ldo, rows_pad, row_scale);
+  else if (elem_size(e) == 2)
+    k_transpose_pad<uint16_t, false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in), ldi,
+                                                          rows, cols, static_cast<uint16_t*>(out),
+                                                          ldo, rows_pad, nullptr);
   else
-    k_transpose_pad<float><<<grid, 256, 0, s>>>(static_cast<const float*>(in), ldi, rows, cols,
-                                                static_cast<float*>(out), ldo, rows_pad);
+    k_transpose_pad<float, false><<<grid, 256, 0, s>>>(static_cast<const float*>(in), ldi, rows,
+                                                       cols, static_cast<float*>(out), ldo,
+                                                       rows_pad, nullptr);
   return hipGetLastError();
 }
 
 hipError_t sum_splits(Elem e, const float* parts, int splits, int64_t stride, int rows,
-                      int cols, void* out, bool accum, const float* scale, hipStream_t s) {
+                      int cols, void* out, bool accum, const float* scale, hipStream_t s,
+                      const float* row_scale) {
   const int64_t count4 = static_cast<int64_t>(rows) * cols / 4;
   if (count4 <= 0) return hipSuccess;
+  if (row_scale && cols % 4 != 0) return hipErrorInvalidValue;
   LCE_BY_ELEM(e, (k_sum_splits<T><<<cdiv_u(count4, 256), 256, 0, s>>>(
-                     parts, splits, stride, count4, static_cast<T*>(out), accum, scale)));
+                     parts, splits, stride, count4, static_cast<T*>(out), accum, scale,
+                     row_scale, cols)));
   return hipGetLastError();
 }
 

@@ -1,0 +1,87 @@
+"""Rows far from their target.  The bf16 gradient path keeps one softmax
+reference per row, its target logit: the chunk's tile holds exp(z - z_target)
+and the gradient GEMMs apply g / S per row.  A row whose largest logit lies
+more than 40 nats above its target logit (a loss above 40 nats) has its chunk
+recomputed with the row max as reference.  These cases drive that recompute
+(every row of every chunk; one row in one chunk of several, beside an ignored
+row; every plan) and compare with the fp64 oracle, for bf16 and, on the same
+inputs, for fp16 and fp32, whose path keeps per-block maxima."""
+import numpy as np
+import pytest
+
+import lce_inputs as li
+from gpu_common import check_all, log, oracle, require_gpu, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+GAP = 40.0   # nats between the row max and the target logit that force the recompute
+
+
+def _ref(case, reduction="mean", upstream=None):
+    return oracle.linear_cross_entropy(case["X"], case["W"], case["b"], case["t"],
+                                       reduction=reduction, upstream=upstream)
+
+
+def _far_targets(case, rows):
+    """Targets of `rows` set to their row's lowest logit (the largest loss)."""
+    z = oracle.logits(case["X"], case["W"], case["b"])
+    t = case["t"].copy()
+    t[rows] = np.argmin(z[rows], axis=1)
+    return {**case, "t": t}, z
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_every_row_far_from_its_target(dt):
+    """Logits of spread ~12 per row and every target at the row minimum: almost
+    every row's loss exceeds 40 nats, so every chunk is recomputed."""
+    require_gpu()
+    N, D, V = 300, 64, 1000
+    case = li.small_case(N, D, V, dtype=dt, seed=81, ignore_frac=0.1, w_std=12.0 / np.sqrt(D))
+    counted = np.nonzero(case["t"] != li.IGNORE_INDEX)[0]
+    case, z = _far_targets(case, counted)
+    gap = z.max(axis=1) - z[np.arange(N), np.where(case["t"] >= 0, case["t"], 0)]
+    far = int((gap[counted] > GAP + 1.0).sum())
+    assert far > counted.size // 2, far
+    log(f"far rows dt={dt}: {far} of {counted.size} counted rows beyond {GAP} nats")
+    gpu = run_gpu(case, dt, chunk_rows=64)
+    check_all(gpu, _ref(case), dt, "mean", z=z)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("group_rows", [0, 128])
+def test_one_far_row_in_one_chunk(dt, group_rows):
+    """One row of chunk 2 (of 5) has its input scaled by 32 (exact in every
+    dtype), so its logits spread ~32 and its loss is far above 40 nats; an
+    ignored row sits in the same chunk.  Only that chunk is recomputed; the
+    result matches the oracle and repeats bit for bit."""
+    require_gpu()
+    N, D, V = 600, 64, 2000
+    case = li.small_case(N, D, V, dtype=dt, seed=82, ignore_frac=0.0)
+    X = case["X"].copy()
+    X[300] *= 32.0
+    t = case["t"].copy()
+    t[301] = li.IGNORE_INDEX
+    case = {**case, "X": X, "t": t}
+    case, z = _far_targets(case, [300])
+    assert z[300].max() - z[300, case["t"][300]] > GAP + 1.0
+    log(f"one far row dt={dt} group_rows={group_rows}")
+    a, b = run_gpu(case, dt, chunk_rows=128, group_rows=group_rows, repeat=2)
+    for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    check_all(a, _ref(case), dt, "mean", z=z)
+
+
+@pytest.mark.parametrize("policy", ["accurate", "compact"])
+def test_far_rows_with_none_reduction(policy):
+    """'none' with an upstream gradient per row, far rows in two chunks, both
+    grad_W policies."""
+    require_gpu()
+    N, D, V = 400, 64, 1500
+    case = li.small_case(N, D, V, dtype="bf16", seed=83, ignore_frac=0.1)
+    X = case["X"].copy()
+    X[[10, 250]] *= 32.0
+    case = {**case, "X": X}
+    case, z = _far_targets(case, [10, 250])
+    up = case["u"]
+    gpu = run_gpu(case, "bf16", reduction="none", chunk_rows=128, upstream=up, acc_policy=policy)
+    check_all(gpu, _ref(case, "none", up), "bf16", "none", z=z)
