@@ -76,6 +76,21 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
 __device__ __forceinline__ float to_f32(float f) { return f; }
 __device__ __forceinline__ float to_f32(_Float16 h) { return static_cast<float>(h); }
 
+// One element of type T at byte offset `off` of a buffer, as fp32 (0 past
+// the descriptor's range).
+template <typename T>
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  } else if constexpr (std::is_same_v<T, _Float16>) {
+    return static_cast<float>(
+        __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0)));
+  } else {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0))
+                           << 16);
+  }
+}
+
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Block id -> logical tile id such that XCD x (which receives block ids
@@ -662,6 +677,21 @@ __device__ __forceinline__ void logits_tile(const LogitsLse& a, int tm, int tn, 
   }
   const int t_rows = kRef ? a.t_rows : a.rows;            // rows of T written
 
+  // Bias of the lane's 32 classes, the same in all eight column blocks:
+  // loaded once per tile, unconditionally, through a descriptor over
+  // b[0 .. V), so that classes past V read 0.  One batch with the target
+  // loads above (a per-element guarded load would wait on each).
+  float bcol[kI][4] = {};
+  if (bias) {                                             // uniform
+    const __amdgpu_buffer_rsrc_t rbias =
+        make_rsrc(bias, static_cast<int64_t>(a.V) * static_cast<int64_t>(sizeof(T)));
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        bcol[i][r] = load_elem<T>(rbias, (vlane + kBlk * i + r) * static_cast<int>(sizeof(T)));
+  }
+
   // The epilogue walks the eight 16-column blocks j one at a time so that
   // only 32 accumulators per lane are live in VGPRs.
   // the tile's panel of T; the lane's first class within it
@@ -688,10 +718,7 @@ __device__ __forceinline__ void logits_tile(const LogitsLse& a, int tm, int tn, 
 #pragma unroll
       for (int i = 0; i < kI; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = vlane + kBlk * i + r;
-          acc[i][j][r] += v < a.V ? to_f32(bias[v]) : 0.0f;
-        }
+        for (int r = 0; r < 4; ++r) acc[i][j][r] += bcol[i][r];
     }
     if (v_tail) {
 #pragma unroll
@@ -754,14 +781,20 @@ __device__ __forceinline__ void logits_tile(const LogitsLse& a, int tm, int tn, 
     //    row's reference.  A block wholly past V (max -inf) stores e = 0 and
     //    sum 0.
     const float ref = kRef ? rcol[j] : (mx == -INFINITY ? 0.0f : mx);
+    const float nref = -ref * kLog2e;
     float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // (z - max) first: the maximum maps to exactly 1 (a one-class row has
-        // loss exactly 0), which a fused z log2(e) - max log2(e) would not give
-        const float e = __builtin_amdgcn_exp2f((acc[i][j][r] - ref) * kLog2e);
+        // Block max: (z - max) first, so that the maximum maps to exactly 1
+        // (a one-class row has loss exactly 0), which a fused
+        // z log2(e) - max log2(e) would not give.  Row reference: no entry
+        // needs to be exact (the combine forms the target entry from zt), so
+        // one fused multiply-add forms the argument.
+        const float x = kRef ? __builtin_fmaf(acc[i][j][r], kLog2e, nref)
+                             : (acc[i][j][r] - ref) * kLog2e;
+        const float e = __builtin_amdgcn_exp2f(x);
         acc[i][j][r] = e;
         sum += e;
       }

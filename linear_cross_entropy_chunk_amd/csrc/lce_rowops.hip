@@ -304,9 +304,11 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine_ref(
   loss_rows[n] = (wrow ? wrow[n] : 1.0f) * (logf(S) + (ref - z));
   beta[n] = gn / S;
   // dL = g (e / S - onehot) = (g / S) (e - S onehot): the target entry takes
-  // its fp32 e minus S, rounded once
+  // its fp32 e minus S, rounded once; e is formed as the logits epilogue
+  // forms it (one fused multiply-add, then exp2), so it is the e inside S
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, -ref * kLog2e));
   Tm[static_cast<int64_t>(t / kTile) * tps + static_cast<int64_t>(n) * kTile + t % kTile] =
-      from_f32<T>(fast_exp(z - ref) - S);
+      from_f32<T>(e - S);
 }
 
 // grad_b partials of the one-reference plan: gb_part[n / 64][v] = sum over
