@@ -205,7 +205,7 @@ void plan(lce_handle* h) {
   h->o_gxp = take(static_cast<size_t>(h->splits) * round_up(h->gx_rows, 64) * D * 4,
                   h->want_x && !(h->gx_group && h->splits == 1));
   h->o_gw32 = take(V * D * 4, h->w_acc32);
-  h->o_gbp = take((c / 64) * Vp * 4, h->want_b);
+  h->o_gbp = take((c / 64) * Vp * 4, h->want_b && !h->rowref);   // the finalize's partials
   h->o_gb32 = take(Vp * 4, h->want_b);
   h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_wrow = take(std::max<int64_t>(N, 1) * 4, true);
@@ -653,9 +653,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       }
     }
     if (want_b && rowref)
-      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(Tc, tps, beta + row0, rows, rows_pad,
-                                               static_cast<int>(Vp), gbp, s));
-    if (want_b)
+      LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(Tc, tps, beta + row0, rows, V, gb32, io->grad_b,
+                                               first, last, h->accum, s));
+    else if (want_b)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
                                     last, h->accum, s));
   }

@@ -70,12 +70,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Wave (wm, wn) owns rows wm * 128 + 16 i + ..., columns wn * 128 + 16 j + ...
 typedef f32x4_t Acc[kI][kJ];
 
-__device__ __forceinline__ float to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-__device__ __forceinline__ float to_f32(float f) { return f; }
-__device__ __forceinline__ float to_f32(_Float16 h) { return static_cast<float>(h); }
-
 // One element of type T at byte offset `off` of a buffer, as fp32 (0 past
 // the descriptor's range).
 template <typename T>

@@ -155,11 +155,11 @@ hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* 
                            void* T, int64_t tps, float* loss_rows, float* beta,
                            int* argmax_out, int* flag, const int* gate, hipStream_t s);
 
-// grad_b partials of the one-reference plan (bf16): gb_part[n / 64][v] (ld =
-// V_pad) = sum of beta[n] T(n, v) over the 64-row block, for n < rows_pad
-// (rows past `rows` count 0) and v < V_pad; T in the panel layout.
-hipError_t bias_cols(const void* T, int64_t tps, const float* beta, int rows, int rows_pad,
-                     int V_pad, float* gb_part, hipStream_t s);
+// grad_b of the one-reference plan (bf16), one chunk: for v < V,
+// acc[v] = (first ? 0 : acc[v]) + sum_{n < rows} beta[n] T(n, v); with last,
+// out[v] = cvt(acc (+ out[v] if accum)) instead.  T in the panel layout.
+hipError_t bias_cols(const void* T, int64_t tps, const float* beta, int rows, int V,
+                     float* acc, void* out, bool first, bool last, bool accum, hipStream_t s);
 
 // In-place finalize: T(n, v) <- dL = g_n (T * exp(m_part[v/kStatCols][n] - lse_n)
 // - [v == tc_n]) for n < rows_pad, v < V_pad (0 where n >= rows or v >= V), T

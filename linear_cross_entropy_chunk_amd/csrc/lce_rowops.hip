@@ -134,65 +134,120 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 }
 
 // ------------------------------------------------------------ row combine
-// kCombRows rows x kCombParts parts per workgroup; part p folds statistics
-// blocks p, p + kCombParts, ... of its row (an online max / rescaled sum),
-// then part 0 merges the parts in a fixed order.  The loads of kCombBatch
-// consecutive blocks of a part are issued before any is folded, so a thread
-// waits on memory once per batch rather than once per block (the fold order,
-// and so the result, is the same).
-constexpr int kCombRows = 8, kCombParts = 32, kCombBatch = 4;
-__global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine(
+// kCbRows rows x kCbParts parts per workgroup; part p folds statistics blocks
+// p, p + kCbParts, ... of its row.  The loads of kCbBatch consecutive blocks
+// of a part are issued before any is folded, so a thread waits on memory
+// once per batch.  The parts are then merged in a fixed order, in two levels:
+// groups of kCbGroup consecutive parts, then the groups.  The lanes of a
+// wave cover kCbRows consecutive rows of kCbParts / 8 ... parts, so each load
+// reads kCbRows consecutive floats of one block.
+//   kRef = false: every block has its own max, so sums are rescaled to the
+//                 larger max as they merge (an online log-sum-exp);
+//   kRef = true:  the blocks share the row's reference, so sums just add.
+// The max (and the lowest block attaining it, for the argmax) merges the
+// same way in both: a part's max is never NaN (the fold skips NaN block
+// maxima, as a comparison with NaN is false).
+constexpr int kCbRows = 8, kCbParts = 128, kCbBatch = 4, kCbGroup = 8;
+
+struct Part {
+  float m, s;
+  int k;
+};
+
+template <bool kRef>
+__device__ __forceinline__ Part merge(Part a, Part b) {
+  Part o;
+  const bool take_b = b.m > a.m || (b.m == a.m && b.k < a.k);
+  o.m = take_b ? b.m : a.m;
+  o.k = take_b ? b.k : a.k;
+  if constexpr (kRef) {
+    o.s = a.s + b.s;
+  } else {   // a part with max -inf holds sum 0 (blocks wholly past V)
+    o.s = (a.m > -INFINITY ? a.s * expf(a.m - o.m) : 0.0f) +
+          (b.m > -INFINITY ? b.s * expf(b.m - o.m) : 0.0f);
+  }
+  return o;
+}
+
+template <bool kRef>
+__device__ __forceinline__ Part fold_row(const float* __restrict__ mp,
+                                         const float* __restrict__ sp, int64_t ldp, int n_vt,
+                                         int n, int p) {
+  Part a{-INFINITY, 0.0f, 0x7fffffff};
+  for (int k0 = p; k0 < n_vt; k0 += kCbBatch * kCbParts) {
+    float mb[kCbBatch], sb[kCbBatch];
+#pragma unroll
+    for (int u = 0; u < kCbBatch; ++u) {
+      const int k = k0 + u * kCbParts;
+      mb[u] = k < n_vt ? mp[k * ldp + n] : -INFINITY;
+      sb[u] = k < n_vt ? sp[k * ldp + n] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kCbBatch; ++u) {
+      const float mk = mb[u];
+      if constexpr (kRef) {
+        if (mk > a.m) {
+          a.m = mk;
+          a.k = k0 + u * kCbParts;
+        }
+        a.s += sb[u];
+      } else if (mk > a.m) {
+        a.s = a.s * expf(a.m - mk) + sb[u];
+        a.m = mk;
+        a.k = k0 + u * kCbParts;
+      } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
+        a.s += sb[u] * expf(mk - a.m);
+      }
+    }
+  }
+  return a;
+}
+
+// Every part of the workgroup's rows folded and merged; part 0 of row r gets
+// the row's (max, sum, lowest block of the max).  Returns false for threads
+// that hold no merged row.
+template <bool kRef>
+__device__ __forceinline__ bool combine_parts(const float* __restrict__ mp,
+                                              const float* __restrict__ sp, int64_t ldp,
+                                              int n_vt, int rows, int& n, Part& out) {
+  __shared__ float sm[kCbParts][kCbRows], ss[kCbParts][kCbRows];
+  __shared__ int sk[kCbParts][kCbRows];
+  const int r = threadIdx.x % kCbRows, p = threadIdx.x / kCbRows;
+  n = blockIdx.x * kCbRows + r;
+  const Part a = n < rows ? fold_row<kRef>(mp, sp, ldp, n_vt, n, p)
+                          : Part{-INFINITY, 0.0f, 0x7fffffff};
+  sm[p][r] = a.m;
+  ss[p][r] = a.s;
+  sk[p][r] = a.k;
+  __syncthreads();
+  if (p % kCbGroup == 0) {
+    Part g{sm[p][r], ss[p][r], sk[p][r]};
+    for (int q = p + 1; q < p + kCbGroup; ++q) g = merge<kRef>(g, Part{sm[q][r], ss[q][r], sk[q][r]});
+    sm[p][r] = g.m;
+    ss[p][r] = g.s;
+    sk[p][r] = g.k;
+  }
+  __syncthreads();
+  if (p != 0 || n >= rows) return false;
+  Part t{sm[0][r], ss[0][r], sk[0][r]};
+  for (int q = kCbGroup; q < kCbParts; q += kCbGroup) t = merge<kRef>(t, Part{sm[q][r], ss[q][r], sk[q][r]});
+  out = t;
+  return true;
+}
+
+__global__ __launch_bounds__(kCbRows * kCbParts) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     const float* __restrict__ wrow, int rows, float* __restrict__ lse,
     float* __restrict__ loss_rows, int* __restrict__ amax) {
-  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
-  __shared__ int sk[kCombParts][kCombRows];
-  const int r = threadIdx.x % kCombRows, p = threadIdx.x / kCombRows;
-  const int n = blockIdx.x * kCombRows + r;
-  float m = -INFINITY, s = 0.0f;
-  int kb = 0x7fffffff;
-  if (n < rows) {
-    for (int k0 = p; k0 < n_vt; k0 += kCombBatch * kCombParts) {
-      float mb[kCombBatch], sb[kCombBatch];
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        const int k = k0 + u * kCombParts;
-        mb[u] = k < n_vt ? mp[k * ldp + n] : -INFINITY;
-        sb[u] = k < n_vt ? sp[k * ldp + n] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        const float mk = mb[u];
-        if (mk > m) {
-          s = s * expf(m - mk) + sb[u];
-          m = mk;
-          kb = k0 + u * kCombParts;
-        } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
-          s += sb[u] * expf(mk - m);
-        }
-      }
-    }
-  }
-  sm[p][r] = m;
-  ss[p][r] = s;
-  sk[p][r] = kb;
-  __syncthreads();
-  if (p == 0 && n < rows) {
-    float M = sm[0][r];
-    for (int q = 1; q < kCombParts; ++q) M = fmaxf(M, sm[q][r]);
-    float S = 0.0f;
-    int K = 0x7fffffff;
-    for (int q = 0; q < kCombParts; ++q) {
-      if (sm[q][r] > -INFINITY) S += ss[q][r] * expf(sm[q][r] - M);
-      if (sm[q][r] == M && sk[q][r] < K) K = sk[q][r];
-    }
-    const float L = M + logf(S);
-    lse[n] = L;
-    loss_rows[n] = tc[n] >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt[n]) : 0.0f;
-    // K stays unset only if every block maximum is NaN; read block 0 then.
-    if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
-  }
+  int n;
+  Part t;
+  if (!combine_parts<false>(mp, sp, ldp, n_vt, rows, n, t)) return;
+  const float L = t.m + logf(t.s);
+  lse[n] = L;
+  loss_rows[n] = tc[n] >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt[n]) : 0.0f;
+  // the block stays unset only if every block maximum is NaN; read block 0 then
+  if (amax) amax[n] = ip[static_cast<int64_t>(t.k < n_vt ? t.k : 0) * ldp + n];
 }
 
 // ---------------------------------------------- one-reference plan (bf16)
@@ -235,59 +290,24 @@ __global__ __launch_bounds__(256) void k_target_logit(
 
 // The combine of the one-reference plan: the blocks' sums share the row's
 // reference, so they add without rescaling; the row max only checks the
-// reference (and gives the argmax).  Same part layout and fixed merge order
-// as k_row_combine.
+// reference (and gives the argmax).
 template <typename T>
-__global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine_ref(
+__global__ __launch_bounds__(kCbRows * kCbParts) void k_row_combine_ref(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     const float* __restrict__ wrow, const float* __restrict__ g, int rows,
     float* __restrict__ rref, T* __restrict__ Tm, int64_t tps, float* __restrict__ loss_rows,
     float* __restrict__ beta, int* __restrict__ amax, int* flag, const int* gate) {
   if (gate && *gate == 0) return;                      // uniform: one flag per launch
-  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
-  __shared__ int sk[kCombParts][kCombRows];
-  const int r = threadIdx.x % kCombRows, p = threadIdx.x / kCombRows;
-  const int n = blockIdx.x * kCombRows + r;
-  float m = -INFINITY, s = 0.0f;
-  int kb = 0x7fffffff;
-  if (n < rows) {
-    for (int k0 = p; k0 < n_vt; k0 += kCombBatch * kCombParts) {
-      float mb[kCombBatch], sb[kCombBatch];
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        const int k = k0 + u * kCombParts;
-        mb[u] = k < n_vt ? mp[k * ldp + n] : -INFINITY;
-        sb[u] = k < n_vt ? sp[k * ldp + n] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        if (mb[u] > m) {
-          m = mb[u];
-          kb = k0 + u * kCombParts;
-        }
-        s += sb[u];
-      }
-    }
-  }
-  sm[p][r] = m;
-  ss[p][r] = s;
-  sk[p][r] = kb;
-  __syncthreads();
-  if (p != 0 || n >= rows) return;
-  float M = sm[0][r];
-  for (int q = 1; q < kCombParts; ++q) M = fmaxf(M, sm[q][r]);
-  float S = 0.0f;
-  int K = 0x7fffffff;
-  for (int q = 0; q < kCombParts; ++q) {
-    S += ss[q][r];
-    if (sm[q][r] == M && sk[q][r] < K) K = sk[q][r];
-  }
-  // K stays unset only if every block maximum is NaN; read block 0 then.
-  if (amax) amax[n] = ip[static_cast<int64_t>(K < n_vt ? K : 0) * ldp + n];
-  const int t = tc[n];
+  int n;
+  Part t;
+  if (!combine_parts<true>(mp, sp, ldp, n_vt, rows, n, t)) return;
+  const float M = t.m, S = t.s;
+  // the block stays unset only if every block maximum is NaN; read block 0 then
+  if (amax) amax[n] = ip[static_cast<int64_t>(t.k < n_vt ? t.k : 0) * ldp + n];
+  const int tt = tc[n];
   const float gn = g[n];
-  if (t < 0) {
+  if (tt < 0) {
     loss_rows[n] = 0.0f;
     beta[n] = gn * 0.0f;          // 0, or NaN when the mean has no rows
     return;
@@ -307,50 +327,60 @@ __global__ __launch_bounds__(kCombRows * kCombParts) void k_row_combine_ref(
   // its fp32 e minus S, rounded once; e is formed as the logits epilogue
   // forms it (one fused multiply-add, then exp2), so it is the e inside S
   const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, -ref * kLog2e));
-  Tm[static_cast<int64_t>(t / kTile) * tps + static_cast<int64_t>(n) * kTile + t % kTile] =
+  Tm[static_cast<int64_t>(tt / kTile) * tps + static_cast<int64_t>(n) * kTile + tt % kTile] =
       from_f32<T>(e - S);
 }
 
-// grad_b partials of the one-reference plan: gb_part[n / 64][v] = sum over
-// 64 rows of beta_n T(n, v), read from T where the logits epilogue and the
-// combine left it (T is not rewritten).  64 rows x 64 classes per workgroup,
-// summed in a fixed order: rows of a quarter in order, then the quarters.
+// grad_b of the one-reference plan: acc[v] += sum over the chunk's rows of
+// beta_n T(n, v), read from T where the logits epilogue and the combine left
+// it (T is not rewritten); the last chunk rounds acc into grad_b.  One
+// workgroup per 64 classes: 8 lanes of 16 bytes cover the 64 classes of a
+// row, 32 row groups take every 32nd row, four rows' loads in flight per
+// thread.  Fixed order throughout: each thread's rows in order, then the
+// row groups in order.
+constexpr int kBcGroups = 32, kBcUnroll = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void k_bias_cols(const T* __restrict__ Tm, int64_t tps,
                                                    const float* __restrict__ beta, int rows,
-                                                   float* __restrict__ gbp, int64_t ldgb) {
+                                                   int V, float* __restrict__ acc,
+                                                   T* __restrict__ out, int first, int last,
+                                                   int accum) {
   constexpr int kVec = 16 / sizeof(T);
-  constexpr int kVecPerRow = 64 / kVec;
-  constexpr int kPer = 64 * kVecPerRow / 256;          // vectors per thread
-  __shared__ float tile[64][65];
-  __shared__ float bs[64];
-  __shared__ float red[4][64];
-  const int v0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  const T* const pan = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile;
-  if (tid < 64) bs[tid] = n0 + tid < rows ? beta[n0 + tid] : 0.0f;
-  __syncthreads();
+  static_assert(kVec * 8 == 64 && 8 * kBcGroups == 256, "64 classes x 32 row groups");
+  __shared__ float red[kBcGroups][65];
+  const int v0 = blockIdx.x * 64;
+  const int cv = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const T* const col = Tm + static_cast<int64_t>(v0 / kTile) * tps + v0 % kTile + cv * kVec;
+  float part[kVec] = {};
+  for (int n0 = rg; n0 < rows; n0 += kBcGroups * kBcUnroll) {
+    i32x4_t raw[kBcUnroll];
+    float b[kBcUnroll];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int idx = tid + 256 * u;
-    const int rl = idx / kVecPerRow, cv = idx % kVecPerRow;
-    const int n = n0 + rl;
-    i32x4_t raw = i32x4_t{0, 0, 0, 0};
-    if (n < rows) raw = *reinterpret_cast<const i32x4_t*>(pan + static_cast<int64_t>(n) * kTile + cv * kVec);
-    const T* x = reinterpret_cast<const T*>(&raw);
+    for (int u = 0; u < kBcUnroll; ++u) {
+      const int n = n0 + u * kBcGroups;
+      raw[u] = n < rows ? *reinterpret_cast<const i32x4_t*>(col + static_cast<int64_t>(n) * kTile)
+                        : i32x4_t{0, 0, 0, 0};
+      b[u] = n < rows ? beta[n] : 0.0f;
+    }
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) tile[rl][cv * kVec + e] = n < rows ? bs[rl] * to_f32(x[e]) : 0.0f;
+    for (int u = 0; u < kBcUnroll; ++u) {
+      if (n0 + u * kBcGroups >= rows) break;
+      const T* x = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) part[e] += b[u] * to_f32(x[e]);
+    }
   }
-  __syncthreads();
-  const int c = tid & 63, qr = tid >> 6;
-  float part = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) part += tile[16 * qr + r][c];
-  red[qr][c] = part;
+  for (int e = 0; e < kVec; ++e) red[rg][cv * kVec + e] = part[e];
   __syncthreads();
-  if (tid < 64)
-    gbp[static_cast<int64_t>(blockIdx.y) * ldgb + v0 + tid] =
-        ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (threadIdx.x >= 64) return;
+  const int v = v0 + threadIdx.x;
+  if (v >= V) return;
+  float sum = 0.0f;
+  for (int q = 0; q < kBcGroups; ++q) sum += red[q][threadIdx.x];
+  const float a = (first ? 0.0f : acc[v]) + sum;
+  if (last) out[v] = from_f32<T>(accum ? to_f32(out[v]) + a : a);
+  else acc[v] = a;
 }
 
 // ------------------------------------------------------- in-place finalize
@@ -807,7 +837,7 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
                        int n_vt, const float* zt, const int* tc, const float* wrow, int rows,
                        float* lse, float* loss_rows, int* argmax_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine<<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(
+  k_row_combine<<<cdiv_u(rows, kCbRows), kCbRows * kCbParts, 0, s>>>(
       m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, rows, lse, loss_rows, argmax_out);
   return hipGetLastError();
 }
@@ -837,18 +867,19 @@ hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* 
                            int64_t tps, float* loss_rows, float* beta, int* argmax_out,
                            int* flag, const int* gate, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine_ref<uint16_t><<<cdiv_u(rows, kCombRows), kCombRows * kCombParts, 0, s>>>(
+  k_row_combine_ref<uint16_t><<<cdiv_u(rows, kCbRows), kCbRows * kCbParts, 0, s>>>(
       m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref,
       static_cast<uint16_t*>(Tb), tps, loss_rows, beta, argmax_out, flag, gate);
   return hipGetLastError();
 }
 
-hipError_t bias_cols(const void* Tb, int64_t tps, const float* beta, int rows, int rows_pad,
-                     int V_pad, float* gb_part, hipStream_t s) {
-  if (rows_pad <= 0) return hipSuccess;
-  const dim3 grid(V_pad / 64, rows_pad / 64);
-  k_bias_cols<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(Tb), tps, beta, rows,
-                                             gb_part, V_pad);
+hipError_t bias_cols(const void* Tb, int64_t tps, const float* beta, int rows, int V,
+                     float* acc, void* out, bool first, bool last, bool accum, hipStream_t s) {
+  if (V <= 0) return hipSuccess;
+  k_bias_cols<uint16_t><<<cdiv_u(V, 64), 256, 0, s>>>(static_cast<const uint16_t*>(Tb), tps,
+                                                      beta, rows, V, acc,
+                                                      static_cast<uint16_t*>(out), first, last,
+                                                      accum);
   return hipGetLastError();
 }
 
