@@ -49,11 +49,13 @@ struct lce_handle {
   bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
   bool gx_group;      // one grad_X GEMM per grad_W group (its rows all in T)
   bool rowref;        // one reference per row: T holds dL / beta, no finalize pass
+  int64_t w_tail_cols;  // grad_W: trailing 256-class tile columns split along K (0: none)
+  int w_tail_splits;    // K ranges of those columns
   int64_t gx_rows;    // most rows of one grad_X GEMM
   int64_t t_rows;     // rows R of the exp / dL buffer T (panel layout)
   // workspace offsets (bytes)
   size_t o_T, o_dLt, o_Wt, o_Xt, o_mp, o_sp, o_ip, o_zt, o_lse, o_g, o_tc, o_gxp,
-      o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, o_rref, o_beta, o_flag, total;
+      o_gw32, o_gbp, o_gb32, o_lrows, o_wrow, o_cnt, o_rref, o_beta, o_flag, o_wtail, total;
   TimingPool timing;
 };
 
@@ -170,6 +172,31 @@ void plan(lce_handle* h) {
   // bf16 only: T's entries may exceed 1 (up to e^kRefGap), which fp16 cannot
   // hold.  Not with a staged dL^T, which the finalize pass forms.
   h->rowref = h->elem == lce::Elem::kBF16 && h->want_any && (!h->want_w || h->w_inplace);
+
+  // grad_W's last round.  D/256 x V/256 tiles on 256 CUs leave a partial
+  // last round (at the large-vocabulary head 80 tiles: 31.3 rounds), during
+  // which most CUs idle for a whole tile.  When that remainder is at most
+  // half a round, the trailing V tile columns that hold it go to a second
+  // launch with K split into ranges (fp32 partials, then the deterministic
+  // split sum into grad_W's last rows), so the main launch ends on a full
+  // round and the remainder takes a fraction of one.  Element-type store
+  // modes only (no fp32 V x D accumulator).
+  h->w_tail_cols = 0;
+  h->w_tail_splits = 1;
+  if (h->want_w && !h->w_acc32 && d.N > 0) {
+    const int64_t tm = cdiv64(d.D, lce::kTile), tn = cdiv64(d.V, lce::kTile);
+    const int64_t rem = (tm * tn) % 256;
+    const int64_t cols = rem ? cdiv64(rem, tm) : 0;
+    const int64_t k_max = h->grp * h->c_pad;                 // largest grad_W K
+    if (cols > 0 && cols < tn && cols * tm <= 128) {
+      // as many ranges as fill one round, each at least 4 stages deep
+      const int64_t sp = std::min<int64_t>(256 / (cols * tm), k_max / 256);
+      if (sp >= 2) {
+        h->w_tail_cols = cols;
+        h->w_tail_splits = static_cast<int>(sp);
+      }
+    }
+  }
   h->gx_rows = h->gx_group ? std::min<int64_t>(h->grp * h->c, d.N) : h->c;
   // split-K for grad_X = dL . W: aim at one workgroup per CU (256; two
   // rounds of 512 measured slower: more partials to sum, twice the tile
@@ -214,6 +241,8 @@ void plan(lce_handle* h) {
   h->o_rref = take(std::max<int64_t>(N, 1) * 4, h->rowref);
   h->o_beta = take(std::max<int64_t>(N, 1) * 4, h->rowref);
   h->o_flag = take(std::max<int64_t>(h->n_chunks, 1) * 4, h->rowref);
+  h->o_wtail = take(static_cast<size_t>(h->w_tail_splits) * h->w_tail_cols * lce::kTile * D * 4,
+                    h->w_tail_cols > 0);
   h->total = o;
 }
 
@@ -649,7 +678,33 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
           gw.mode = gfirst && !h->accum ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
         }
         gw.out_scale = dl_unscale;
-        LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gw, s));
+        // the trailing tile columns of a partial last round, split along K
+        const int64_t v_main = V - std::min<int64_t>(V, h->w_tail_cols * lce::kTile);
+        const int k_split = static_cast<int>(   // whole 64-deep stages for every element type
+            round_up(cdiv64(gw.K, std::max(h->w_tail_splits, 1)), 64));
+        const int t_splits = static_cast<int>(cdiv64(gw.K, k_split));
+        if (h->w_tail_cols > 0 && t_splits >= 2 && v_main > 0) {
+          lce::GemmNT gt = gw;
+          gw.N = static_cast<int>(v_main);
+          gt.N = static_cast<int>(V - v_main);
+          if (h->w_inplace) gt.B = static_cast<const char*>(gw.B) + (v_main / lce::kTile) * tps * es;
+          else gt.B = static_cast<const char*>(gw.B) + v_main * h->k_grp * es;
+          gt.splits = t_splits;
+          gt.k_split = k_split;
+          gt.split_stride = static_cast<int64_t>(gt.N) * D;
+          gt.C = at<float>(workspace, h->o_wtail);
+          gt.mode = lce::EpiMode::kStoreF32;
+          gt.out_scale = nullptr;
+          LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gw, s));
+          LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gt, s));
+          LCE_LAUNCH(h, LCE_K_SPLIT_SUM,
+                     lce::sum_splits(el, static_cast<const float*>(gt.C), t_splits,
+                                     gt.split_stride, gt.N, D,
+                                     static_cast<char*>(io->grad_W) + v_main * D * es,
+                                     gw.mode == lce::EpiMode::kAccumOut, dl_unscale, s));
+        } else {
+          LCE_LAUNCH(h, LCE_K_GEMM_W, lce::gemm_nt(el, gw, s));
+        }
       }
     }
     if (want_b && rowref)
