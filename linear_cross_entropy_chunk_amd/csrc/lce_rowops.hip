@@ -134,20 +134,34 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 }
 
 // ------------------------------------------------------------ row combine
-// kCbRows rows x kCbParts parts per workgroup; part p folds statistics blocks
-// p, p + kCbParts, ... of its row.  The loads of kCbBatch consecutive blocks
-// of a part are issued before any is folded, so a thread waits on memory
-// once per batch.  The parts are then merged in a fixed order, in two levels:
-// groups of kCbGroup consecutive parts, then the groups.  The lanes of a
-// wave cover kCbRows consecutive rows of kCbParts / 8 ... parts, so each load
-// reads kCbRows consecutive floats of one block.
+// Each workgroup (kCbThreads threads) takes kRows consecutive rows, each row
+// split into kParts = kCbThreads / kRows parts; part p folds statistics
+// blocks p, p + kParts, ... of its row.  The loads of kBatch blocks of a
+// part are issued before any is folded, so a thread waits on memory once per
+// batch.  The parts are then merged in a fixed order, in two levels: groups
+// of kCbGroup consecutive parts, then the groups.  Two layouts:
+//   - 32 rows x 32 parts (chunks of at least kCbWideRows rows): a wave's 64
+//     lanes are 32 consecutive rows of 2 parts, so each load instruction
+//     reads two whole 128-byte lines and every line of the statistics is
+//     read by one workgroup only;
+//   - 8 rows x 128 parts (smaller chunks, where 32-row workgroups would be
+//     too few to keep the loads in flight): each load reads eight 32-byte
+//     runs, and the four quarters of a line go to four workgroups, often on
+//     different XCDs whose L2s each fetch the whole line.
 //   kRef = false: every block has its own max, so sums are rescaled to the
 //                 larger max as they merge (an online log-sum-exp);
 //   kRef = true:  the blocks share the row's reference, so sums just add.
 // The max (and the lowest block attaining it, for the argmax) merges the
 // same way in both: a part's max is never NaN (the fold skips NaN block
 // maxima, as a comparison with NaN is false).
-constexpr int kCbRows = 8, kCbParts = 128, kCbBatch = 4, kCbGroup = 8;
+constexpr int kCbThreads = 1024, kCbGroup = 8, kCbWideRows = 2048;
+
+template <int kRows>
+struct CbLayout {
+  static constexpr int kParts = kCbThreads / kRows;
+  static constexpr int kBatch = kRows == 32 ? 16 : 4;
+  static_assert(kRows * kParts == kCbThreads && kParts % kCbGroup == 0, "whole groups");
+};
 
 struct Part {
   float m, s;
@@ -169,10 +183,11 @@ __device__ __forceinline__ Part merge(Part a, Part b) {
   return o;
 }
 
-template <bool kRef>
+template <bool kRef, int kRows>
 __device__ __forceinline__ Part fold_row(const float* __restrict__ mp,
                                          const float* __restrict__ sp, int64_t ldp, int n_vt,
                                          int n, int p) {
+  constexpr int kCbParts = CbLayout<kRows>::kParts, kCbBatch = CbLayout<kRows>::kBatch;
   Part a{-INFINITY, 0.0f, 0x7fffffff};
   for (int k0 = p; k0 < n_vt; k0 += kCbBatch * kCbParts) {
     float mb[kCbBatch], sb[kCbBatch];
@@ -206,15 +221,16 @@ __device__ __forceinline__ Part fold_row(const float* __restrict__ mp,
 // Every part of the workgroup's rows folded and merged; part 0 of row r gets
 // the row's (max, sum, lowest block of the max).  Returns false for threads
 // that hold no merged row.
-template <bool kRef>
+template <bool kRef, int kRows>
 __device__ __forceinline__ bool combine_parts(const float* __restrict__ mp,
                                               const float* __restrict__ sp, int64_t ldp,
                                               int n_vt, int rows, int& n, Part& out) {
+  constexpr int kCbRows = kRows, kCbParts = CbLayout<kRows>::kParts;
   __shared__ float sm[kCbParts][kCbRows], ss[kCbParts][kCbRows];
   __shared__ int sk[kCbParts][kCbRows];
   const int r = threadIdx.x % kCbRows, p = threadIdx.x / kCbRows;
   n = blockIdx.x * kCbRows + r;
-  const Part a = n < rows ? fold_row<kRef>(mp, sp, ldp, n_vt, n, p)
+  const Part a = n < rows ? fold_row<kRef, kRows>(mp, sp, ldp, n_vt, n, p)
                           : Part{-INFINITY, 0.0f, 0x7fffffff};
   sm[p][r] = a.m;
   ss[p][r] = a.s;
@@ -235,14 +251,15 @@ __device__ __forceinline__ bool combine_parts(const float* __restrict__ mp,
   return true;
 }
 
-__global__ __launch_bounds__(kCbRows * kCbParts) void k_row_combine(
+template <int kRows>
+__global__ __launch_bounds__(kCbThreads) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     const float* __restrict__ wrow, int rows, float* __restrict__ lse,
     float* __restrict__ loss_rows, int* __restrict__ amax) {
   int n;
   Part t;
-  if (!combine_parts<false>(mp, sp, ldp, n_vt, rows, n, t)) return;
+  if (!combine_parts<false, kRows>(mp, sp, ldp, n_vt, rows, n, t)) return;
   const float L = t.m + logf(t.s);
   lse[n] = L;
   loss_rows[n] = tc[n] >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt[n]) : 0.0f;
@@ -291,8 +308,8 @@ __global__ __launch_bounds__(256) void k_target_logit(
 // The combine of the one-reference plan: the blocks' sums share the row's
 // reference, so they add without rescaling; the row max only checks the
 // reference (and gives the argmax).
-template <typename T>
-__global__ __launch_bounds__(kCbRows * kCbParts) void k_row_combine_ref(
+template <typename T, int kRows>
+__global__ __launch_bounds__(kCbThreads) void k_row_combine_ref(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     const float* __restrict__ wrow, const float* __restrict__ g, int rows,
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(kCbRows * kCbParts) void k_row_combine_ref(
   if (gate && *gate == 0) return;                      // uniform: one flag per launch
   int n;
   Part t;
-  if (!combine_parts<true>(mp, sp, ldp, n_vt, rows, n, t)) return;
+  if (!combine_parts<true, kRows>(mp, sp, ldp, n_vt, rows, n, t)) return;
   const float M = t.m, S = t.s;
   // the block stays unset only if every block maximum is NaN; read block 0 then
   if (amax) amax[n] = ip[static_cast<int64_t>(t.k < n_vt ? t.k : 0) * ldp + n];
@@ -837,8 +854,12 @@ hipError_t row_combine(const float* m_part, const float* s_part, const int* i_pa
                        int n_vt, const float* zt, const int* tc, const float* wrow, int rows,
                        float* lse, float* loss_rows, int* argmax_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine<<<cdiv_u(rows, kCbRows), kCbRows * kCbParts, 0, s>>>(
-      m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, rows, lse, loss_rows, argmax_out);
+  if (rows >= kCbWideRows)
+    k_row_combine<32><<<cdiv_u(rows, 32), kCbThreads, 0, s>>>(
+        m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, rows, lse, loss_rows, argmax_out);
+  else
+    k_row_combine<8><<<cdiv_u(rows, 8), kCbThreads, 0, s>>>(
+        m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, rows, lse, loss_rows, argmax_out);
   return hipGetLastError();
 }
 
@@ -867,9 +888,15 @@ hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* 
                            int64_t tps, float* loss_rows, float* beta, int* argmax_out,
                            int* flag, const int* gate, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  k_row_combine_ref<uint16_t><<<cdiv_u(rows, kCbRows), kCbRows * kCbParts, 0, s>>>(
-      m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref,
-      static_cast<uint16_t*>(Tb), tps, loss_rows, beta, argmax_out, flag, gate);
+  uint16_t* Tm = static_cast<uint16_t*>(Tb);
+  if (rows >= kCbWideRows)
+    k_row_combine_ref<uint16_t, 32><<<cdiv_u(rows, 32), kCbThreads, 0, s>>>(
+        m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref, Tm, tps, loss_rows, beta,
+        argmax_out, flag, gate);
+  else
+    k_row_combine_ref<uint16_t, 8><<<cdiv_u(rows, 8), kCbThreads, 0, s>>>(
+        m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref, Tm, tps, loss_rows, beta,
+        argmax_out, flag, gate);
   return hipGetLastError();
 }
 
