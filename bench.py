@@ -408,8 +408,12 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> dict:
     return {"bytes_each_way": nbytes, "ms": ms, "gbs_read_plus_write": 2 * nbytes / ms / 1e6}
 
 
-# rocprofv3 kernel names of each timed kernel class
-KERNEL_NAMES = {"logits": "k_logits_lse", "gemm_x": "k_gemm_grad_x", "gemm_w": "k_gemm_grad_w",
+# rocprofv3 kernel names of each timed kernel class.  grad_W's main launch
+# stores bf16 (epilogue mode 3); the launch of its trailing tile columns, K
+# split into fp32 partials, is mode 0.
+KERNEL_NAMES = {"logits": "k_logits_lse", "gemm_x": "k_gemm_grad_x",
+                "gemm_w": "k_gemm_grad_w<unsigned short, 3,",
+                "gemm_w_tail": "k_gemm_grad_w<unsigned short, 0,",
                 "ce_rows": "k_ce_rows", "copy": "copyBuffer"}
 
 
