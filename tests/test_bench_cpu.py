@@ -47,17 +47,22 @@ def test_counter_summary_scales_by_the_copy(tmp_path, traffic_file):
         ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1000.0),
         ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1200.0),
         ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 1100.0),
-        ("void lce::k_gemm_grad_w<...>(...)", 50.0),
+        ("void lce::k_gemm_grad_w<unsigned short, 3, false, true>(...)", 50.0),
+        ("void lce::k_gemm_grad_w<unsigned short, 0, false, true>(...)", 5.0),
         ("some_other_kernel", 9e9),
     ])
     _write_csv(write, "WRITE_SIZE", [
         ("copyBuffer(...)", gib_kib),
         ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 300.0),
         ("void lce::k_logits_lse<unsigned short, true, false, false>(...)", 300.0),
-        ("void lce::k_gemm_grad_w<...>(...)", 7.0),
+        ("void lce::k_gemm_grad_w<unsigned short, 3, false, true>(...)", 7.0),
+        ("void lce::k_gemm_grad_w<unsigned short, 0, false, true>(...)", 1.0),
     ])
     out = bench.summarize_counters(str(fetch), str(write), "w1", "cmd")
-    assert set(out) == {"logits", "gemm_w"}
+    # grad_W's main launch (bf16 store) and its K-split tail are kept apart
+    assert set(out) == {"logits", "gemm_w", "gemm_w_tail"}
+    assert out["gemm_w"]["read_bytes"] == pytest.approx(50.0 * 2.0 * 1024)
+    assert out["gemm_w_tail"]["write_bytes"] == pytest.approx(1.0 * 1024)
     lg = out["logits"]
     assert lg["copy_scale_fetch"] == pytest.approx(2.0)
     assert lg["copy_scale_write"] == pytest.approx(1.0)
