@@ -70,6 +70,15 @@ def load_traffic(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+def counted_plan(args, label: str, cfg) -> bool:
+    """Whether this run launches the kernels the committed counters were taken
+    on: the workload's own dtype and the default plan (accurate, the default
+    chunk and group sizes, forward and backward).  Other plans change the
+    launches' shapes, so their traffic is not the counted one."""
+    return (label == cfg.name and args.acc_policy == "accurate" and args.group_rows == 0
+            and args.chunk_rows is None and not args.forward_only)
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -279,7 +288,8 @@ def bench_lce(args) -> dict:
         "group_rows": args.group_rows,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": load_traffic(dom, cfg.name) if label == cfg.name else None,
+                     "traffic": load_traffic(dom, cfg.name) if counted_plan(args, label, cfg)
+                                else None,
                      "avg_launch_ms": per_kernel[dom]["avg_ms"],
                      "flops_per_launch": flops_per_launch},
         "kernels": {k: round(v["ms_total"] / args.steps, 4) for k, v in per_kernel.items()},

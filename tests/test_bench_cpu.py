@@ -108,3 +108,16 @@ def test_bench_flags_parse():
     assert r.returncode == 0
     for flag in ("--group-rows", "--no-per-chunk", "--no-ce"):
         assert flag in r.stdout
+
+
+def test_traffic_only_for_the_counted_plan():
+    """The committed counters were taken on the default plan; compact, a group
+    cap, another chunk size or the loss-only forward launch other shapes."""
+    import argparse
+    cfg = type("Cfg", (), {"name": "large-vocab-bf16"})()
+    base = dict(acc_policy="accurate", group_rows=0, chunk_rows=None, forward_only=False)
+    assert bench.counted_plan(argparse.Namespace(**base), "large-vocab-bf16", cfg)
+    for k, v in (("acc_policy", "compact"), ("group_rows", 2048), ("chunk_rows", 1024),
+                 ("forward_only", True)):
+        assert not bench.counted_plan(argparse.Namespace(**{**base, k: v}), "large-vocab-bf16", cfg)
+    assert not bench.counted_plan(argparse.Namespace(**base), "large-vocab-f16", cfg)
