@@ -49,6 +49,9 @@ struct lce_handle {
   bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
   bool gx_group;      // one grad_X GEMM per grad_W group (its rows all in T)
   bool rowref;        // one reference per row: T holds dL / beta, no finalize pass
+  bool grp_stats;     // whole-tile chunks in groups: statistics buffers for a whole
+                      // group, so the combine (and the gated repair) can run per group
+  int64_t ldp;        // row stride of the statistics partials and zt
   int64_t w_tail_cols;  // grad_W: trailing 256-class tile columns split along K (0: none)
   int w_tail_splits;    // K ranges of those columns
   int64_t gx_rows;    // most rows of one grad_X GEMM
@@ -172,6 +175,13 @@ void plan(lce_handle* h) {
   // bf16 only: T's entries may exceed 1 (up to e^kRefGap), which fp16 cannot
   // hold.  Not with a staged dL^T, which the finalize pass forms.
   h->rowref = h->elem == lce::Elem::kBF16 && h->want_any && (!h->want_w || h->w_inplace);
+  // With chunks on 256-row tile boundaries in groups of several, the
+  // statistics buffers hold a whole group, so that the combine runs once per
+  // group instead of once per chunk (fewer launches, and its rows span the
+  // group): for the one-reference plan when the group's chunks all stay in T
+  // (with the gated repair and the grad_b sums), and for the loss-only
+  // forward of 'none'.
+  h->grp_stats = h->grp > 1 && h->c % lce::kTile == 0;
 
   // grad_W's last round.  D/256 x V/256 tiles on 256 CUs leave a partial
   // last round (at the large-vocabulary head 80 tiles: 31.3 rounds), during
@@ -222,11 +232,12 @@ void plan(lce_handle* h) {
   // 2-byte grad_X reads W in place (k-major operand); fp32 uses a transposed copy
   h->o_Wt = take(D * Vp * es, h->want_x && !h->half);
   h->o_Xt = take(D * h->k_grp * es, h->want_w);
-  h->o_mp = take(h->n_vt * c * 4, true);
-  h->o_sp = take(h->n_vt * c * 4, true);
-  h->o_ip = take(h->n_vt * c * 4, h->want_argmax);
-  h->o_zt = take(c * 4, true);
-  h->o_lse = take(c * 4, true);
+  h->ldp = h->grp_stats ? h->k_grp : c;
+  h->o_mp = take(h->n_vt * h->ldp * 4, true);
+  h->o_sp = take(h->n_vt * h->ldp * 4, true);
+  h->o_ip = take(h->n_vt * h->ldp * 4, h->want_argmax);
+  h->o_zt = take(h->ldp * 4, true);
+  h->o_lse = take(h->ldp * 4, true);
   h->o_g = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_tc = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_gxp = take(static_cast<size_t>(h->splits) * round_up(h->gx_rows, 64) * D * 4,
@@ -501,6 +512,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   float* wrow = at<float>(workspace, h->o_wrow);
   int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
   const bool rowref = h->rowref && grads;
+  // the combine per group (statistics of the whole group): the one-reference
+  // plan with the group's chunks in T, or the loss-only forward
+  const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
   int* flags = at<int>(workspace, h->o_flag);
@@ -585,8 +599,12 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.tc = tc + row0;
     la.rows = rows; la.V = V; la.D = D;
     la.T = grads ? Tc : nullptr; la.tps = tps;
-    la.m_part = mp; la.s_part = sp; la.i_part = h->want_argmax ? ip : nullptr; la.ldp = cp;
-    la.zt = zt;
+    // statistics of the chunk's rows: at column jj c_pad of the group's
+    // buffers when the combine runs per group, else at column 0
+    const int64_t sc = grp_comb ? jj * cp : 0;
+    la.m_part = mp + sc; la.s_part = sp + sc;
+    la.i_part = h->want_argmax ? ip + sc : nullptr; la.ldp = h->ldp;
+    la.zt = zt + sc;
     // one-reference plan: the padding rows up to rows_pad are written as 0
     // (grad_W's K range covers them)
     la.rref = rowref ? rref + row0 : nullptr;
@@ -597,29 +615,52 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
     const float* wrow_c = io->class_weight ? wrow + row0 : nullptr;
     int* amax_c = h->want_argmax ? io->argmax + row0 : nullptr;
-    if (rowref) {
-      // combine, then the repair of rows whose reference was too low: both
-      // launches do nothing unless the combine raised the chunk's flag
-      int* flag = flags + ck;
-      LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine_ref(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
-                                                        wrow_c, g + row0, rows, rref + row0, Tc,
-                                                        tps, loss_rows, beta + row0, amax_c,
-                                                        flag, nullptr, s));
-      lce::LogitsLse lr = la;
+    // combine, then the repair of rows whose reference was too low: both
+    // repair launches do nothing unless the combine raised a flag.  Per
+    // chunk here, or per group at the group's end (below).
+    auto combine_ref = [&](lce::LogitsLse lr, int64_t r0, int nrows, void* Tb, int* flag,
+                           int flag_rows) -> lce_status {
+      float* loss_r = (none && io->loss) ? io->loss + r0 : lrows + r0;
+      const float* wrow_r = io->class_weight ? wrow + r0 : nullptr;
+      int* amax_r = h->want_argmax ? io->argmax + r0 : nullptr;
+      LCE_LAUNCH(h, LCE_K_COMBINE,
+                 lce::row_combine_ref(lr.m_part, lr.s_part, lr.i_part, h->ldp, h->n_vt, lr.zt,
+                                      tc + r0, wrow_r, g + r0, nrows, rref + r0, Tb, tps, loss_r,
+                                      beta + r0, amax_r, flag, flag_rows, nullptr, s));
       lr.gate = flag;
+      lr.gate_rows = flag_rows;
       LCE_LAUNCH(h, LCE_K_REPAIR, lce::logits_lse(el, lr, s));
-      LCE_LAUNCH(h, LCE_K_REPAIR, lce::row_combine_ref(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
-                                                       wrow_c, g + row0, rows, rref + row0, Tc,
-                                                       tps, loss_rows, beta + row0, amax_c,
-                                                       flag, flag, s));
+      LCE_LAUNCH(h, LCE_K_REPAIR,
+                 lce::row_combine_ref(lr.m_part, lr.s_part, lr.i_part, h->ldp, h->n_vt, lr.zt,
+                                      tc + r0, wrow_r, g + r0, nrows, rref + r0, Tb, tps, loss_r,
+                                      beta + r0, amax_r, flag, flag_rows, flag, s));
+      return LCE_OK;
+    };
+    if (rowref && !grp_comb) {
+      const lce_status st = combine_ref(la, row0, rows, Tc, flags + ck, 0);
+      if (st != LCE_OK) return st;
+    } else if (rowref) {
+      // per group: the group's last chunk runs it below
+    } else if (grp_comb) {
+      // loss-only forward: the group's combine after its last chunk's logits
+      if (jj + 1 == h->grp || last) {
+        const int64_t g_row0 = (ck - jj) * h->c;
+        const int g_rows = static_cast<int>(row0 + rows - g_row0);
+        float* loss_g = (none && io->loss) ? io->loss + g_row0 : lrows + g_row0;
+        LCE_LAUNCH(h, LCE_K_COMBINE,
+                   lce::row_combine(mp, sp, ip, h->ldp, h->n_vt, zt, tc + g_row0,
+                                    io->class_weight ? wrow + g_row0 : nullptr, g_rows, lse,
+                                    loss_g, h->want_argmax ? io->argmax + g_row0 : nullptr, s));
+      }
+      continue;
     } else {
-      LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, cp, h->n_vt, zt, tc + row0,
+      LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, h->ldp, h->n_vt, zt, tc + row0,
                                                     wrow_c, rows, lse, loss_rows, amax_c, s));
       if (!grads) continue;
       char* dLt_j = dLt ? static_cast<char*>(dLt) + jj * cp * es : nullptr;
       LCE_LAUNCH(h, LCE_K_FINALIZE, lce::finalize_dlogits(el, Tc, tps,
                                     want_w && !h->w_inplace ? dLt_j : nullptr,
-                                    h->k_grp, mp, cp, lse, g + row0, tc + row0, rows, rows_pad,
+                                    h->k_grp, mp, h->ldp, lse, g + row0, tc + row0, rows, rows_pad,
                                     V, static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale, s));
     }
     if (want_x && !h->gx_group) {
@@ -636,6 +677,27 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       if (jj + 1 == h->grp || last) {
         const int64_t g_row0 = (ck - jj) * h->c;
         const int g_rows = static_cast<int>(row0 + rows - g_row0);
+        const int64_t gi = ck / h->grp;
+        const bool gfirst = gi == 0, glast = last;
+        if (rowref && grp_comb) {
+          // the group's rows back to back from T's row 0 and statistics
+          // column 0; one flag per chunk
+          lce::LogitsLse lg = la;
+          lg.X = Xb + g_row0 * d.D * es;
+          lg.tc = tc + g_row0;
+          lg.rows = g_rows;
+          lg.T = T;
+          lg.m_part = mp; lg.s_part = sp; lg.i_part = h->want_argmax ? ip : nullptr;
+          lg.zt = zt;
+          lg.rref = rref + g_row0;
+          lg.t_rows = static_cast<int>(round_up(g_rows, 64));
+          const lce_status st = combine_ref(lg, g_row0, g_rows, T, flags + (ck - jj),
+                                            static_cast<int>(h->c));
+          if (st != LCE_OK) return st;
+          if (want_b)
+            LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(T, tps, beta + g_row0, g_rows, V, gb32,
+                                                     io->grad_b, gfirst, glast, h->accum, s));
+        }
         // (one-reference plan: X^T's column k times beta_k)
         if (h->w_inplace)
           LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, Xb + g_row0 * d.D * es, D, g_rows,
@@ -650,8 +712,6 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         // grad_W[V][D] += dL^T . X over the group's rows, as (X^T)[D][K]
         // against dL^T with the transposed store: in place, dL is T's panels
         // read k-major; staged, the finalize's dL^T[V][K].
-        const int64_t gi = ck / h->grp;
-        const bool gfirst = gi == 0, glast = last;
         lce::GemmNT gw{};
         gw.A = Xt; gw.lda = h->k_grp;
         gw.K = static_cast<int>(jj * cp + rows_pad);
@@ -707,10 +767,10 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         }
       }
     }
-    if (want_b && rowref)
+    if (want_b && rowref && !grp_comb)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(Tc, tps, beta + row0, rows, V, gb32, io->grad_b,
                                                first, last, h->accum, s));
-    else if (want_b)
+    else if (want_b && !rowref)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
                                     last, h->accum, s));
   }

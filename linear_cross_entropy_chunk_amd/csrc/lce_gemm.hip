@@ -833,21 +833,27 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
   logits_tile<T, kStoreT, kArgmax, kKTail, kRef>(a, tm, tn, lds);
 }
 
-// The repair pass of the one-reference plan: nothing unless the chunk's flag
-// is set (the common case costs one launch), else every tile of the chunk
-// again, walked by a grid of at most one workgroup per CU.  The flag is read
-// by every wave of the workgroup alike, so the exit is uniform; each tile
-// ends with the main loop's barrier, after which the LDS ring is free for the
-// next tile.
+// The repair pass of the one-reference plan: nothing unless a flag is set
+// (the common case costs one launch), else the tiles of the flagged rows
+// again, walked by a grid of at most one workgroup per CU.  Flag k covers
+// gate_rows rows, whole 256-row tiles (0: one flag for all rows).  The flags
+// are read by every wave of the workgroup alike, so the exits and skips are
+// uniform; each tile ends with the main loop's barrier, after which the LDS
+// ring is free for the next tile.
 template <typename T, bool kArgmax, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_logits_repair(LogitsLse a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
-  if (*a.gate == 0) return;
   const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
+  const int per = a.gate_rows > 0 ? a.gate_rows / kTile : tiles_n;   // row tiles per flag
+  const int nflags = cdiv(tiles_n, per);
+  int any = 0;
+  for (int f = 0; f < nflags; ++f) any |= a.gate[f];
+  if (any == 0) return;
   const int tiles = tiles_m * tiles_n;
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     int tm, tn;
     tile_coords(t, tiles_m, tiles_n, 4, tm, tn);
+    if (a.gate[tn / per] == 0) continue;
     logits_tile<T, true, kArgmax, kKTail, true>(a, tm, tn, lds);
   }
 }
@@ -977,7 +983,8 @@ hipError_t launch_logits(const LogitsLse& a, hipStream_t s) {
   if (a.rref && (!std::is_same_v<T, uint16_t> || a.T == nullptr || a.t_rows < a.rows ||
                  static_cast<int64_t>(a.t_rows) > ((a.rows + kTile - 1) / kTile) * kTile))
     return hipErrorInvalidValue;
-  if (a.gate && !a.rref) return hipErrorInvalidValue;
+  if (a.gate && (!a.rref || a.gate_rows < 0 || a.gate_rows % kTile != 0))
+    return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(tiles)), block(kThreads);
   constexpr int kBK = kRowBytes / static_cast<int>(sizeof(T));
   if (a.D % kBK == 0) launch_logits_k<T, false>(a, grid, block, s);

@@ -87,9 +87,11 @@ hipError_t gemm_nt(Elem e, const GemmNT& g, hipStream_t s);
 //   ref = rref[n], one reference per row for all its classes, when rref is
 //         set (bf16 with T only).  Rows rows <= n < t_rows of T are then
 //         written as 0 (a ragged chunk's padding, read by grad_W's K range).
-// With `gate` set the launch does nothing unless *gate != 0, and then walks
-// the tiles with a grid of at most one workgroup per CU (the repair pass of
-// rows whose reference was too low).
+// With `gate` set the launch is the repair pass of rows whose reference was
+// too low: gate[k] is the flag of rows [k gate_rows, (k + 1) gate_rows)
+// (gate_rows a multiple of kTile, or 0 for one flag over all rows); the
+// launch does nothing unless a flag is set, and then recomputes, with a grid
+// of at most one workgroup per CU, the tiles of the flagged rows.
 struct LogitsLse {
   const void* X; int64_t ldx;     // chunk rows [rows][D]
   const void* W; int64_t ldw;     // [V][D]
@@ -101,7 +103,8 @@ struct LogitsLse {
   float* zt;                      // [rows]
   const float* rref;              // [rows] per-row reference, or null
   int t_rows;                     // rows of T written (rref set: >= rows)
-  const int* gate;                // null, or the repair flag of the chunk
+  const int* gate;                // null, or the repair flags
+  int gate_rows;                  // rows per flag (0: one flag)
 };
 hipError_t logits_lse(Elem e, const LogitsLse& a, hipStream_t s);
 
@@ -146,14 +149,17 @@ hipError_t target_logits(Elem e, const void* X, int64_t ldx, const void* W, int6
 //   - otherwise loss_rows = w (log S + rref - zt), beta = g / S, and the
 //     target entry of T becomes exp(zt - rref) - S, so that
 //     dL[n][v] = beta[n] T(n, v) (softmax times S, minus S at the target).
-// argmax_out as row_combine.  With `gate` set the launch does nothing unless
-// *gate != 0 (the repair's combine).
+// argmax_out as row_combine.  flag[k] belongs to rows [k flag_rows,
+// (k + 1) flag_rows) (flag_rows a multiple of 256, or 0 for one flag over all
+// rows).  With `gate` (the same flags) the launch is the repair's combine:
+// rows whose flag is clear are left alone.
 constexpr float kRefGap = 40.0f;
 hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* i_part,
                            int64_t ldp, int n_vt, const float* zt, const int* tc,
                            const float* wrow, const float* g, int rows, float* rref,
                            void* T, int64_t tps, float* loss_rows, float* beta,
-                           int* argmax_out, int* flag, const int* gate, hipStream_t s);
+                           int* argmax_out, int* flag, int flag_rows, const int* gate,
+                           hipStream_t s);
 
 // grad_b of the one-reference plan (bf16), one chunk: for v < V,
 // acc[v] = (first ? 0 : acc[v]) + sum_{n < rows} beta[n] T(n, v); with last,

@@ -314,8 +314,11 @@ __global__ __launch_bounds__(kCbThreads) void k_row_combine_ref(
     int64_t ldp, int n_vt, const float* __restrict__ zt, const int* __restrict__ tc,
     const float* __restrict__ wrow, const float* __restrict__ g, int rows,
     float* __restrict__ rref, T* __restrict__ Tm, int64_t tps, float* __restrict__ loss_rows,
-    float* __restrict__ beta, int* __restrict__ amax, int* flag, const int* gate) {
-  if (gate && *gate == 0) return;                      // uniform: one flag per launch
+    float* __restrict__ beta, int* __restrict__ amax, int* flag, int flag_rows,
+    const int* gate) {
+  // the repair's combine: a workgroup's rows share one flag (flag_rows is a
+  // multiple of the workgroup's rows), so the exit is uniform
+  if (gate && gate[flag_rows > 0 ? blockIdx.x * kRows / flag_rows : 0] == 0) return;
   int n;
   Part t;
   if (!combine_parts<true, kRows>(mp, sp, ldp, n_vt, rows, n, t)) return;
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(kCbThreads) void k_row_combine_ref(
     // exp(z - ref) may overflow, or beta underflow: recompute the chunk with
     // this row's max as its reference
     rref[n] = M;
-    *flag = 1;
+    flag[flag_rows > 0 ? n / flag_rows : 0] = 1;
     return;
   }
   const float z = zt[n];
@@ -886,17 +889,18 @@ hipError_t row_combine_ref(const float* m_part, const float* s_part, const int* 
                            int64_t ldp, int n_vt, const float* zt, const int* tc,
                            const float* wrow, const float* g, int rows, float* rref, void* Tb,
                            int64_t tps, float* loss_rows, float* beta, int* argmax_out,
-                           int* flag, const int* gate, hipStream_t s) {
+                           int* flag, int flag_rows, const int* gate, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (flag_rows < 0 || flag_rows % 256 != 0) return hipErrorInvalidValue;
   uint16_t* Tm = static_cast<uint16_t*>(Tb);
   if (rows >= kCbWideRows)
     k_row_combine_ref<uint16_t, 32><<<cdiv_u(rows, 32), kCbThreads, 0, s>>>(
         m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref, Tm, tps, loss_rows, beta,
-        argmax_out, flag, gate);
+        argmax_out, flag, flag_rows, gate);
   else
     k_row_combine_ref<uint16_t, 8><<<cdiv_u(rows, 8), kCbThreads, 0, s>>>(
         m_part, s_part, i_part, ldp, n_vt, zt, tc, wrow, g, rows, rref, Tm, tps, loss_rows, beta,
-        argmax_out, flag, gate);
+        argmax_out, flag, flag_rows, gate);
   return hipGetLastError();
 }
 

@@ -85,3 +85,59 @@ def test_far_rows_with_none_reduction(policy):
     up = case["u"]
     gpu = run_gpu(case, "bf16", reduction="none", chunk_rows=128, upstream=up, acc_policy=policy)
     check_all(gpu, _ref(case, "none", up), "bf16", "none", z=z)
+
+
+@pytest.mark.parametrize("far_rows", [[600], [5, 300, 700, 1000]])
+def test_far_rows_with_the_combine_per_group(far_rows):
+    """256-row chunks, four to a grad_W group: the statistics, the combine,
+    the gated repair and the grad_b sums run once per group, the repair
+    recomputing only the flagged chunks' tiles.  One far row in chunk 2, or
+    one in every chunk; an ignored row beside the first."""
+    require_gpu()
+    N, D, V = 1024, 64, 2000
+    case = li.small_case(N, D, V, dtype="bf16", seed=84, ignore_frac=0.05)
+    X = case["X"].copy()
+    X[far_rows] *= 32.0
+    t = case["t"].copy()
+    t[far_rows[0] + 1] = li.IGNORE_INDEX
+    case = {**case, "X": X, "t": t}
+    case, z = _far_targets(case, far_rows)
+    assert all(z[r].max() - z[r, case["t"][r]] > GAP + 1.0 for r in far_rows)
+    log(f"far rows per group: {far_rows}")
+    a, b = run_gpu(case, "bf16", chunk_rows=256, group_rows=1024, repeat=2)
+    for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    check_all(a, _ref(case), "bf16", "mean", z=z)
+
+
+def test_combine_per_group_matches_per_chunk():
+    """The same problem with the combine per group (256-row chunks) and per
+    chunk (group_rows = the chunk rows): both meet the oracle's bar, and their
+    losses agree to fp32 rounding."""
+    require_gpu()
+    N, D, V = 1024, 64, 3000
+    case = li.small_case(N, D, V, dtype="bf16", seed=85, ignore_frac=0.1)
+    grp = run_gpu(case, "bf16", chunk_rows=256, group_rows=1024)
+    per = run_gpu(case, "bf16", chunk_rows=256, group_rows=256)
+    ref = _ref(case)
+    check_all(grp, ref, "bf16", "mean")
+    check_all(per, ref, "bf16", "mean")
+    assert abs(grp["loss"][0] - per["loss"][0]) <= 1e-6 * abs(ref["loss"])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_loss_only_forward_with_the_combine_per_group(dt):
+    """'none' without an upstream gradient (the loss-only forward) with
+    256-row chunks four to a group: the statistics of the group's chunks
+    are combined once, after its last chunk; a ragged last group (three
+    chunks, the last one short).  Per-row loss and argmax against the
+    oracle, and the per-chunk combine gives the same losses."""
+    require_gpu()
+    N, D, V = 1700, 64, 2500
+    case = li.small_case(N, D, V, dtype=dt, seed=86, ignore_frac=0.1)
+    grp = run_gpu(case, dt, reduction="none", chunk_rows=256, group_rows=1024)
+    per = run_gpu(case, dt, reduction="none", chunk_rows=256, group_rows=256)
+    ref = _ref(case, "none")
+    check_all(grp, ref, dt, "none", z=oracle.logits(case["X"], case["W"], case["b"]), grads="")
+    np.testing.assert_allclose(grp["loss"], per["loss"], rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(grp["argmax"], per["argmax"])
