@@ -136,3 +136,76 @@ def test_ce_inplace_replays_from_a_graph(V):
         _same({"dl": z.cpu().numpy(), "loss": loss.cpu().numpy(), "nv": nv.cpu().numpy()},
               eager[k], f"replay {k}")
     del graph
+
+
+@pytest.mark.parametrize("chunk,group", [(64, 64), (256, 1024)])
+def test_repair_replays_from_a_graph(chunk, group):
+    """bf16 keeps one softmax reference per row and recomputes, behind a
+    device-side flag, the chunks with a row whose loss exceeds 40 nats.  Three
+    replays of one captured call: the second's inputs have two such rows
+    (input rows scaled by 32, targets at their rows' lowest logits), so its
+    gated repair launches recompute while the first's and third's do
+    nothing.  Per-chunk combine (64-row chunks) and per-group combine
+    (256-row chunks, four to a group); every replay bit for bit against an
+    eager call, the far one also against the oracle."""
+    require_gpu()
+    N, D, V = 1024, 64, 2000
+    far = [300, 700]
+
+    def make(seed, with_far):
+        case = li.small_case(N, D, V, dtype="bf16", seed=seed, ignore_frac=0.05)
+        if with_far:
+            X = case["X"].copy()
+            X[far] *= 32.0
+            z = oracle.logits(X, case["W"], case["b"])
+            t = case["t"].copy()
+            t[far] = np.argmin(z[far], axis=1)
+            case = {**case, "X": X, "t": t}
+        return case
+
+    cases = [make(70, False), make(71, True), make(72, False)]
+    op = LinearCrossEntropy(N, D, V, torch.bfloat16, bias=True, reduction="mean",
+                            chunk_rows=chunk, argmax=True, group_rows=group)
+
+    def upload(case):
+        return (to_dev(case["X"], "bf16"), to_dev(case["W"], "bf16"),
+                torch.from_numpy(case["t"]).to("cuda"), to_dev(case["b"], "bf16"))
+
+    eager = []
+    for case in cases:
+        eager.append(_host(op(*upload(case))))
+    torch.cuda.synchronize()
+
+    X, W, t, b = upload(cases[0])
+    out = op.make_outputs(grads=True)
+    io = op.make_io(X, W, t, b, out=out)
+    op.run_io(io)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        op.run_io(io)
+    log(f"graph repair chunk={chunk} group={group}: captured")
+    for k, case in enumerate(cases):
+        Xk, Wk, tk, bk = upload(case)
+        X.copy_(Xk)
+        W.copy_(Wk)
+        t.copy_(tk)
+        b.copy_(bk)
+        for v in out.values():
+            if v.is_floating_point():
+                v.fill_(float("nan"))
+            else:
+                v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _host(out)
+        _same(got, eager[k], f"replay {k}")
+        if k == 1:
+            ref = oracle.linear_cross_entropy(case["X"], case["W"], case["b"], case["t"],
+                                              reduction="mean")
+            got64 = {kk: v.astype(np.float64) if v.dtype == np.float32 else v
+                     for kk, v in got.items()}
+            check_all(got64, ref, "bf16", "mean",
+                      z=oracle.logits(case["X"], case["W"], case["b"]))
+    del graph
