@@ -513,7 +513,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   int64_t* cnt = at<int64_t>(workspace, h->o_cnt);
   const bool rowref = h->rowref && grads;
   // the combine per group (statistics of the whole group): the one-reference
-  // plan with the group's chunks in T, or the loss-only forward
+  // plan with the group's chunks in T, or a call without gradients
   const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
@@ -642,7 +642,8 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     } else if (rowref) {
       // per group: the group's last chunk runs it below
     } else if (grp_comb) {
-      // loss-only forward: the group's combine after its last chunk's logits
+      // no gradients (the loss-only forward of 'none', or a call that asks
+      // for none): the group's combine after its last chunk's logits
       if (jj + 1 == h->grp || last) {
         const int64_t g_row0 = (ck - jj) * h->c;
         const int g_rows = static_cast<int>(row0 + rows - g_row0);
