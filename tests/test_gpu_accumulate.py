@@ -119,3 +119,30 @@ def test_accumulate_needs_the_buffers():
     with pytest.raises(ValueError):
         op(x, torch.zeros(16, 32, device="cuda"), torch.zeros(8, dtype=torch.int64,
                                                                device="cuda"))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_accumulate_with_ragged_groups(dt, reduction):
+    """256-row chunks four to a group with a ragged end (N=1700: groups of
+    1024 and 676 rows, the last chunk 164 rows), bias: the bf16 path sums
+    grad_b once per group and forms grad_X once per group; every gradient
+    adds into the caller's buffers."""
+    require_gpu()
+    N, D, V = 1700, 512, 3001
+    case = li.small_case(N, D, V, dtype=dt, seed=44, ignore_frac=0.1)
+    up = case["u"] if reduction == "none" else None
+    ref = oracle.linear_cross_entropy(case["X"], case["W"], case["b"], case["t"],
+                                      reduction=reduction, upstream=up)
+    log(f"accumulate, ragged groups, {dt} {reduction}")
+    op = LinearCrossEntropy(N, D, V, TORCH_DT[dt], bias=True, reduction=reduction,
+                            chunk_rows=256, accumulate=True)
+    pre = {k: _prefill(ref[k].shape, np.abs(ref[k]).max(), dt, seed)
+           for seed, k in enumerate(("grad_X", "grad_W", "grad_b"))}
+    out = {k: _dev(v, dt) for k, v in pre.items()}
+    ud = None if up is None else torch.from_numpy(up.astype(np.float32)).to("cuda")
+    op(_dev(case["X"], dt), _dev(case["W"], dt), torch.from_numpy(case["t"]).to("cuda"),
+       _dev(case["b"], dt), grad_output=ud, out=out)
+    torch.cuda.synchronize()
+    for k in ("grad_X", "grad_W", "grad_b"):
+        _check(out[k], pre[k], ref[k], dt, k)

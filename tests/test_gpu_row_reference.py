@@ -141,3 +141,50 @@ def test_loss_only_forward_with_the_combine_per_group(dt):
     check_all(grp, ref, dt, "none", z=oracle.logits(case["X"], case["W"], case["b"]), grads="")
     np.testing.assert_allclose(grp["loss"], per["loss"], rtol=1e-6, atol=1e-6)
     np.testing.assert_array_equal(grp["argmax"], per["argmax"])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("group_rows", [0, 768])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_ragged_groups_with_gradients(dt, group_rows, reduction):
+    """Gradients with 256-row chunks several to a group and a ragged end:
+    N=1700 in 256-row chunks (the last one 164 rows), D=512, V=3001 (a
+    ragged last class tile), bias, 10% ignored rows.  The default cap holds
+    1024 rows for 16-bit types (groups of 4 chunks and 3: 256, 256, 164
+    rows) and 512 for fp32 (groups of 2, the last one 164 rows); a cap of
+    768 rows gives groups of 3 chunks, the last one a single short chunk.
+    bf16 combines each group once after its last chunk; every dtype keeps
+    group-sized statistics.  'none' runs the backward with an upstream
+    gradient per row."""
+    require_gpu()
+    N, D, V = 1700, 512, 3001
+    case = li.small_case(N, D, V, dtype=dt, seed=87, ignore_frac=0.1)
+    up = case["u"] if reduction == "none" else None
+    log(f"ragged groups dt={dt} group_rows={group_rows} {reduction}")
+    gpu = run_gpu(case, dt, reduction=reduction, chunk_rows=256, group_rows=group_rows,
+                  upstream=up)
+    check_all(gpu, _ref(case, reduction, up), dt, reduction,
+              z=oracle.logits(case["X"], case["W"], case["b"]))
+
+
+def test_far_rows_in_a_ragged_last_group():
+    """The gated repair in a ragged last group: N=1700 in 256-row chunks,
+    four to a group (1024 and 676 rows), far rows in the second group's
+    first chunk and in its last chunk of 164 rows, beside an ignored row."""
+    require_gpu()
+    N, D, V = 1700, 64, 2000
+    far = [1100, 1650]
+    case = li.small_case(N, D, V, dtype="bf16", seed=88, ignore_frac=0.05)
+    X = case["X"].copy()
+    X[far] *= 32.0
+    t = case["t"].copy()
+    t[1651] = li.IGNORE_INDEX
+    case = {**case, "X": X, "t": t}
+    case, z = _far_targets(case, far)
+    assert all(z[r].max() - z[r, case["t"][r]] > GAP + 1.0 for r in far)
+    log("far rows in a ragged last group")
+    for reduction in ("mean", "none"):
+        up = case["u"] if reduction == "none" else None
+        gpu = run_gpu(case, "bf16", reduction=reduction, chunk_rows=256, group_rows=1024,
+                      upstream=up)
+        check_all(gpu, _ref(case, reduction, up), "bf16", reduction, z=z)
