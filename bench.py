@@ -13,8 +13,8 @@ HIP events recorded on the library's stream during the timed steps), and the
 fp64 CPU oracle timed on a bounded row sample of the same workload.  The
 default run adds three records to the same line:
   per_chunk  the same workload on the per-chunk path (group_rows = 2048: each
-             chunk's dL consumed by both gradient GEMMs right after its
-             finalize, grad_W carried across chunks in an fp32 accumulator);
+             chunk's dL consumed by both gradient GEMMs right after it is
+             formed, grad_W carried across chunks in an fp32 accumulator);
   ce         the standalone in-place softmax cross-entropy on fp32 logits
              [16384, 131072] (GB/s against 8 TB/s);
   copy       a plain 1 GiB device-to-device copy in the same process, the

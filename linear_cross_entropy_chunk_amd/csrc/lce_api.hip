@@ -143,7 +143,7 @@ void plan(lce_handle* h) {
   // the fp32 V x D accumulator it saves (K up to 4 D / element size), or at
   // most group_rows rows when the descriptor sets it (group_rows <= the chunk
   // rows gives one chunk per group: each chunk's dL is consumed by both
-  // gradient GEMMs right after its finalize, and grad_W is carried across
+  // gradient GEMMs right after it is formed, and grad_W is carried across
   // chunks in an fp32 accumulator).  COMPACT keeps one chunk per group (least
   // memory).  A non-mixed 16-bit layout (acc_dtype = the input dtype)
   // accumulates the gradients in the input dtype chunk by chunk: COMPACT's
