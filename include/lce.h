@@ -253,6 +253,13 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
  * zero grad_X row.  With N == 0, MEAN gives a NaN loss, SUM a zero loss, and
  * grad_W / grad_b are filled with zeros.
  *
+ * NaN in X, W or b propagates as in IEEE arithmetic on the definition: a
+ * row with a NaN logit has a NaN loss (0 if it is not counted) and a NaN
+ * grad_X row, and, since its dL enters every sum over rows (as 0 * NaN on a
+ * row that is not counted), NaN in every element of grad_W and grad_b.  The
+ * argmax of such a row is unspecified.  lce_ce_inplace likewise: a row
+ * holding a NaN logit gets a NaN loss and a NaN gradient row.
+ *
  * `workspace` is a device buffer of at least lce_workspace_size bytes,
  * 256-byte aligned; its contents on entry are irrelevant and on return are
  * unspecified.  Calls that share a workspace or outputs must be ordered on

@@ -176,9 +176,12 @@ __device__ __forceinline__ Part merge(Part a, Part b) {
   o.k = take_b ? b.k : a.k;
   if constexpr (kRef) {
     o.s = a.s + b.s;
-  } else {   // a part with max -inf holds sum 0 (blocks wholly past V)
-    o.s = (a.m > -INFINITY ? a.s * expf(a.m - o.m) : 0.0f) +
-          (b.m > -INFINITY ? b.s * expf(b.m - o.m) : 0.0f);
+  } else {
+    // A part with max -inf holds sum 0 (blocks wholly past V) or NaN (every
+    // logit NaN, which the NaN-skipping max leaves at -inf): its sum is
+    // added as it is, so that a NaN reaches the row's result.
+    o.s = (a.m > -INFINITY ? a.s * expf(a.m - o.m) : a.s) +
+          (b.m > -INFINITY ? b.s * expf(b.m - o.m) : b.s);
   }
   return o;
 }
@@ -210,8 +213,9 @@ __device__ __forceinline__ Part fold_row(const float* __restrict__ mp,
         a.s = a.s * expf(a.m - mk) + sb[u];
         a.m = mk;
         a.k = k0 + u * kCbParts;
-      } else if (mk > -INFINITY) {   // blocks wholly past V hold max -inf, sum 0
-        a.s += sb[u] * expf(mk - a.m);
+      } else {
+        // blocks with max -inf: sum 0 (wholly past V) or NaN (all NaN)
+        a.s += mk > -INFINITY ? sb[u] * expf(mk - a.m) : sb[u];
       }
     }
   }
@@ -669,13 +673,17 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
     }
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u)
-      s += fast_exp(x[u][0] - m) + fast_exp(x[u][1] - m) + fast_exp(x[u][2] - m) +
-           fast_exp(x[u][3] - m);
+      if (base + u * kCeThreads < V4)   // padding adds nothing (its exp would be NaN while m is -inf)
+        s += fast_exp(x[u][0] - m) + fast_exp(x[u][1] - m) + fast_exp(x[u][2] - m) +
+             fast_exp(x[u][3] - m);
   }
+  // A thread whose max is -inf holds sum 0 (no elements) or NaN (every
+  // element NaN, which the NaN-skipping max leaves at -inf): that sum is
+  // added as it is, so that a NaN reaches the row's result.
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
     const float M = fmaxf(m, om);
-    s = (m > -INFINITY ? s * fast_exp(m - M) : 0.0f) + (om > -INFINITY ? os * fast_exp(om - M) : 0.0f);
+    s = (m > -INFINITY ? s * fast_exp(m - M) : s) + (om > -INFINITY ? os * fast_exp(om - M) : os);
     m = M;
   }
   if ((threadIdx.x & 63) == 0) {
@@ -688,7 +696,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
     for (int w = 1; w < kCeThreads / 64; ++w) M = fmaxf(M, wm[w]);
     float S = 0.0f;
     for (int w = 0; w < kCeThreads / 64; ++w)
-      if (wm[w] > -INFINITY) S += wsum[w] * expf(wm[w] - M);
+      S += wm[w] > -INFINITY ? wsum[w] * expf(wm[w] - M) : wsum[w];
     const float L = M + logf(S);
     const float zt = t >= 0 ? z[static_cast<int64_t>(n) * V + t] : 0.0f;
     loss_rows[n] = t >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt) : 0.0f;
