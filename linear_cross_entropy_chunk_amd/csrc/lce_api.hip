@@ -739,8 +739,11 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
           gw.mode = gfirst && !h->accum ? lce::EpiMode::kStoreOut : lce::EpiMode::kAccumOut;
         }
         gw.out_scale = dl_unscale;
-        // the trailing tile columns of a partial last round, split along K
-        const int64_t v_main = V - std::min<int64_t>(V, h->w_tail_cols * lce::kTile);
+        // the trailing tile columns of a partial last round, split along K:
+        // classes from the first of those columns on (a tile boundary, also
+        // when the last column is ragged)
+        const int64_t v_main =
+            std::max<int64_t>(0, cdiv64(V, lce::kTile) - h->w_tail_cols) * lce::kTile;
         const int k_split = static_cast<int>(   // whole 64-deep stages for every element type
             round_up(cdiv64(gw.K, std::max(h->w_tail_splits, 1)), 64));
         const int t_splits = static_cast<int>(cdiv64(gw.K, k_split));
