@@ -257,7 +257,8 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
  * row with a NaN logit has a NaN loss (0 if it is not counted) and a NaN
  * grad_X row, and, since its dL enters every sum over rows (as 0 * NaN on a
  * row that is not counted), NaN in every element of grad_W and grad_b.  The
- * argmax of such a row is unspecified.  lce_ce_inplace likewise: a row
+ * argmax of a row whose logits are all NaN is 0; with some NaN logits it is
+ * a valid class, otherwise unspecified.  lce_ce_inplace likewise: a row
  * holding a NaN logit gets a NaN loss and a NaN gradient row.
  *
  * `workspace` is a device buffer of at least lce_workspace_size bytes,

@@ -255,6 +255,17 @@ __device__ __forceinline__ bool combine_parts(const float* __restrict__ mp,
   return true;
 }
 
+// The row's argmax from the partials of the block holding its max.  No
+// block is chosen only if every block maximum is NaN (NaN-skipping maxima
+// leave -inf and no class), and a block with no class holds 0x7fffffff:
+// such a row, whose every logit is NaN, gets class 0, the first NaN, so the
+// result is always a valid class.
+__device__ __forceinline__ int row_argmax(const int* __restrict__ ip, int64_t ldp, int n_vt,
+                                          int k, int n) {
+  const int a = ip[static_cast<int64_t>(k < n_vt ? k : 0) * ldp + n];
+  return a == 0x7fffffff ? 0 : a;
+}
+
 template <int kRows>
 __global__ __launch_bounds__(kCbThreads) void k_row_combine(
     const float* __restrict__ mp, const float* __restrict__ sp, const int* __restrict__ ip,
@@ -267,8 +278,7 @@ __global__ __launch_bounds__(kCbThreads) void k_row_combine(
   const float L = t.m + logf(t.s);
   lse[n] = L;
   loss_rows[n] = tc[n] >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt[n]) : 0.0f;
-  // the block stays unset only if every block maximum is NaN; read block 0 then
-  if (amax) amax[n] = ip[static_cast<int64_t>(t.k < n_vt ? t.k : 0) * ldp + n];
+  if (amax) amax[n] = row_argmax(ip, ldp, n_vt, t.k, n);
 }
 
 // ---------------------------------------------- one-reference plan (bf16)
@@ -327,8 +337,7 @@ __global__ __launch_bounds__(kCbThreads) void k_row_combine_ref(
   Part t;
   if (!combine_parts<true, kRows>(mp, sp, ldp, n_vt, rows, n, t)) return;
   const float M = t.m, S = t.s;
-  // the block stays unset only if every block maximum is NaN; read block 0 then
-  if (amax) amax[n] = ip[static_cast<int64_t>(t.k < n_vt ? t.k : 0) * ldp + n];
+  if (amax) amax[n] = row_argmax(ip, ldp, n_vt, t.k, n);
   const int tt = tc[n];
   const float gn = g[n];
   if (tt < 0) {

@@ -10,9 +10,9 @@ masking beyond what the definition states).
 - The standalone CE: a NaN logit makes its row's loss and gradient row NaN.
 
 The GPU's NaN positions must equal the oracle's, and its finite values meet
-the usual tolerances.  The argmax of a row whose logits include a NaN is not
-specified (the oracle's is numpy's first-NaN rule) and is compared on the
-finite rows only."""
+the usual tolerances.  The argmax of a row whose logits are all NaN is class
+0 (numpy's first-NaN rule, the oracle's); with only some logits NaN it is
+not specified, but it is a valid class."""
 import numpy as np
 import pytest
 
@@ -46,6 +46,10 @@ def _check(gpu, ref, dt, reduction, z):
         ok = _finite_rows(ref[key]) if ref[key].ndim > 1 else ~np.isnan(ref[key])
         if ok.any():
             check_grad(gpu[key][ok], ref[key][ok], dt, key)
+    all_nan = np.isnan(z).all(axis=1)
+    np.testing.assert_array_equal(gpu["argmax"][all_nan], 0)
+    np.testing.assert_array_equal(ref["argmax"][all_nan], 0)
+    assert np.all((gpu["argmax"] >= 0) & (gpu["argmax"] < z.shape[1]))
     rows = ~np.isnan(z).any(axis=1)
     zs = np.sort(z[rows], axis=1)
     check_argmax(gpu["argmax"][rows], ref["argmax"][rows], zs[:, -1] - zs[:, -2], zs[:, -1],
@@ -93,6 +97,7 @@ def test_nan_in_one_row_of_w(dt):
     np.testing.assert_array_equal(gpu["loss"][~counted], 0.0)
     for key in ("grad_X", "grad_W", "grad_b"):
         _same_nans(gpu[key], ref[key], key)
+    assert np.all((gpu["argmax"] >= 0) & (gpu["argmax"] < V))
 
 
 def test_nan_logit_in_the_standalone_ce():
@@ -136,6 +141,7 @@ def test_a_whole_statistics_block_of_nan(dt, upstream):
     assert np.isnan(ref["loss"][counted]).all()
     _same_nans(gpu["loss"], ref["loss"], "loss")
     np.testing.assert_array_equal(gpu["loss"][~counted], 0.0)
+    assert np.all((gpu["argmax"] >= 0) & (gpu["argmax"] < V))
     if upstream:
         for key in ("grad_X", "grad_W", "grad_b"):
             _same_nans(gpu[key], ref[key], key)
