@@ -293,7 +293,13 @@ def bench_lce(args) -> dict:
                      "avg_launch_ms": per_kernel[dom]["avg_ms"],
                      "flops_per_launch": flops_per_launch},
         "kernels": {k: round(v["ms_total"] / args.steps, 4) for k, v in per_kernel.items()},
+        # every GEMM class does 2*N*V*D flops per step (grad_W's class includes
+        # its K-split tail launch), so its rate is those flops over its time
+        "kernel_tflops": {k: round(2.0 * N * V * D / (per_kernel[k]["ms_total"] / args.steps / 1e3)
+                                   / 1e12, 1)
+                          for k in ("logits", "gemm_x", "gemm_w") if k in per_kernel},
     }
+    result["kernel_frac"] = {k: round(v / peak, 4) for k, v in result["kernel_tflops"].items()}
     if args.graph:
         result["graph"] = True
         result["eager_ms_per_step"] = eager_ms
