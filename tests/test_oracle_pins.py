@@ -448,3 +448,35 @@ def test_standalone_ce_class_weights_match_torch(reduction):
     l, dl = oracle.softmax_cross_entropy(z, t, reduction=reduction, grad_scale=1.5, class_weight=cw)
     np.testing.assert_allclose(l, loss.detach().numpy(), rtol=1e-13)
     np.testing.assert_allclose(dl, zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------ NaN propagation
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_nan_rows_propagate_as_in_torch(reduction):
+    """A NaN in one counted input row and in one ignored row: the oracle's
+    loss and gradients hold NaN exactly where torch's float64 cross_entropy
+    with autograd does (the ignored row's loss stays 0, its dL is 0 * NaN),
+    and equal torch's values elsewhere."""
+    case = _case(N=8, D=5, V=11, seed=4, ignore_frac=0.0)
+    X, t = case["X"].astype(np.float64), case["t"].copy()
+    X[2, 1] = np.nan
+    X[5, 3] = np.nan
+    t[5] = -100
+    ref = oracle.linear_cross_entropy(X, case["W"], case["b"], t, reduction=reduction,
+                                      upstream=np.ones(8) if reduction == "none" else None)
+    Xt = torch.tensor(X, requires_grad=True)
+    Wt = torch.tensor(case["W"], dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(case["b"], dtype=torch.float64, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(Xt @ Wt.T + bt, torch.tensor(t),
+                                             ignore_index=-100, reduction=reduction)
+    (loss.sum() if reduction == "none" else loss).backward()
+    got = {"loss": loss.detach().numpy(), "grad_X": Xt.grad.numpy(),
+           "grad_W": Wt.grad.numpy(), "grad_b": bt.grad.numpy()}
+    for k, v in got.items():
+        r = np.asarray(ref[k], np.float64).reshape(np.shape(v))
+        np.testing.assert_array_equal(np.isnan(r), np.isnan(v), err_msg=k)
+        ok = ~np.isnan(v)
+        np.testing.assert_allclose(r[ok], v[ok], rtol=1e-12, atol=1e-12, err_msg=k)
+    assert np.isnan(got["grad_W"]).all() and np.isnan(got["grad_X"][[2, 5]]).all()
+    if reduction == "none":
+        assert np.isnan(got["loss"][2]) and got["loss"][5] == 0.0
