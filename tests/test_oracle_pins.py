@@ -480,3 +480,22 @@ def test_nan_rows_propagate_as_in_torch(reduction):
     assert np.isnan(got["grad_W"]).all() and np.isnan(got["grad_X"][[2, 5]]).all()
     if reduction == "none":
         assert np.isnan(got["loss"][2]) and got["loss"][5] == 0.0
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_standalone_ce_nan_row_as_in_torch(reduction):
+    """A NaN logit in one row: the standalone CE's loss and in-place gradient
+    hold NaN where torch's float64 cross_entropy with autograd does."""
+    rng = np.random.default_rng(12)
+    z = rng.standard_normal((6, 13))
+    z[3, 7] = np.nan
+    t = rng.integers(0, 13, 6)
+    loss, dl = oracle.softmax_cross_entropy(z, t, reduction=reduction)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(t), reduction=reduction)
+    (lt.sum() if reduction == "none" else lt).backward()
+    for got, want, name in ((np.atleast_1d(loss), np.atleast_1d(lt.detach().numpy()), "loss"),
+                            (dl, zt.grad.numpy(), "gradient")):
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(want), err_msg=name)
+        ok = ~np.isnan(want)
+        np.testing.assert_allclose(got[ok], want[ok], rtol=1e-12, atol=1e-12, err_msg=name)
