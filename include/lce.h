@@ -19,8 +19,9 @@
  *     apply (grad_X's rows as they are stored, X's rows as they are staged
  *     for grad_W, the rows of the grad_b sums), so no pass rewrites the
  *     tile.  A row whose largest logit exceeds r_n by more than 40 (a loss
- *     above 40 nats, where exp(z - r_n) could overflow) has its chunk
- *     recomputed, on the device, with the row max as its reference.
+ *     above 40 nats, where exp(z - r_n) could overflow) has the 256-row
+ *     tile that holds it recomputed, on the device, with the row max as its
+ *     reference.
  *   - fp16 and fp32 (and bf16 with the staged dL^T below): exp(z - block
  *     max), rewritten in place into dL by a finalize pass.
  * Which rows of that tile the workspace holds at once depends on the grad_W

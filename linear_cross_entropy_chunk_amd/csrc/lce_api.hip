@@ -251,7 +251,9 @@ void plan(lce_handle* h) {
   h->o_cnt = take(3 * 8 + 2 * 4, true);
   h->o_rref = take(std::max<int64_t>(N, 1) * 4, h->rowref);
   h->o_beta = take(std::max<int64_t>(N, 1) * 4, h->rowref);
-  h->o_flag = take(std::max<int64_t>(h->n_chunks, 1) * 4, h->rowref);
+  // one repair flag per 256-row tile of each chunk (chunk ck's at ck * fpc)
+  h->o_flag = take(std::max<int64_t>(h->n_chunks * cdiv64(h->c_pad, lce::kTile), 1) * 4,
+                   h->rowref);
   h->o_wtail = take(static_cast<size_t>(h->w_tail_splits) * h->w_tail_cols * lce::kTile * D * 4,
                     h->w_tail_cols > 0);
   h->total = o;
@@ -517,7 +519,10 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
+  // repair flags, one per 256-row tile of a chunk, so that a row whose
+  // reference is too low costs the recompute of its tile's rows only
   int* flags = at<int>(workspace, h->o_flag);
+  const int64_t fpc = cdiv64(h->c_pad, lce::kTile);
   // fp16 keeps dL times a power of two 2^k (from the largest row weight) so
   // that it stays inside fp16's range; the gradients' element-type stores
   // multiply by 2^-k.  Exact scalings: no rounding is added.
@@ -539,7 +544,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     LCE_LAUNCH(h, LCE_K_TRANSPOSE, lce::transpose_pad(el, io->W, D, V, D, Wt, Vp, static_cast<int>(Vp), s));
   if (rowref)
     LCE_LAUNCH(h, LCE_K_PREP, lce::target_logits(el, io->X, D, io->W, D, io->b, tc, N, D, rref,
-                                                 flags, static_cast<int>(h->n_chunks), s));
+                                                 flags, static_cast<int>(h->n_chunks * fpc), s));
 
   // grad_X[xrow0 .. + nrows) = dL . W for dL rows held in T from Tb on, with
   // M = D against dL[rows][V] (K = V): the transposed store writes grad_X
@@ -637,7 +642,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
       return LCE_OK;
     };
     if (rowref && !grp_comb) {
-      const lce_status st = combine_ref(la, row0, rows, Tc, flags + ck, 0);
+      const lce_status st = combine_ref(la, row0, rows, Tc, flags + ck * fpc, lce::kTile);
       if (st != LCE_OK) return st;
     } else if (rowref) {
       // per group: the group's last chunk runs it below
@@ -682,7 +687,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
         const bool gfirst = gi == 0, glast = last;
         if (rowref && grp_comb) {
           // the group's rows back to back from T's row 0 and statistics
-          // column 0; one flag per chunk
+          // column 0; one flag per 256-row tile
           lce::LogitsLse lg = la;
           lg.X = Xb + g_row0 * d.D * es;
           lg.tc = tc + g_row0;
@@ -692,8 +697,10 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
           lg.zt = zt;
           lg.rref = rref + g_row0;
           lg.t_rows = static_cast<int>(round_up(g_rows, 64));
-          const lce_status st = combine_ref(lg, g_row0, g_rows, T, flags + (ck - jj),
-                                            static_cast<int>(h->c));
+          // (the chunks are whole 256-row tiles here, so the group's flags
+          // follow one another as its rows do)
+          const lce_status st = combine_ref(lg, g_row0, g_rows, T, flags + (ck - jj) * fpc,
+                                            lce::kTile);
           if (st != LCE_OK) return st;
           if (want_b)
             LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(T, tps, beta + g_row0, g_rows, V, gb32,

@@ -144,8 +144,8 @@ hipError_t target_logits(Elem e, const void* X, int64_t ldx, const void* W, int6
 // S = sum_k s_part[k][n] (sums of exp(z - rref[n])) and M the row max,
 //   - tc < 0: loss_rows 0, beta = g * 0;
 //   - M - rref > kRefGap: the reference is too far below the row max (a row
-//     whose loss is then above kRefGap nats): rref[n] = M and *flag = 1, so that
-//     the gated repair pass recomputes the chunk with that row's max;
+//     whose loss is then above kRefGap nats): rref[n] = M and its flag is set,
+//     so that the gated repair pass recomputes the flag's rows with that row's max;
 //   - otherwise loss_rows = w (log S + rref - zt), beta = g / S, and the
 //     target entry of T becomes exp(zt - rref) - S, so that
 //     dL[n][v] = beta[n] T(n, v) (softmax times S, minus S at the target).

@@ -1,8 +1,8 @@
 """Rows far from their target.  The bf16 gradient path keeps one softmax
 reference per row, its target logit: the chunk's tile holds exp(z - z_target)
 and the gradient GEMMs apply g / S per row.  A row whose largest logit lies
-more than 40 nats above its target logit (a loss above 40 nats) has its chunk
-recomputed with the row max as reference.  These cases drive that recompute
+more than 40 nats above its target logit (a loss above 40 nats) has its
+256-row tile recomputed with the row max as reference.  These cases drive that recompute
 (every row of every chunk; one row in one chunk of several, beside an ignored
 row; every plan) and compare with the fp64 oracle, for bf16 and, on the same
 inputs, for fp16 and fp32, whose path keeps per-block maxima."""
@@ -52,8 +52,9 @@ def test_every_row_far_from_its_target(dt):
 def test_one_far_row_in_one_chunk(dt, group_rows):
     """One row of chunk 2 (of 5) has its input scaled by 32 (exact in every
     dtype), so its logits spread ~32 and its loss is far above 40 nats; an
-    ignored row sits in the same chunk.  Only that chunk is recomputed; the
-    result matches the oracle and repeats bit for bit."""
+    ignored row sits in the same chunk.  Only that row's tile (the whole
+    128-row chunk) is recomputed; the result matches the oracle and repeats
+    bit for bit."""
     require_gpu()
     N, D, V = 600, 64, 2000
     case = li.small_case(N, D, V, dtype=dt, seed=82, ignore_frac=0.0)
@@ -91,7 +92,7 @@ def test_far_rows_with_none_reduction(policy):
 def test_far_rows_with_the_combine_per_group(far_rows):
     """256-row chunks, four to a grad_W group: the statistics, the combine,
     the gated repair and the grad_b sums run once per group, the repair
-    recomputing only the flagged chunks' tiles.  One far row in chunk 2, or
+    recomputing only the flagged 256-row tiles.  One far row in chunk 2, or
     one in every chunk; an ignored row beside the first."""
     require_gpu()
     N, D, V = 1024, 64, 2000
@@ -188,3 +189,25 @@ def test_far_rows_in_a_ragged_last_group():
         gpu = run_gpu(case, "bf16", reduction=reduction, chunk_rows=256, group_rows=1024,
                       upstream=up)
         check_all(gpu, _ref(case, reduction, up), "bf16", reduction, z=z)
+
+
+@pytest.mark.parametrize("group_rows", [1024, 2048])
+def test_far_row_inside_a_long_chunk(group_rows):
+    """1024-row chunks (four 256-row tiles each), one far row in the third
+    tile of the second chunk and one in the last tile of the last chunk:
+    only those tiles' rows are recomputed, per chunk (group_rows = the chunk)
+    or per group of two chunks."""
+    require_gpu()
+    N, D, V = 3000, 64, 2500
+    far = [1024 + 600, 2990]
+    case = li.small_case(N, D, V, dtype="bf16", seed=89, ignore_frac=0.05)
+    X = case["X"].copy()
+    X[far] *= 32.0
+    case = {**case, "X": X}
+    case, z = _far_targets(case, far)
+    assert all(z[r].max() - z[r, case["t"][r]] > GAP + 1.0 for r in far)
+    log(f"far rows inside long chunks, group_rows={group_rows}")
+    a, b = run_gpu(case, "bf16", chunk_rows=1024, group_rows=group_rows, repeat=2)
+    for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    check_all(a, _ref(case), "bf16", "mean", z=z)
