@@ -835,26 +835,36 @@ __global__ __launch_bounds__(kThreads) void k_logits_lse(LogitsLse a) {
 
 // The repair pass of the one-reference plan: nothing unless a flag is set
 // (the common case costs one launch), else the tiles of the flagged rows
-// again, walked by a grid of at most one workgroup per CU.  Flag k covers
-// gate_rows rows, whole 256-row tiles (0: one flag for all rows).  The flags
-// are read by every wave of the workgroup alike, so the exits and skips are
-// uniform; each tile ends with the main loop's barrier, after which the LDS
-// ring is free for the next tile.
+// again, shared evenly by a grid of at most one workgroup per CU.  Flag f
+// covers gate_rows rows, whole 256-row tiles (0: one flag for all rows).
+// The work items are (flagged row tile, class tile) pairs, numbered row
+// tile by row tile; workgroup b takes items b, b + grid, ...  The flags are
+// read by every wave of the workgroup alike, so the exits and the search
+// for an item's row tile are uniform; each tile ends with the main loop's
+// barrier, after which the LDS ring is free for the next tile.
 template <typename T, bool kArgmax, bool kKTail>
 __global__ __launch_bounds__(kThreads) void k_logits_repair(LogitsLse a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsOperandBytes];
   const int tiles_m = cdiv(a.V, kTile), tiles_n = cdiv(a.rows, kTile);
   const int per = a.gate_rows > 0 ? a.gate_rows / kTile : tiles_n;   // row tiles per flag
   const int nflags = cdiv(tiles_n, per);
-  int any = 0;
-  for (int f = 0; f < nflags; ++f) any |= a.gate[f];
-  if (any == 0) return;
-  const int tiles = tiles_m * tiles_n;
-  for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
-    int tm, tn;
-    tile_coords(t, tiles_m, tiles_n, 4, tm, tn);
-    if (a.gate[tn / per] == 0) continue;
-    logits_tile<T, true, kArgmax, kKTail, true>(a, tm, tn, lds);
+  int flagged = 0;                                   // flagged row tiles
+  for (int f = 0; f < nflags; ++f)
+    if (a.gate[f]) flagged += min(per, tiles_n - f * per);
+  const int items = flagged * tiles_m;
+  for (int w = blockIdx.x; w < items; w += gridDim.x) {
+    // the (w / tiles_m)-th flagged row tile, in row order
+    int k = w / tiles_m, tn = 0;
+    for (int f = 0; f < nflags; ++f) {
+      if (!a.gate[f]) continue;
+      const int cnt = min(per, tiles_n - f * per);
+      if (k < cnt) {
+        tn = f * per + k;
+        break;
+      }
+      k -= cnt;
+    }
+    logits_tile<T, true, kArgmax, kKTail, true>(a, w % tiles_m, tn, lds);
   }
 }
 
