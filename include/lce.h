@@ -364,13 +364,17 @@ enum {
  * with a profiler, Liger-Kernel issue #343's proton run).  While enabled, every launch of a kernel class
  * whose bit (1u << LCE_K_*) is in `kernel_mask` is bracketed by two
  * hipEventRecord calls on the call's stream (events come from a fixed pool
- * created here; launches beyond the pool are not timed).  mask 0 disables
- * the hook and releases the events.  Host only; HIP errors -> LCE_ERR_HIP. */
+ * of 4096 pairs created here; launches beyond the pool are not timed, and
+ * the next lce_timing_read says so).  mask 0 disables the hook and releases
+ * the events.  Host only; HIP errors -> LCE_ERR_HIP. */
 LCE_API lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask);
 
 /* Wait for the recorded events, then write per-class totals since the last
  * read: ms[k] (milliseconds) and launches[k] for k < LCE_K_COUNT (either
- * pointer may be NULL), and restart the count. */
+ * pointer may be NULL), and restart the count.  If launches of a timed class
+ * found the pool full since the last read, the totals cover the timed ones
+ * only and the call returns LCE_ERR_UNSUPPORTED (lce_last_error gives the
+ * count). */
 LCE_API lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches);
 
 /* Static, human-readable name of a status code (an implementation entry; the

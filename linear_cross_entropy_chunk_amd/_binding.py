@@ -49,8 +49,9 @@ class LceError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = f"{where}: {lce_status_string(status)}"
-        if status == LCE_ERR_HIP:
-            msg += f" ({lce_last_error()})"
+        detail = lce_last_error()
+        if status == LCE_ERR_HIP or (detail and detail.startswith(where)):
+            msg += f" ({detail})"
         super().__init__(msg)
 
 

@@ -21,11 +21,12 @@
 
 // Events bracketing selected kernel classes (the benchmark timing hook).
 struct TimingPool {
-  static constexpr size_t kPairs = 2048;
+  static constexpr size_t kPairs = 4096;
   uint32_t mask = 0;
   std::vector<hipEvent_t> ev;   // 2 per slot
   std::vector<int> kind;        // kernel class per slot
   size_t used = 0;
+  int64_t dropped = 0;          // launches of a timed class that found the pool full
 };
 
 struct lce_handle {
@@ -49,7 +50,7 @@ struct lce_handle {
   bool w_inplace;     // grad_W reads dL where it lies in T (2-byte k-major operand)
   bool gx_group;      // one grad_X GEMM per grad_W group (its rows all in T)
   bool rowref;        // one reference per row: T holds dL / beta, no finalize pass
-  bool grp_stats;     // whole-tile chunks in groups: statistics buffers for a whole
+  bool grp_stats;     // chunks back to back in groups: statistics buffers for a whole
                       // group, so the combine (and the gated repair) can run per group
   int64_t ldp;        // row stride of the statistics partials and zt
   int64_t w_tail_cols;  // grad_W: trailing 256-class tile columns split along K (0: none)
@@ -89,7 +90,9 @@ lce_status hip_status(hipError_t e) {
 #define LCE_LAUNCH(h, k, call)                                                   \
   do {                                                                           \
     TimingPool& tp_ = (h)->timing;                                               \
-    const bool on_ = ((tp_.mask >> (k)) & 1u) && tp_.used < tp_.kind.size();    \
+    const bool want_ = (tp_.mask >> (k)) & 1u;                                   \
+    const bool on_ = want_ && tp_.used < tp_.kind.size();                        \
+    if (want_ && !on_) ++tp_.dropped;                                            \
     if (on_) LCE_HIP(hipEventRecord(tp_.ev[2 * tp_.used], s));                   \
     LCE_HIP(call);                                                               \
     if (on_) {                                                                   \
@@ -175,13 +178,14 @@ void plan(lce_handle* h) {
   // bf16 only: T's entries may exceed 1 (up to e^kRefGap), which fp16 cannot
   // hold.  Not with a staged dL^T, which the finalize pass forms.
   h->rowref = h->elem == lce::Elem::kBF16 && h->want_any && (!h->want_w || h->w_inplace);
-  // With chunks on 256-row tile boundaries in groups of several, the
-  // statistics buffers hold a whole group, so that the combine runs once per
-  // group instead of once per chunk (fewer launches, and its rows span the
-  // group): for the one-reference plan when the group's chunks all stay in T
-  // (with the gated repair and the grad_b sums), and for the loss-only
-  // forward of 'none'.
-  h->grp_stats = h->grp > 1 && h->c % lce::kTile == 0;
+  // With chunks of a multiple of 64 rows in groups of several, the chunks'
+  // rows lie back to back in the statistics buffers, which hold a whole
+  // group, so that the combine runs once per group instead of once per chunk
+  // (fewer launches, and its rows span the group): for the one-reference
+  // plan when the group's chunks all stay in T (with the gated repair, whose
+  // flags cover the group's 256-row tiles, and the grad_b sums), and for
+  // the loss-only forward of 'none'.
+  h->grp_stats = h->grp > 1 && h->c % 64 == 0;
 
   // grad_W's last round.  D/256 x V/256 tiles on 256 CUs leave a partial
   // last round (at the large-vocabulary head 80 tiles: 31.3 rounds), during
@@ -427,6 +431,7 @@ lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask) {
     tp.ev.clear();
     tp.kind.clear();
     tp.used = 0;
+    tp.dropped = 0;
     tp.mask = 0;
     return LCE_OK;
   }
@@ -436,6 +441,7 @@ lce_status lce_timing_enable(lce_handle* h, uint32_t kernel_mask) {
     tp.kind.assign(TimingPool::kPairs, 0);
   }
   tp.used = 0;
+  tp.dropped = 0;
   tp.mask = kernel_mask;
   return LCE_OK;
 }
@@ -456,6 +462,15 @@ lce_status lce_timing_read(lce_handle* h, double* ms, int64_t* launches) {
   for (int k = 0; k < LCE_K_COUNT; ++k) {
     if (ms) ms[k] = tot[k];
     if (launches) launches[k] = cnt[k];
+  }
+  if (tp.dropped > 0) {
+    // the totals cover the timed launches only: say so rather than let a
+    // partial count pass for a whole one
+    snprintf(g_last_error, sizeof(g_last_error),
+             "lce_timing_read: %lld launches found the pool of %zu event pairs full and "
+             "were not timed", static_cast<long long>(tp.dropped), TimingPool::kPairs);
+    tp.dropped = 0;
+    return LCE_ERR_UNSUPPORTED;
   }
   return LCE_OK;
 }
@@ -517,6 +532,11 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   // the combine per group (statistics of the whole group): the one-reference
   // plan with the group's chunks in T, or a call without gradients
   const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
+  // Chunks shorter than a 256-row tile would leave most rows of every logits
+  // tile empty.  With the combine per group, the group's chunks (back to back
+  // in T and in the statistics) then run as one logits launch at the group's
+  // first chunk, which writes the layout the chunks' launches would.
+  const bool merge = grp_comb && h->c < lce::kTile;
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
   // repair flags, one per 256-row tile of a chunk, so that a row whose
@@ -615,7 +635,14 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.rref = rowref ? rref + row0 : nullptr;
     la.t_rows = rowref ? rows_pad : rows;
     la.gate = nullptr;
-    LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
+    if (!merge) {
+      LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
+    } else if (jj == 0) {
+      const int64_t g_rows_all = std::min<int64_t>(h->grp * h->c, d.N - row0);
+      la.rows = static_cast<int>(g_rows_all);
+      la.t_rows = static_cast<int>(rowref ? round_up(g_rows_all, 64) : g_rows_all);
+      LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
+    }
 
     float* loss_rows = (none && io->loss) ? io->loss + row0 : lrows + row0;
     const float* wrow_c = io->class_weight ? wrow + row0 : nullptr;
