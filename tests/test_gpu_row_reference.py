@@ -211,3 +211,40 @@ def test_far_row_inside_a_long_chunk(group_rows):
     for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax"):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     check_all(a, _ref(case), "bf16", "mean", z=z)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+def test_far_rows_with_short_chunks_sharing_a_launch(chunk):
+    """Chunks shorter than a 256-row tile, several to a group: the group's
+    chunks share one logits launch and one combine, and the gated repair
+    recomputes the 256-row tiles of the far rows (which straddle chunk
+    boundaries).  N=1000 with groups of 512 rows (a ragged last group)."""
+    require_gpu()
+    N, D, V = 1000, 64, 1800
+    far = [100, 700, 990]
+    case = li.small_case(N, D, V, dtype="bf16", seed=90, ignore_frac=0.05)
+    X = case["X"].copy()
+    X[far] *= 32.0
+    case = {**case, "X": X}
+    case, z = _far_targets(case, far)
+    log(f"far rows, {chunk}-row chunks sharing a launch")
+    a, b = run_gpu(case, "bf16", chunk_rows=chunk, group_rows=512, repeat=2)
+    for k in ("loss", "grad_X", "grad_W", "grad_b", "argmax"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    check_all(a, _ref(case), "bf16", "mean", z=z)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_loss_only_forward_with_short_chunks_sharing_a_launch(dt):
+    """'none' without an upstream gradient in 64-row chunks, eight to a
+    group: one logits launch and one combine per group; the per-chunk plan
+    gives the same losses."""
+    require_gpu()
+    N, D, V = 1100, 64, 2500
+    case = li.small_case(N, D, V, dtype=dt, seed=91, ignore_frac=0.1)
+    grp = run_gpu(case, dt, reduction="none", chunk_rows=64, group_rows=512)
+    per = run_gpu(case, dt, reduction="none", chunk_rows=64, group_rows=64)
+    ref = _ref(case, "none")
+    check_all(grp, ref, dt, "none", z=oracle.logits(case["X"], case["W"], case["b"]), grads="")
+    np.testing.assert_allclose(grp["loss"], per["loss"], rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(grp["argmax"], per["argmax"])
