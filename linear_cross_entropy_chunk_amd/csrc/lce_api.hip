@@ -247,7 +247,11 @@ void plan(lce_handle* h) {
   h->o_gxp = take(static_cast<size_t>(h->splits) * round_up(h->gx_rows, 64) * D * 4,
                   h->want_x && !(h->gx_group && h->splits == 1));
   h->o_gw32 = take(V * D * 4, h->w_acc32);
-  h->o_gbp = take((c / 64) * Vp * 4, h->want_b && !h->rowref);   // the finalize's partials
+  // the finalize's grad_b partials, one row per 64 rows it covers: a whole
+  // group when short chunks share their logits launch (16-bit gradients,
+  // finalize per group)
+  const bool fin_group = h->grp_stats && h->c < lce::kTile && h->w_inplace;
+  h->o_gbp = take(((fin_group ? h->k_grp : c) / 64) * Vp * 4, h->want_b && !h->rowref);
   h->o_gb32 = take(Vp * 4, h->want_b);
   h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
   h->o_wrow = take(std::max<int64_t>(N, 1) * 4, true);
@@ -533,10 +537,11 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   // plan with the group's chunks in T, or a call without gradients
   const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
   // Chunks shorter than a 256-row tile would leave most rows of every logits
-  // tile empty.  With the combine per group, the group's chunks (back to back
-  // in T and in the statistics) then run as one logits launch at the group's
+  // tile empty.  When the group's chunks lie back to back in T and in
+  // group-sized statistics (the combine per group, or 16-bit gradients whose
+  // finalize runs per chunk), they run as one logits launch at the group's
   // first chunk, which writes the layout the chunks' launches would.
-  const bool merge = grp_comb && h->c < lce::kTile;
+  const bool merge = h->grp_stats && h->c < lce::kTile && (grp_comb || (grads && h->w_inplace));
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
   // repair flags, one per 256-row tile of a chunk, so that a row whose
@@ -625,8 +630,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.rows = rows; la.V = V; la.D = D;
     la.T = grads ? Tc : nullptr; la.tps = tps;
     // statistics of the chunk's rows: at column jj c_pad of the group's
-    // buffers when the combine runs per group, else at column 0
-    const int64_t sc = grp_comb ? jj * cp : 0;
+    // buffers when the combine runs per group or the launch is shared, else
+    // at column 0
+    const int64_t sc = (grp_comb || merge) ? jj * cp : 0;
     la.m_part = mp + sc; la.s_part = sp + sc;
     la.i_part = h->want_argmax ? ip + sc : nullptr; la.ldp = h->ldp;
     la.zt = zt + sc;
@@ -686,6 +692,29 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
                                     loss_g, h->want_argmax ? io->argmax + g_row0 : nullptr, s));
       }
       continue;
+    } else if (merge) {
+      // 16-bit gradients whose chunks shared a logits launch: the combine,
+      // the finalize and the grad_b partials once per group, over the
+      // group's rows back to back in T, after its last chunk
+      if (jj + 1 == h->grp || last) {
+        const int64_t g_row0 = (ck - jj) * h->c;
+        const int g_rows = static_cast<int>(row0 + rows - g_row0);
+        const int g_rows_pad = static_cast<int>(round_up(g_rows, 64));
+        float* loss_g = (none && io->loss) ? io->loss + g_row0 : lrows + g_row0;
+        LCE_LAUNCH(h, LCE_K_COMBINE,
+                   lce::row_combine(mp, sp, ip, h->ldp, h->n_vt, zt, tc + g_row0,
+                                    io->class_weight ? wrow + g_row0 : nullptr, g_rows, lse,
+                                    loss_g, h->want_argmax ? io->argmax + g_row0 : nullptr, s));
+        LCE_LAUNCH(h, LCE_K_FINALIZE,
+                   lce::finalize_dlogits(el, T, tps, nullptr, h->k_grp, mp, h->ldp, lse,
+                                         g + g_row0, tc + g_row0, g_rows, g_rows_pad, V,
+                                         static_cast<int>(Vp), want_b ? gbp : nullptr, dl_scale,
+                                         s));
+        if (want_b)
+          LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, g_rows_pad / 64, Vp, V, gb32,
+                                                          io->grad_b, ck - jj == 0, last,
+                                                          h->accum, s));
+      }
     } else {
       LCE_LAUNCH(h, LCE_K_COMBINE, lce::row_combine(mp, sp, ip, h->ldp, h->n_vt, zt, tc + row0,
                                                     wrow_c, rows, lse, loss_rows, amax_c, s));
@@ -808,7 +837,7 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     if (want_b && rowref && !grp_comb)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_cols(Tc, tps, beta + row0, rows, V, gb32, io->grad_b,
                                                first, last, h->accum, s));
-    else if (want_b && !rowref)
+    else if (want_b && !rowref && !merge)
       LCE_LAUNCH(h, LCE_K_BIAS, lce::bias_grad_reduce(el, gbp, rows_pad / 64, Vp, V, gb32, io->grad_b, first,
                                     last, h->accum, s));
   }
