@@ -101,6 +101,10 @@ lce_status hip_status(hipError_t e) {
     }                                                                            \
   } while (0)
 
+// Fewest rows a logits launch covers when consecutive chunks can share one
+// (eight 256-row tiles: each launch reads all of W once).
+constexpr int64_t kLaunchRows = 2048;
+
 // next power of two >= x (x >= 1)
 int64_t next_pow2(int64_t x) {
   int64_t p = 1;
@@ -250,7 +254,7 @@ void plan(lce_handle* h) {
   // the finalize's grad_b partials, one row per 64 rows it covers: a whole
   // group when short chunks share their logits launch (16-bit gradients,
   // finalize per group)
-  const bool fin_group = h->grp_stats && h->c < lce::kTile && h->w_inplace;
+  const bool fin_group = h->grp_stats && h->c < kLaunchRows && h->w_inplace;
   h->o_gbp = take(((fin_group ? h->k_grp : c) / 64) * Vp * 4, h->want_b && !h->rowref);
   h->o_gb32 = take(Vp * 4, h->want_b);
   h->o_lrows = take(std::max<int64_t>(N, 1) * 4, true);
@@ -536,12 +540,17 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
   // the combine per group (statistics of the whole group): the one-reference
   // plan with the group's chunks in T, or a call without gradients
   const bool grp_comb = h->grp_stats && (rowref ? h->w_inplace : !grads);
-  // Chunks shorter than a 256-row tile would leave most rows of every logits
-  // tile empty.  When the group's chunks lie back to back in T and in
-  // group-sized statistics (the combine per group, or 16-bit gradients whose
-  // finalize runs per chunk), they run as one logits launch at the group's
-  // first chunk, which writes the layout the chunks' launches would.
-  const bool merge = h->grp_stats && h->c < lce::kTile && (grp_comb || (grads && h->w_inplace));
+  // Short chunks make poor logits launches: below 256 rows most rows of
+  // every tile are empty, and each launch reads all of W again, so 256-row
+  // chunks read it eight times as often as 2048-row ones.  When a group's
+  // chunks lie back to back in T and in group-sized statistics (the combine
+  // per group, or 16-bit gradients), consecutive chunks share a logits launch
+  // of at least kLaunchRows rows (at most the group), which writes the layout
+  // the chunks' own launches would.  Chunks of kLaunchRows or more keep one
+  // launch each.
+  const bool share_ok = h->grp_stats && (grp_comb || (grads && h->w_inplace));
+  const int64_t unit = share_ok ? std::max<int64_t>(1, cdiv64(kLaunchRows, h->c)) : 1;
+  const bool merge = unit > 1;
   float* rref = at<float>(workspace, h->o_rref);
   float* beta = at<float>(workspace, h->o_beta);
   // repair flags, one per 256-row tile of a chunk, so that a row whose
@@ -643,10 +652,12 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
     la.gate = nullptr;
     if (!merge) {
       LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
-    } else if (jj == 0) {
-      const int64_t g_rows_all = std::min<int64_t>(h->grp * h->c, d.N - row0);
-      la.rows = static_cast<int>(g_rows_all);
-      la.t_rows = static_cast<int>(rowref ? round_up(g_rows_all, 64) : g_rows_all);
+    } else if (jj % unit == 0) {
+      // this chunk and the next unit - 1 of its group
+      const int64_t u_rows =
+          std::min<int64_t>(std::min(unit, h->grp - jj) * h->c, d.N - row0);
+      la.rows = static_cast<int>(u_rows);
+      la.t_rows = static_cast<int>(rowref ? round_up(u_rows, 64) : u_rows);
       LCE_LAUNCH(h, LCE_K_LOGITS, lce::logits_lse(el, la, s));
     }
 
