@@ -516,8 +516,8 @@ def main() -> int:
         print(json.dumps(out, indent=1))
         return 0
     if args.gpus != 1:
-        print(f"this build runs on one GPU only (--gpus {args.gpus} requested); the multi-GPU "
-              "sharding is a design note, not an implementation", file=sys.stderr)
+        print(f"the library runs on one GPU only (--gpus {args.gpus} requested); sharding over "
+              "several GPUs is designed but not implemented", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
