@@ -124,7 +124,9 @@ typedef enum { LCE_MEAN = 0, LCE_SUM = 1, LCE_NONE = 2 } lce_reduction;
  * groups in an fp32 V x D accumulator in the workspace (see the file comment
  * and lce_desc.group_rows for how many chunks form a group).  COMPACT adds
  * each chunk's fp32 product straight into the 16-bit grad_W (one rounding
- * per chunk) and needs no V x D accumulator.  Identical for fp32 input. */
+ * per chunk, at the size of what grad_W then holds, including values that
+ * LCE_ACCUMULATE adds to) and needs no V x D accumulator.  Identical for
+ * fp32 input. */
 typedef enum { LCE_ACCURATE = 0, LCE_COMPACT = 1 } lce_acc_policy;
 
 /* Output flags (the pages' compute_input_grad / compute_linear_weight_grad /
