@@ -764,8 +764,9 @@ lce_status lce_forward_backward(lce_handle* h, const lce_io* io, void* workspace
           lg.zt = zt;
           lg.rref = rref + g_row0;
           lg.t_rows = static_cast<int>(round_up(g_rows, 64));
-          // (the chunks are whole 256-row tiles here, so the group's flags
-          // follow one another as its rows do)
+          // (flags by 256-row tile of the group, from its first chunk's
+          // first flag: cdiv(g_rows, 256) of them, within the grp * fpc
+          // flags its chunks own, since every chunk owns at least one)
           const lce_status st = combine_ref(lg, g_row0, g_rows, T, flags + (ck - jj) * fpc,
                                             lce::kTile);
           if (st != LCE_OK) return st;
