@@ -304,15 +304,18 @@ LCE_API lce_status lce_destroy(lce_handle* h);
 LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
 
 /* Standalone softmax cross-entropy on precomputed fp32 logits [N, V]
- * (row-major, row stride V, 16-byte aligned, V % 4 == 0), enqueued on
+ * (row-major, row stride V, 4-byte aligned, any V >= 1), enqueued on
  * `stream` (Liger-Kernel issue #343: the loss, with the gradient written over
  * the logits).  Writes the loss (MEAN / SUM: loss[1]; NONE: loss[N]) and
  * overwrites `logits` in place with the gradient g_n (softmax - onehot), g_n
  * as for lce_forward_backward with grad_output = grad_scale on every counted
  * row for NONE.  class_weight ([V] fp32 or NULL) weighs rows as in lce_io.
  * n_valid may be NULL.  Errors: INVALID_ARG (N < 0, V < 1, NULL pointers),
- * UNSUPPORTED (a reduction outside lce_reduction, V % 4 != 0, misaligned
- * logits, N or V above 2^31 - 1), WORKSPACE, HIP. */
+ * UNSUPPORTED (a reduction outside lce_reduction, logits not 4-byte
+ * aligned, N or V above 2^31 - 1), WORKSPACE, HIP.  Rows of 65536 to
+ * 131072 classes with V % 4 == 0 and 16-byte aligned logits are read from
+ * memory once; other rows are read twice (the second read mostly from
+ * cache for rows up to a few hundred KiB). */
 LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets,
                           const float* class_weight, int64_t N,
                           int64_t V, int64_t ignore_index, int32_t reduction,

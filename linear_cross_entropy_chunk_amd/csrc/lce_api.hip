@@ -294,7 +294,7 @@ lce_status ce_check(const float* logits, const int64_t* targets, int64_t N, int6
   if (reduction < LCE_MEAN || reduction > LCE_NONE) return LCE_ERR_UNSUPPORTED;
   if (N > 0 && (!logits || !targets)) return LCE_ERR_INVALID_ARG;
   if (!loss) return LCE_ERR_INVALID_ARG;
-  if (V % 4 != 0 || (logits && !aligned16(logits))) return LCE_ERR_UNSUPPORTED;
+  if (logits && (reinterpret_cast<uintptr_t>(logits) & 3) != 0) return LCE_ERR_UNSUPPORTED;
   if (N > 2147483647LL || V > 2147483647LL) return LCE_ERR_UNSUPPORTED;
   return LCE_OK;
 }

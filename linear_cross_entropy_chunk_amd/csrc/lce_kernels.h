@@ -214,6 +214,7 @@ hipError_t scale(Elem e, const void* in, void* out, int64_t n, int64_t cols,
 
 // Standalone CE: rows of fp32 logits overwritten with g_n (softmax - onehot);
 // loss_rows[n] = w[n] (lse - z_t) (0 if tc < 0; w = wrow[n], 1 when null).
+// z 4-byte aligned, any V >= 1.
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
                            const float* wrow, float* loss_rows, hipStream_t s);
 

@@ -650,7 +650,9 @@ __global__ __launch_bounds__(256) void k_scale(const T* in, T* out, int64_t n, i
 // g_n (softmax - onehot).  The target logit is read before any overwrite.
 // Each thread keeps kCeUnroll independent 16-byte loads in flight, so a
 // workgroup has 1024 x 8 x 16 bytes outstanding: enough to cover the memory
-// latency at the per-CU share of HBM bandwidth.
+// latency at the per-CU share of HBM bandwidth.  Rows of any length and any
+// 4-byte alignment: the elements before the row's first 16-byte boundary (h
+// < 4) and after its last whole vector (r < 4) go one per thread.
 constexpr int kCeThreads = 1024;
 constexpr int kCeUnroll = 8;
 __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, int V,
@@ -661,11 +663,22 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
   __shared__ float wm[kCeThreads / 64], wsum[kCeThreads / 64];
   __shared__ float bcast[2];
   const int n = blockIdx.x;
-  f32x4_t* row = reinterpret_cast<f32x4_t*>(z + static_cast<int64_t>(n) * V);
-  const int V4 = V >> 2;
+  const int tid = threadIdx.x;
+  float* rowp = z + static_cast<int64_t>(n) * V;
+  const int h = min(static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(rowp) >> 2) & 3)) & 3), V);
+  const int V4 = (V - h) >> 2;
+  const int r = (V - h) & 3;
+  f32x4_t* row = reinterpret_cast<f32x4_t*>(rowp + h);
   const int t = tc[n];
-  float m = -INFINITY, s = 0.0f;
-  for (int base = threadIdx.x; base < V4; base += kCeThreads * kCeUnroll) {
+  // this thread's single element outside the vectors, if any
+  const int xi = tid < h ? tid : (tid < h + r ? h + 4 * V4 + (tid - h) : -1);
+  const float xs = xi >= 0 ? rowp[xi] : -INFINITY;
+  // The exponentials take the running max as reference, or 0 while it is
+  // -inf (every element so far -inf or NaN): -inf elements then add 0 and
+  // NaN ones NaN, as they would against the row's own max.
+  float m = fmaxf(-INFINITY, xs);
+  float s = xi >= 0 ? fast_exp(xs - (m == -INFINITY ? 0.0f : m)) : 0.0f;
+  for (int base = tid; base < V4; base += kCeThreads * kCeUnroll) {
     f32x4_t x[kCeUnroll];
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u) {
@@ -677,44 +690,46 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
     for (int u = 0; u < kCeUnroll; ++u)
       mx = fmaxf(mx, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
     if (mx > m) {
-      s *= fast_exp(m - mx);
+      s *= fast_exp(m - mx);                // 0 (or NaN stays NaN) when m was -inf
       m = mx;
     }
+    const float ref = m == -INFINITY ? 0.0f : m;
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u)
-      if (base + u * kCeThreads < V4)   // padding adds nothing (its exp would be NaN while m is -inf)
-        s += fast_exp(x[u][0] - m) + fast_exp(x[u][1] - m) + fast_exp(x[u][2] - m) +
-             fast_exp(x[u][3] - m);
+      if (base + u * kCeThreads < V4)       // padding adds nothing
+        s += fast_exp(x[u][0] - ref) + fast_exp(x[u][1] - ref) + fast_exp(x[u][2] - ref) +
+             fast_exp(x[u][3] - ref);
   }
-  // A thread whose max is -inf holds sum 0 (no elements) or NaN (every
-  // element NaN, which the NaN-skipping max leaves at -inf): that sum is
-  // added as it is, so that a NaN reaches the row's result.
+  // A thread whose max is -inf holds sum 0 (no elements, or only -inf ones)
+  // or NaN (a NaN element, which the NaN-skipping max leaves at -inf): that
+  // sum is added as it is, so that a NaN reaches the row's result.
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(m, o), os = __shfl_xor(s, o);
     const float M = fmaxf(m, om);
     s = (m > -INFINITY ? s * fast_exp(m - M) : s) + (om > -INFINITY ? os * fast_exp(om - M) : os);
     m = M;
   }
-  if ((threadIdx.x & 63) == 0) {
-    wm[threadIdx.x >> 6] = m;
-    wsum[threadIdx.x >> 6] = s;
+  if ((tid & 63) == 0) {
+    wm[tid >> 6] = m;
+    wsum[tid >> 6] = s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     float M = wm[0];
     for (int w = 1; w < kCeThreads / 64; ++w) M = fmaxf(M, wm[w]);
     float S = 0.0f;
     for (int w = 0; w < kCeThreads / 64; ++w)
       S += wm[w] > -INFINITY ? wsum[w] * expf(wm[w] - M) : wsum[w];
     const float L = M + logf(S);
-    const float zt = t >= 0 ? z[static_cast<int64_t>(n) * V + t] : 0.0f;
+    const float zt = t >= 0 ? rowp[t] : 0.0f;
     loss_rows[n] = t >= 0 ? (wrow ? wrow[n] : 1.0f) * (L - zt) : 0.0f;
     bcast[0] = L;
   }
   __syncthreads();
   const float L = bcast[0];
   const float gn = g[n];
-  for (int base = threadIdx.x; base < V4; base += kCeThreads * kCeUnroll) {
+  if (xi >= 0) rowp[xi] = gn * fast_exp(xs - L) - (xi == t ? gn : 0.0f);
+  for (int base = tid; base < V4; base += kCeThreads * kCeUnroll) {
     f32x4_t x[kCeUnroll];
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u) {
@@ -729,7 +744,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         y[e] = gn * fast_exp(x[u][e] - L);
-        if (4 * i + e == t) y[e] -= gn;
+        if (h + 4 * i + e == t) y[e] -= gn;
       }
       __builtin_nontemporal_store(y, row + i);
     }
@@ -1017,9 +1032,13 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
                            const float* wrow, float* loss_rows, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  // Rows of 64K..128K classes stay on chip (one HBM read); others stream twice.
+  // Rows of 64K..128K classes stay on chip (one HBM read) when every row
+  // starts on a 16-byte boundary; others stream twice.
   const int V4 = V / 4;
-  auto fits = [&](int reg) { return V4 <= kOnThreads * reg + kCeTailVec; };
+  auto fits = [&](int reg) {
+    return V % 4 == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0 &&
+           V4 <= kOnThreads * reg + kCeTailVec;
+  };
   if (V4 >= 16384 && fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else if (V4 >= 16384 && fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else if (V4 >= 16384 && fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);

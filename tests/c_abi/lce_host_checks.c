@@ -173,8 +173,9 @@ int main(void) {
   EXPECT(lce_ce_workspace_size(0, 1, &ws) == LCE_OK && ws > 0);
   EXPECT(lce_ce_workspace_size(-1, 1, &ws) == LCE_ERR_INVALID_ARG);
   EXPECT(lce_ce_workspace_size(1, 1, NULL) == LCE_ERR_INVALID_ARG);
-  EXPECT(lce_ce_inplace((float*)fake, (const int64_t*)fake, NULL, 16, 1022, -100, LCE_MEAN, 1.0f,
-                        (float*)fake, NULL, fake, 1 << 20, NULL) == LCE_ERR_UNSUPPORTED);
+  EXPECT(lce_ce_inplace((float*)((char*)fake + 2), (const int64_t*)fake, NULL, 16, 1022, -100,
+                        LCE_MEAN, 1.0f, (float*)fake, NULL, fake, 1 << 20, NULL) ==
+         LCE_ERR_UNSUPPORTED);                        /* logits not 4-byte aligned */
   EXPECT(lce_ce_inplace((float*)fake, (const int64_t*)fake, NULL, 16, 1024, -100, 3, 1.0f,
                         (float*)fake, NULL, fake, 1 << 20, NULL) == LCE_ERR_UNSUPPORTED);
   EXPECT(lce_ce_inplace((float*)fake, (const int64_t*)fake, NULL, 16, 1024, -100, LCE_MEAN, 1.0f,

@@ -161,8 +161,12 @@ def check_all(gpu: dict, ref: dict, dt: str, reduction: str, z=None, grads="xwb"
 
 
 def run_ce(z: np.ndarray, t: np.ndarray, *, reduction: str = "mean", ignore_index: int = -100,
-           grad_scale: float = 1.0, class_weight=None):
-    zd = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to("cuda")
+           grad_scale: float = 1.0, class_weight=None, offset: int = 0):
+    """The standalone CE on a copy of z; with `offset` the logits start that
+    many floats into a fresh allocation (4-byte, not 16-byte, alignment)."""
+    flat = torch.empty(z.size + offset, dtype=torch.float32, device="cuda")
+    zd = flat[offset:].view(z.shape)
+    zd.copy_(torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)))
     td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).to("cuda")
     op = CrossEntropyInplace(z.shape[0], z.shape[1], reduction=reduction,
                              ignore_index=ignore_index)

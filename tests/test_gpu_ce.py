@@ -69,3 +69,89 @@ def test_ce_long_rows_on_chip(V, reduction):
         assert abs(loss[0] - ref_loss) <= 1e-5 * abs(ref_loss)
     assert rel_err(dl, ref_dl) <= 1e-4
     assert np.all(dl[4] == 0.0)
+
+
+def _check_ce(z, t, reduction, offset=0, grad_scale=1.0):
+    loss, nv, dl = run_ce(z, t, reduction=reduction, offset=offset, grad_scale=grad_scale)
+    ref_loss, ref_dl = oracle.softmax_cross_entropy(z, t, reduction=reduction,
+                                                    grad_scale=grad_scale)
+    ign = t == -100
+    assert nv == int((~ign).sum())
+    if reduction == "none":
+        assert rel_err(loss, ref_loss) <= 1e-5
+        assert np.all(loss[ign] == 0.0)
+    else:
+        assert abs(loss[0] - ref_loss) <= 1e-5 * abs(ref_loss)
+    assert rel_err(dl, ref_dl) <= 1e-4
+    assert np.all(dl[ign] == 0.0)
+    return dl
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 7, 1021, 4097, 50257])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_ce_any_row_length(V, reduction):
+    """V not a multiple of 4: row n starts n V mod 4 floats past a 16-byte
+    boundary, so consecutive rows take every alignment, with their first and
+    last elements outside the 16-byte vectors.  Targets on those elements
+    (the first and last classes) and ignored rows included."""
+    require_gpu()
+    rng = np.random.default_rng(1000 + V)
+    N = 13
+    z = (rng.standard_normal((N, V)) * 3.0).astype(np.float32)
+    t = rng.integers(0, V, N)
+    t[[1, 2]] = [0, V - 1]
+    t[5] = -100
+    log(f"ce any length V={V} reduction={reduction}")
+    _check_ce(z, t, reduction, grad_scale=1.25)
+
+
+@pytest.mark.parametrize("V", [65537, 131071, 131073])
+def test_ce_long_rows_not_a_multiple_of_4(V):
+    """Long rows that do not start on 16-byte boundaries stream twice instead
+    of staying on chip."""
+    require_gpu()
+    rng = np.random.default_rng(V)
+    N = 6
+    z = (rng.standard_normal((N, V)) * 2.0).astype(np.float32)
+    t = rng.integers(0, V, N)
+    t[[0, 1]] = [V - 1, 0]
+    t[3] = -100
+    log(f"ce long unaligned rows V={V}")
+    _check_ce(z, t, "none")
+
+
+@pytest.mark.parametrize("V", [4096, 131072])
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_ce_logits_off_a_16_byte_boundary(V, offset):
+    """Logits that start 4, 8 or 12 bytes past a 16-byte boundary (a view into
+    a larger buffer): accepted, every row takes the element-wise head and
+    tail; the rows of 131072 classes then stream instead of staying on chip."""
+    require_gpu()
+    rng = np.random.default_rng(V + offset)
+    N = 5
+    z = (rng.standard_normal((N, V)) * 2.0).astype(np.float32)
+    t = rng.integers(0, V, N)
+    t[0] = V - 1
+    t[2] = -100
+    log(f"ce offset {offset} V={V}")
+    _check_ce(z, t, "mean", offset=offset)
+
+
+@pytest.mark.parametrize("V", [4096, 4097, 50257, 100000])
+def test_ce_masked_logits(V):
+    """Classes masked to -inf: the upper half of every row (whole threads'
+    shares of the streaming kernel see only -inf), and all but three classes
+    of one row.  The loss stays finite and the masked gradient is exactly 0,
+    as in the oracle (pinned to torch)."""
+    require_gpu()
+    rng = np.random.default_rng(2000 + V)
+    N = 7
+    z = (rng.standard_normal((N, V)) * 2.0).astype(np.float32)
+    z[:, V // 2:] = -np.inf
+    z[3, 3:] = -np.inf
+    t = rng.integers(0, V // 2, N)
+    t[3] = 1
+    t[5] = -100
+    log(f"ce masked V={V}")
+    dl = _check_ce(z, t, "none")
+    assert np.all(dl[:, V // 2:] == 0.0) and np.all(dl[3, 3:] == 0.0)

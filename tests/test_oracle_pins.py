@@ -499,3 +499,25 @@ def test_standalone_ce_nan_row_as_in_torch(reduction):
         np.testing.assert_array_equal(np.isnan(got), np.isnan(want), err_msg=name)
         ok = ~np.isnan(want)
         np.testing.assert_allclose(got[ok], want[ok], rtol=1e-12, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_standalone_ce_masked_logits_as_in_torch(reduction):
+    """Logits masked to -inf (a class range of every row, and all but two
+    classes of one row; no target among them): the loss stays finite and
+    the masked classes' gradient is exactly 0, as in torch's float64
+    cross_entropy with autograd."""
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((6, 16))
+    z[:, 4:12] = -np.inf
+    z[2, 13:] = -np.inf
+    t = np.array([0, 1, 12, 13, 14, 15])
+    loss, dl = oracle.softmax_cross_entropy(z, t, reduction=reduction)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(t), reduction=reduction)
+    (lt.sum() if reduction == "none" else lt).backward()
+    assert np.all(np.isfinite(loss)) and np.all(np.isfinite(dl))
+    assert np.all(dl[:, 4:12] == 0.0) and np.all(dl[2, 13:] == 0.0)
+    np.testing.assert_allclose(np.atleast_1d(loss), np.atleast_1d(lt.detach().numpy()),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dl, zt.grad.numpy(), rtol=1e-12, atol=1e-12)

@@ -82,8 +82,8 @@ def test_noalloc_ce_refuses_more_rows_than_its_scratch():
                                          B.LCE_MEAN, fake)
     assert st == B.LCE_ERR_UNSUPPORTED
     assert "exceeds the static scratch" in B.lce_last_error()
-    assert B.lce_ce_inplace_noalloc_status(fake, fake, 16, 1022, B.LCE_MEAN, fake) == \
-        B.LCE_ERR_UNSUPPORTED                                  # V % 4 != 0
+    assert B.lce_ce_inplace_noalloc_status(fake + 2, fake, 16, 1024, B.LCE_MEAN, fake) == \
+        B.LCE_ERR_UNSUPPORTED                                  # logits not 4-byte aligned
     assert B.lce_ce_inplace_noalloc_status(fake, fake, 16, 1024, 7, fake) == \
         B.LCE_ERR_UNSUPPORTED                                  # unknown reduction
     assert B.lce_ce_inplace_noalloc_status(fake, fake, 16, 1024, B.LCE_MEAN, 0) == \
