@@ -1,4 +1,4 @@
-"""NaN inputs propagate as in the plain definition (IEEE arithmetic, no
+"""NaN and -inf inputs behave as in the plain definition (IEEE arithmetic, no
 masking beyond what the definition states).
 
 - A NaN in one row n of X makes every logit of that row NaN: its loss is NaN
@@ -8,6 +8,8 @@ masking beyond what the definition states).
 - A NaN in one row of W makes one logit of every row NaN, so every counted
   loss and every gradient element is NaN.
 - The standalone CE: a NaN logit makes its row's loss and gradient row NaN.
+- -inf logits (classes masked by a -inf bias) are softmax entries of exactly
+  0: the losses stay finite and those classes' gradients are exactly 0.
 
 The GPU's NaN positions must equal the oracle's, and its finite values meet
 the usual tolerances.  The argmax of a row whose logits are all NaN is class
@@ -172,3 +174,36 @@ def test_ce_row_nan_but_its_target(v):
     ok = ~np.isnan(ref_loss)
     check_loss(loss[ok], ref_loss[ok], "f32", "none")
     check_grad(grad[ok], ref_grad[ok], "f32", "gradient")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("reduction,grads", [("mean", "xwb"), ("none", "xwb"), ("none", "")])
+def test_classes_masked_by_a_minus_inf_bias(dt, reduction, grads):
+    """Classes masked with a -inf bias, no target among them: a whole
+    128-class statistics block (256..383), a range inside another (700..719)
+    and the last 30 classes of the ragged last tile.  Their logits are -inf,
+    which the definition turns into softmax entries of exactly 0: every loss
+    stays finite, the masked classes' grad_W rows and grad_b entries are
+    exactly 0, and the rest meets the oracle's tolerances.  Gradients by
+    mean and by 'none' with an upstream gradient, and the loss-only forward."""
+    require_gpu()
+    case = li.small_case(N, D, V, dtype=dt, seed=106, ignore_frac=0.05)
+    masked = np.zeros(V, bool)
+    masked[256:384] = masked[700:720] = masked[V - 30:] = True
+    b = case["b"].copy()
+    b[masked] = -np.inf
+    t = case["t"].copy()
+    t[(t >= 0) & masked[np.clip(t, 0, V - 1)]] = 1
+    up = case["u"] if reduction == "none" and grads else None
+    log(f"-inf bias dt={dt} {reduction} grads={grads!r}")
+    gpu = run_gpu({**case, "b": b, "t": t}, dt, reduction=reduction, chunk_rows=128,
+                  upstream=up, grads=grads)
+    ref = oracle.linear_cross_entropy(case["X"], case["W"], b, t, reduction=reduction,
+                                      upstream=up)
+    assert np.all(np.isfinite(ref["loss"])) and np.all(np.isfinite(gpu["loss"]))
+    check_loss(gpu["loss"], ref["loss"], dt, reduction)
+    if grads:
+        for key in ("grad_X", "grad_W", "grad_b"):
+            check_grad(gpu[key], ref[key], dt, key)
+        assert np.all(gpu["grad_W"][masked] == 0.0) and np.all(gpu["grad_b"][masked] == 0.0)
+    assert not np.any(masked[gpu["argmax"]])
