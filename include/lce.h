@@ -58,14 +58,16 @@
  *     anything is enqueued.
  *   - The caller owns every device buffer, including the workspace; the
  *     library owns only the host-side handle.  Inputs are never modified,
- *     except the logits buffer of lce_ce_inplace, which by contract is
- *     overwritten with the gradient.
+ *     except the logits buffer of lce_ce_inplace and
+ *     lce_ce_inplace_noalloc, which by contract is overwritten with the
+ *     gradient.
  *   - All matrices are dense row-major with the row length as stride.
  *   - bf16 tensors are raw bfloat16 bit patterns, fp16 tensors IEEE binary16
  *     (both uint16_t in memory).
  *   - Rows of X and W must be 16-byte aligned: D % 8 == 0 for bf16 / fp16,
  *     D % 4 == 0 for fp32 (LCE_ERR_UNSUPPORTED otherwise); base pointers
- *     16-byte aligned.
+ *     16-byte aligned.  The standalone CE takes any V and logits aligned
+ *     to 4 bytes.
  *   - Size limits of lce_create (LCE_ERR_UNSUPPORTED otherwise): N, V and D
  *     below 2^31 - 1024; D <= 2^20 and rows per chunk <= 2^20; fp32 inputs
  *     that request grad_X also need V <= 2^21 - 256.  (The GEMMs address a
@@ -262,7 +264,10 @@ LCE_API lce_status lce_chunk_info(const lce_handle* h, int64_t* chunk_rows,
  * row that is not counted), NaN in every element of grad_W and grad_b.  The
  * argmax of a row whose logits are all NaN is 0; with some NaN logits it is
  * a valid class, otherwise unspecified.  lce_ce_inplace likewise: a row
- * holding a NaN logit gets a NaN loss and a NaN gradient row.
+ * holding a NaN logit gets a NaN loss and a NaN gradient row.  A -inf logit
+ * (a class masked with a -inf bias here, or a -inf logit given to
+ * lce_ce_inplace) is a softmax entry of exactly 0: the loss stays finite
+ * unless the target's own logit is -inf, and its gradient entries are 0.
  *
  * `workspace` is a device buffer of at least lce_workspace_size bytes,
  * 256-byte aligned; its contents on entry are irrelevant and on return are
