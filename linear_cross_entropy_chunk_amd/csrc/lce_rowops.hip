@@ -755,7 +755,9 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
 // 16-byte vectors per thread in registers plus a tail of up to kCeTailVec
 // vectors in LDS (copied there straight from memory), so the row is read from
 // HBM once and written once.  Max, then exp(x - max) in place with its sum,
-// then the gradient g (e / sum - onehot): one exponential per element.
+// then the gradient g (e / sum - onehot): one exponential per element.  As in
+// k_ce_rows, the elements before the row's first 16-byte boundary and after
+// its last whole vector (fewer than 4 each) go one per thread.
 constexpr int kCeTailVec = 8192;                       // 128 KiB of LDS
 constexpr int kOnThreads = 512;                        // 2 waves per SIMD: 256 registers each
 template <int kRegVec>
@@ -771,11 +773,16 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  f32x4_t* row = reinterpret_cast<f32x4_t*>(z + static_cast<int64_t>(n) * V);
-  const int V4 = V >> 2;
+  float* rowp = z + static_cast<int64_t>(n) * V;
+  const int h = min(static_cast<int>((4 - ((reinterpret_cast<uintptr_t>(rowp) >> 2) & 3)) & 3), V);
+  f32x4_t* row = reinterpret_cast<f32x4_t*>(rowp + h);
+  const int V4 = (V - h) >> 2;
+  const int r = (V - h) & 3;
   const int nreg = min(V4, kOnThreads * kRegVec);       // vectors held in registers
   const int ntail = V4 - nreg;                          // vectors held in LDS
   const int t = tc[n];
+  // this thread's single element outside the vectors, if any
+  const int xi = tid < h ? tid : (tid < h + r ? h + 4 * V4 + (tid - h) : -1);
 
   // The tail, 1 KiB blocks of 64 vectors, one copy instruction each; lanes
   // past the row end read as zero (and are never used).
@@ -792,7 +799,8 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
     x[u] = i < nreg ? v : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
   float zt = 0.0f;
-  if (tid == 0 && t >= 0) zt = z[static_cast<int64_t>(n) * V + t];
+  if (tid == 0 && t >= 0) zt = rowp[t];
+  float xs = xi >= 0 ? rowp[xi] : -INFINITY;
   __builtin_amdgcn_s_waitcnt(dev::waitcnt_vm(0));
   __syncthreads();
 
@@ -821,7 +829,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
     return bcast[1];
   };
 
-  float m = -INFINITY;
+  float m = xs;
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u)
     m = fmaxf(m, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
@@ -831,7 +839,8 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   }
   const float M = block_max(m);
 
-  float s = 0.0f;
+  xs = xi >= 0 ? fast_exp(xs - M) : 0.0f;
+  float s = xs;
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u)
 #pragma unroll
@@ -854,19 +863,21 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
 
   const float gn = g[n];
   const float scale = gn / S;
+  if (xi >= 0) rowp[xi] = xs * scale - (xi == t ? gn : 0.0f);
+  const int tb = t - h;                                 // the target's index in the vectors
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u) {
     const int i = tid + u * kOnThreads;
     if (i >= nreg) continue;
     f32x4_t y = x[u] * scale;
-    if (t >= 4 * i && t < 4 * i + 4) y[t - 4 * i] -= gn;
+    if (tb >= 4 * i && tb < 4 * i + 4) y[tb - 4 * i] -= gn;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, y), rs, tid * 16,
                                            u * kOnThreads * 16, 0);
   }
   for (int j = tid; j < ntail; j += kOnThreads) {
     const int i = nreg + j;
     f32x4_t y = tail[j] * scale;
-    if (t >= 4 * i && t < 4 * i + 4) y[t - 4 * i] -= gn;
+    if (tb >= 4 * i && tb < 4 * i + 4) y[tb - 4 * i] -= gn;
     __builtin_nontemporal_store(y, row + i);
   }
 }
@@ -1032,16 +1043,15 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
                            const float* wrow, float* loss_rows, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  // Rows of 64K..128K classes stay on chip (one HBM read) when every row
-  // starts on a 16-byte boundary; others stream twice.
+  // Rows of 24K..128K classes stay on chip (one HBM read); shorter rows
+  // stream twice (their second read mostly from cache: measured as fast at
+  // 16K classes and 13-16% slower from 24K to 50K), and so do longer ones.
+  // A row's vectors number at most V / 4 whatever its alignment.
   const int V4 = V / 4;
-  auto fits = [&](int reg) {
-    return V % 4 == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0 &&
-           V4 <= kOnThreads * reg + kCeTailVec;
-  };
-  if (V4 >= 16384 && fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
-  else if (V4 >= 16384 && fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
-  else if (V4 >= 16384 && fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  auto fits = [&](int reg) { return V4 >= 6144 && V4 <= kOnThreads * reg + kCeTailVec; };
+  if (fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   return hipGetLastError();
 }

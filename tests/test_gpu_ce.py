@@ -105,10 +105,11 @@ def test_ce_any_row_length(V, reduction):
     _check_ce(z, t, reduction, grad_scale=1.25)
 
 
-@pytest.mark.parametrize("V", [65537, 131071, 131073])
+@pytest.mark.parametrize("V", [32004, 65537, 131071, 131073, 140001])
 def test_ce_long_rows_not_a_multiple_of_4(V):
-    """Long rows that do not start on 16-byte boundaries stream twice instead
-    of staying on chip."""
+    """Rows that stay on chip (24K to 128K classes: registers, then the LDS
+    tail) with consecutive rows at every alignment, and a row too long for
+    the chip (140001 classes), which streams twice."""
     require_gpu()
     rng = np.random.default_rng(V)
     N = 6
@@ -124,8 +125,8 @@ def test_ce_long_rows_not_a_multiple_of_4(V):
 @pytest.mark.parametrize("offset", [1, 2, 3])
 def test_ce_logits_off_a_16_byte_boundary(V, offset):
     """Logits that start 4, 8 or 12 bytes past a 16-byte boundary (a view into
-    a larger buffer): accepted, every row takes the element-wise head and
-    tail; the rows of 131072 classes then stream instead of staying on chip."""
+    a larger buffer): accepted, and every row takes the element-wise head and
+    tail, in the streaming kernel (4096 classes) and on chip (131072)."""
     require_gpu()
     rng = np.random.default_rng(V + offset)
     N = 5
@@ -140,9 +141,10 @@ def test_ce_logits_off_a_16_byte_boundary(V, offset):
 @pytest.mark.parametrize("V", [4096, 4097, 50257, 100000])
 def test_ce_masked_logits(V):
     """Classes masked to -inf: the upper half of every row (whole threads'
-    shares of the streaming kernel see only -inf), and all but three classes
-    of one row.  The loss stays finite and the masked gradient is exactly 0,
-    as in the oracle (pinned to torch)."""
+    shares of the streaming kernel, 4096 and 4097 classes, see only -inf;
+    50257 and 100000 stay on chip), and all but three classes of one row.
+    The loss stays finite and the masked gradient is exactly 0, as in the
+    oracle (pinned to torch)."""
     require_gpu()
     rng = np.random.default_rng(2000 + V)
     N = 7
