@@ -752,22 +752,22 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
 }
 
 // Single-read variant for long rows: the whole row stays on chip, kRegVec
-// 16-byte vectors per thread in registers plus a tail of up to kCeTailVec
+// 16-byte vectors per thread in registers plus a tail of up to kTailVec
 // vectors in LDS (copied there straight from memory), so the row is read from
 // HBM once and written once.  Max, then exp(x - max) in place with its sum,
 // then the gradient g (e / sum - onehot): one exponential per element.  As in
 // k_ce_rows, the elements before the row's first 16-byte boundary and after
 // its last whole vector (fewer than 4 each) go one per thread.
-constexpr int kCeTailVec = 8192;                       // 128 KiB of LDS
-constexpr int kOnThreads = 512;                        // 2 waves per SIMD: 256 registers each
-template <int kRegVec>
-__global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict__ z, int V,
+// kThr threads of kRegVec vectors each: 512 threads (two waves per SIMD, 256
+// registers each) or 1024 (four per SIMD, 128 each); kTailVec vectors of LDS.
+template <int kThr, int kRegVec, int kTailVec>
+__global__ __launch_bounds__(kThr) void k_ce_rows_onchip(float* __restrict__ z, int V,
                                                               const int* __restrict__ tc,
                                                               const float* __restrict__ g,
                                                               const float* __restrict__ wrow,
                                                               float* __restrict__ loss_rows) {
-  __shared__ __attribute__((aligned(16))) f32x4_t tail[kCeTailVec];
-  __shared__ float wred[kOnThreads / 64];
+  __shared__ __attribute__((aligned(16))) f32x4_t tail[kTailVec];
+  __shared__ float wred[kThr / 64];
   __shared__ float bcast[2];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   f32x4_t* row = reinterpret_cast<f32x4_t*>(rowp + h);
   const int V4 = (V - h) >> 2;
   const int r = (V - h) & 3;
-  const int nreg = min(V4, kOnThreads * kRegVec);       // vectors held in registers
+  const int nreg = min(V4, kThr * kRegVec);       // vectors held in registers
   const int ntail = V4 - nreg;                          // vectors held in LDS
   const int t = tc[n];
   // this thread's single element outside the vectors, if any
@@ -787,15 +787,15 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   // The tail, 1 KiB blocks of 64 vectors, one copy instruction each; lanes
   // past the row end read as zero (and are never used).
   const __amdgpu_buffer_rsrc_t rs = dev::make_rsrc(row, static_cast<int64_t>(V4) * 16);
-  for (int b = wave; b * 64 < ntail; b += kOnThreads / 64)
+  for (int b = wave; b * 64 < ntail; b += kThr / 64)
     dev::copy16_to_lds(rs, (nreg + b * 64 + lane) * 16, dev::lds_addr(tail + b * 64));
   // Register part: one lane offset, the vector stride in the scalar offset.
   f32x4_t x[kRegVec];
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u) {
-    const int i = tid + u * kOnThreads;
+    const int i = tid + u * kThr;
     const f32x4_t v = __builtin_bit_cast(
-        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, u * kOnThreads * 16, 0));
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, u * kThr * 16, 0));
     x[u] = i < nreg ? v : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
   float zt = 0.0f;
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
     __syncthreads();
     if (tid == 0) {
       float r = wred[0];
-      for (int w = 1; w < kOnThreads / 64; ++w) r = fmaxf(r, wred[w]);
+      for (int w = 1; w < kThr / 64; ++w) r = fmaxf(r, wred[w]);
       bcast[0] = r;
     }
     __syncthreads();
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
     __syncthreads();
     if (tid == 0) {
       float r = 0.0f;
-      for (int w = 0; w < kOnThreads / 64; ++w) r += wred[w];
+      for (int w = 0; w < kThr / 64; ++w) r += wred[w];
       bcast[1] = r;
     }
     __syncthreads();
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u)
     m = fmaxf(m, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
-  for (int j = tid; j < ntail; j += kOnThreads) {
+  for (int j = tid; j < ntail; j += kThr) {
     const f32x4_t v = tail[j];
     m = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
   }
@@ -848,7 +848,7 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
       x[u][e] = fast_exp(x[u][e] - M);       // -inf slots become 0
       s += x[u][e];
     }
-  for (int j = tid; j < ntail; j += kOnThreads) {
+  for (int j = tid; j < ntail; j += kThr) {
     f32x4_t v = tail[j];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -867,14 +867,14 @@ __global__ __launch_bounds__(kOnThreads) void k_ce_rows_onchip(float* __restrict
   const int tb = t - h;                                 // the target's index in the vectors
 #pragma unroll
   for (int u = 0; u < kRegVec; ++u) {
-    const int i = tid + u * kOnThreads;
+    const int i = tid + u * kThr;
     if (i >= nreg) continue;
     f32x4_t y = x[u] * scale;
     if (tb >= 4 * i && tb < 4 * i + 4) y[tb - 4 * i] -= gn;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, y), rs, tid * 16,
-                                           u * kOnThreads * 16, 0);
+                                           u * kThr * 16, 0);
   }
-  for (int j = tid; j < ntail; j += kOnThreads) {
+  for (int j = tid; j < ntail; j += kThr) {
     const int i = nreg + j;
     f32x4_t y = tail[j] * scale;
     if (tb >= 4 * i && tb < 4 * i + 4) y[tb - 4 * i] -= gn;
@@ -1043,15 +1043,20 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g,
                            const float* wrow, float* loss_rows, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  // Rows of 24K..128K classes stay on chip (one HBM read); shorter rows
+  // Rows of 24K..150K classes stay on chip (one HBM read); shorter rows
   // stream twice (their second read mostly from cache: measured as fast at
   // 16K classes and 13-16% slower from 24K to 50K), and so do longer ones.
   // A row's vectors number at most V / 4 whatever its alignment.
   const int V4 = V / 4;
-  auto fits = [&](int reg) { return V4 >= 6144 && V4 <= kOnThreads * reg + kCeTailVec; };
-  if (fits(16)) k_ce_rows_onchip<16><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
-  else if (fits(32)) k_ce_rows_onchip<32><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
-  else if (fits(48)) k_ce_rows_onchip<48><<<N, kOnThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  auto fits = [&](int thr, int reg, int tail) { return V4 >= 6144 && V4 <= thr * reg + tail; };
+  if (fits(512, 16, 8192))
+    k_ce_rows_onchip<512, 16, 8192><<<N, 512, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (fits(512, 32, 8192))
+    k_ce_rows_onchip<512, 32, 8192><<<N, 512, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (fits(512, 48, 8192))
+    k_ce_rows_onchip<512, 48, 8192><<<N, 512, 0, s>>>(z, V, tc, g, wrow, loss_rows);
+  else if (fits(1024, 28, 9728))   // up to 153600 classes: 152 KiB of LDS
+    k_ce_rows_onchip<1024, 28, 9728><<<N, 1024, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else k_ce_rows<<<N, kCeThreads, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   return hipGetLastError();
 }

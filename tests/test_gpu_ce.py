@@ -46,11 +46,12 @@ def test_ce_large_logits_and_all_ignored():
     assert nv == 0 and math.isnan(loss[0]) and np.all(np.isnan(dl))
 
 
-@pytest.mark.parametrize("V", [65536, 100000, 131068, 131072])
+@pytest.mark.parametrize("V", [65536, 100000, 131068, 131072, 151936])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 def test_ce_long_rows_on_chip(V, reduction):
-    """Rows of 64K..128K classes take the single-read path (the row held in
-    registers and LDS); ragged lengths exercise its partial vectors."""
+    """Rows of 64K..152K classes take the single-read path (the row held in
+    registers and LDS; 151936 classes with 1024 threads); ragged lengths
+    exercise its partial vectors."""
     require_gpu()
     rng = np.random.default_rng(V + 1)
     N = 9
@@ -105,11 +106,12 @@ def test_ce_any_row_length(V, reduction):
     _check_ce(z, t, reduction, grad_scale=1.25)
 
 
-@pytest.mark.parametrize("V", [32004, 65537, 131071, 131073, 140001])
+@pytest.mark.parametrize("V", [32004, 65537, 131071, 131073, 140001, 160001])
 def test_ce_long_rows_not_a_multiple_of_4(V):
-    """Rows that stay on chip (24K to 128K classes: registers, then the LDS
-    tail) with consecutive rows at every alignment, and a row too long for
-    the chip (140001 classes), which streams twice."""
+    """Rows that stay on chip (24K to 150K classes: registers, then the LDS
+    tail; 512 threads up to 131072 classes, 1024 above) with consecutive
+    rows at every alignment, and a row too long for the chip (160001
+    classes), which streams twice."""
     require_gpu()
     rng = np.random.default_rng(V)
     N = 6
@@ -138,7 +140,7 @@ def test_ce_logits_off_a_16_byte_boundary(V, offset):
     _check_ce(z, t, "mean", offset=offset)
 
 
-@pytest.mark.parametrize("V", [4096, 4097, 50257, 100000])
+@pytest.mark.parametrize("V", [4096, 4097, 50257, 100000, 151936])
 def test_ce_masked_logits(V):
     """Classes masked to -inf: the upper half of every row (whole threads'
     shares of the streaming kernel, 4096 and 4097 classes, see only -inf;
