@@ -13,7 +13,7 @@ from linear_cross_entropy_chunk_amd import _binding as B
 REDUCTION = {"mean": B.LCE_MEAN, "sum": B.LCE_SUM, "none": B.LCE_NONE}
 
 # (N, V, reduction, class weights): the first call on-chip rows, the second
-# a smaller problem on the streamed-row kernel.
+# a smaller problem, one row per wave.
 CALLS = [(300, 131072, "mean", False), (37, 1000, "none", True)]
 
 
