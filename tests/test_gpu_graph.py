@@ -97,10 +97,12 @@ def test_fused_call_replays_from_a_graph(dt, reduction):
     del graph
 
 
-@pytest.mark.parametrize("V", [1000, 100000])
+@pytest.mark.parametrize("V", [1000, 8192, 50257, 100000])
 def test_ce_inplace_replays_from_a_graph(V):
-    """Streamed rows (V = 1000) and on-chip rows (V = 100000); the logits are
-    restored from a pristine copy before every replay."""
+    """Every kernel of the standalone CE: one row per wave (V = 1000), two
+    passes (8192), on chip with rows at every alignment (50257) and aligned
+    (100000); the logits are restored from a pristine copy before every
+    replay."""
     require_gpu()
     N = 61
     rng = np.random.default_rng(V + 3)
