@@ -317,10 +317,9 @@ LCE_API lce_status lce_ce_workspace_size(int64_t N, int64_t V, size_t* bytes);
  * row for NONE.  class_weight ([V] fp32 or NULL) weighs rows as in lce_io.
  * n_valid may be NULL.  Errors: INVALID_ARG (N < 0, V < 1, NULL pointers),
  * UNSUPPORTED (a reduction outside lce_reduction, logits not 4-byte
- * aligned, N or V above 2^31 - 1), WORKSPACE, HIP.  Rows of up to 4099
- * classes and of 24576 to 153600 classes are held on chip and read from
- * memory once; other rows are read twice (the second read of a short row
- * mostly from cache). */
+ * aligned, N or V above 2^31 - 1), WORKSPACE, HIP.  Rows of up to 153600
+ * classes are held on chip and read from memory once; longer rows are read
+ * twice. */
 LCE_API lce_status lce_ce_inplace(float* logits, const int64_t* targets,
                           const float* class_weight, int64_t N,
                           int64_t V, int64_t ignore_index, int32_t reduction,

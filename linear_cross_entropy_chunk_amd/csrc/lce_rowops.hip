@@ -758,8 +758,9 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ z, i
 // then the gradient g (e / sum - onehot): one exponential per element.  As in
 // k_ce_rows, the elements before the row's first 16-byte boundary and after
 // its last whole vector (fewer than 4 each) go one per thread.
-// kThr threads of kRegVec vectors each: 512 threads (two waves per SIMD, 256
-// registers each) or 1024 (four per SIMD, 128 each); kTailVec vectors of LDS.
+// kThr threads of kRegVec vectors each: 256 threads (registers only, several
+// workgroups per CU), 512 (two waves per SIMD, 256 registers each) or 1024
+// (four per SIMD, 128 each); kTailVec vectors of LDS.
 template <int kThr, int kRegVec, int kTailVec>
 __global__ __launch_bounds__(kThr) void k_ce_rows_onchip(float* __restrict__ z, int V,
                                                               const int* __restrict__ tc,
@@ -1110,20 +1111,22 @@ hipError_t ce_inplace_rows(float* z, int N, int V, const int* tc, const float* g
   if (N <= 0) return hipSuccess;
   // Rows of up to 4099 classes go one per wave, in registers (1000 classes:
   // 2.6x the two-pass rate; at 6000-8192 classes a wave of 32 vectors per
-  // lane was slower than two passes); rows of 24K to 150K classes stay on
-  // chip in a workgroup (one HBM read either way).  Rows in between stream
-  // twice (their second read mostly from cache: measured as fast at 16K
-  // classes and 13-16% slower from 24K to 50K), and so do longer ones.  A
-  // row's vectors number at most V / 4 whatever its alignment.
+  // lane was slower than two passes); rows of 4100 to 153600 classes stay on
+  // chip in a workgroup (one HBM read either way: 4100 classes 1.4x, 6000
+  // to 50000 classes 3-16% faster than two passes, 8192 classes 5% slower);
+  // longer rows stream twice.  A row's vectors number at most V / 4
+  // whatever its alignment.
   const int V4 = V / 4;
   const unsigned wave_grid = cdiv_u(N, kWaveRows);
-  auto fits = [&](int thr, int reg, int tail) { return V4 >= 6144 && V4 <= thr * reg + tail; };
+  auto fits = [&](int thr, int reg, int tail) { return V4 >= 1025 && V4 <= thr * reg + tail; };
   if (V4 <= 64 * 4)
     k_ce_rows_wave<4><<<wave_grid, 64 * kWaveRows, 0, s>>>(z, N, V, tc, g, wrow, loss_rows);
   else if (V4 <= 64 * 8)
     k_ce_rows_wave<8><<<wave_grid, 64 * kWaveRows, 0, s>>>(z, N, V, tc, g, wrow, loss_rows);
   else if (V4 <= 64 * 16)
     k_ce_rows_wave<16><<<wave_grid, 64 * kWaveRows, 0, s>>>(z, N, V, tc, g, wrow, loss_rows);
+  else if (fits(256, 16, 64))      // registers only: up to 16640 classes
+    k_ce_rows_onchip<256, 16, 64><<<N, 256, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else if (fits(512, 16, 8192))
     k_ce_rows_onchip<512, 16, 8192><<<N, 512, 0, s>>>(z, V, tc, g, wrow, loss_rows);
   else if (fits(512, 32, 8192))

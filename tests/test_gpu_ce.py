@@ -88,7 +88,7 @@ def _check_ce(z, t, reduction, offset=0, grad_scale=1.0):
     return dl
 
 
-@pytest.mark.parametrize("V", [1, 2, 3, 5, 7, 1021, 2049, 4097, 8193, 50257])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 7, 1021, 2049, 4097, 8193, 16641, 50257])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 def test_ce_any_row_length(V, reduction):
     """V not a multiple of 4: row n starts n V mod 4 floats past a 16-byte
@@ -128,8 +128,8 @@ def test_ce_long_rows_not_a_multiple_of_4(V):
 def test_ce_logits_off_a_16_byte_boundary(V, offset):
     """Logits that start 4, 8 or 12 bytes past a 16-byte boundary (a view into
     a larger buffer): accepted, and every row takes the element-wise head and
-    tail, one row per wave (4096 classes), in two passes (12000) and on chip
-    (131072)."""
+    tail, one row per wave (4096 classes) and on chip (12000 with 256
+    threads, 131072 with 512)."""
     require_gpu()
     rng = np.random.default_rng(V + offset)
     N = 5
@@ -141,12 +141,12 @@ def test_ce_logits_off_a_16_byte_boundary(V, offset):
     _check_ce(z, t, "mean", offset=offset)
 
 
-@pytest.mark.parametrize("V", [4096, 8192, 8193, 50257, 100000, 151936])
+@pytest.mark.parametrize("V", [4096, 8193, 50257, 100000, 151936, 160001])
 def test_ce_masked_logits(V):
     """Classes masked to -inf: the upper half of every row (whole threads'
-    shares of the two-pass kernel, 8192 and 8193 classes, see only -inf;
-    4096 classes go one row per wave, 50257 and up stay on chip), and all
-    but three classes of one row.
+    shares of the two-pass kernel, 160001 classes, see only -inf; 4096
+    classes go one row per wave, 8193 to 151936 stay on chip), and all but
+    three classes of one row.
     The loss stays finite and the masked gradient is exactly 0, as in the
     oracle (pinned to torch)."""
     require_gpu()

@@ -97,12 +97,12 @@ def test_fused_call_replays_from_a_graph(dt, reduction):
     del graph
 
 
-@pytest.mark.parametrize("V", [1000, 8192, 50257, 100000])
+@pytest.mark.parametrize("V", [1000, 8192, 50257, 100000, 160001])
 def test_ce_inplace_replays_from_a_graph(V):
-    """Every kernel of the standalone CE: one row per wave (V = 1000), two
-    passes (8192), on chip with rows at every alignment (50257) and aligned
-    (100000); the logits are restored from a pristine copy before every
-    replay."""
+    """Every kernel of the standalone CE: one row per wave (V = 1000), on
+    chip with 256 threads (8192), with rows at every alignment (50257) and
+    aligned (100000), and two passes (160001); the logits are restored from
+    a pristine copy before every replay."""
     require_gpu()
     N = 61
     rng = np.random.default_rng(V + 3)

@@ -149,14 +149,14 @@ def test_a_whole_statistics_block_of_nan(dt, upstream):
             _same_nans(gpu[key], ref[key], key)
 
 
-@pytest.mark.parametrize("v", [4096, 8192, 65536])
+@pytest.mark.parametrize("v", [4096, 8192, 65536, 160001])
 def test_ce_row_nan_but_its_target(v):
     """A row NaN everywhere except the 4-class vector that holds its target.
-    The two-pass kernel (V=8192) gives each thread two vectors, so all of
-    the row's threads but one see NaN only and their NaN-skipping maxima
-    stay -inf; the wave kernel (V=4096) and the on-chip one (V=65536) take
-    one max over the row.  Either way the row's loss and gradient must be
-    NaN and the other rows unchanged."""
+    The two-pass kernel (V=160001) gives each thread a few dozen vectors, so
+    all of the row's threads but one see NaN only and their NaN-skipping
+    maxima stay -inf; the wave kernel (V=4096) and the on-chip ones (8192,
+    65536) take one max over the row.  Either way the row's loss and
+    gradient must be NaN and the other rows unchanged."""
     require_gpu()
     rng = np.random.default_rng(105)
     n = 32
